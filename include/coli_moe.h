@@ -1,0 +1,188 @@
+/*
+ * coli_moe.h -- C ABI of one routed Mixture-of-Experts layer forward on AMD
+ * Instinct MI355X (gfx950), hand-written HIP kernels.
+ *
+ * The layer (sources: web pages about the Colibri / colibri MoE engine):
+ *   1. float32 router: logits = hidden . Wr, sigmoid scores, a per-expert
+ *      selection bias, noaux_tc top-k with n_group = 1, the selected scores
+ *      renormalised and multiplied by routed_scaling_factor
+ *      ("colibri engine teardown" page, "Three key engineering decisions",
+ *      item 1: sigmoid router, noaux_tc, n_group = 1, routed_scaling_factor;
+ *      norm, router and bias stay float32);
+ *   2. grouping of (token, slot) assignments by expert with a counting sort
+ *      and a prefix sum into per-expert offsets (cf-1.com Colibri article,
+ *      section 3.3, colibri_forward step 3), done on the device with no host
+ *      round trip;
+ *   3. per-expert SwiGLU FFN over int4 weights with one float32 scale per 64
+ *      weights ("gs64", same teardown page, item 1; three expert matrices,
+ *      cf-1.com article section 2.1);
+ *   4. weighted combine of the k expert outputs of each token (cf-1.com
+ *      article section 3.3, step 5) plus a shared expert with weight 1
+ *      (teardown page, "System map": the shared expert is resident).
+ *
+ * API shape: init / forward / free with negative integer error codes, a dry
+ * run for zero tokens, and a handle that is not thread-safe (trdm.cn article
+ * "Colibri: a pure-C lightweight inference engine built for MoE models",
+ * sections 4.2, 5.1 and 5.2).
+ *
+ * Conventions for every function below:
+ *  - "device" pointers point to HIP device memory of the current device;
+ *    "host" pointers to ordinary host memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue work on that stream; nothing synchronises with the
+ *    host unless stated.  Device-side faults surface at the caller's next
+ *    synchronisation.
+ *  - The library never allocates device memory: weights, the workspace,
+ *    inputs and outputs belong to the caller, who keeps them alive while a
+ *    handle uses them.
+ *  - A handle must not be used from two threads at once, nor on two streams
+ *    whose work may overlap (calls share the handle's workspace).
+ *  - Inputs must be finite.  NaN or Inf in the hidden state or weights gives
+ *    unspecified routing and outputs.
+ */
+#ifndef COLI_MOE_H
+#define COLI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes (0 = success). */
+#define COLI_MOE_OK 0
+#define COLI_MOE_ECAPACITY (-1) /* T > max_tokens, or the workspace is too small */
+#define COLI_MOE_EROUTING (-2)  /* top_k < 1 or > n_experts or > 32, n_group != 1, group_size != 64 */
+#define COLI_MOE_EDEVICE (-3)   /* a HIP launch or runtime call failed */
+#define COLI_MOE_EARG (-4)      /* NULL or misaligned pointer, unsupported dimension */
+
+/* Layer configuration, fixed at init. */
+typedef struct {
+  int32_t hidden;            /* h: multiple of 64, 64..16384 */
+  int32_t n_experts;         /* E: routed experts, 1..512 */
+  int32_t top_k;             /* k: experts per token, 1..min(E, 32) */
+  int32_t inter;             /* I: expert intermediate size, multiple of 64, 64..16384 */
+  int32_t n_shared;          /* shared experts: 0 or 1 */
+  int32_t group_size;        /* weights per scale: must be 64 */
+  int32_t n_group;           /* expert groups of noaux_tc: must be 1 */
+  int32_t max_tokens;        /* most tokens one forward may take, >= 1 */
+  int32_t prefill_threshold; /* T >= this takes the bf16 MFMA path; 0 = 256 */
+  float routed_scaling_factor;
+} coli_moe_config_t;
+
+/*
+ * Weight tables, all DEVICE pointers, borrowed (the caller owns them and
+ * keeps them alive and unchanged while the handle exists).
+ *
+ * int4 gs64 storage of a weight matrix [rows][cols]: byte c/2 of a row holds
+ * weight c in its low nibble when c is even and in its high nibble when c is
+ * odd, as a 4-bit two's-complement code q in [-8, 7]; the float32 scale
+ * s[row][c/64] belongs to the 64 weights of group c/64; weight = q * s.
+ * Groups run along the input (reduction) axis.  Rows are contiguous.
+ *
+ * All code and scale arrays must be 16-byte aligned; router_w and sel_bias
+ * 4-byte aligned.
+ */
+typedef struct {
+  const float *router_w;   /* [hidden][n_experts] float32 */
+  const float *sel_bias;   /* [n_experts] float32 selection bias; NULL = zeros */
+  const uint8_t *gate_q;   /* [n_experts][inter][hidden/2]   (W1) */
+  const float *gate_s;     /* [n_experts][inter][hidden/64] */
+  const uint8_t *up_q;     /* [n_experts][inter][hidden/2]   (W3) */
+  const float *up_s;       /* [n_experts][inter][hidden/64] */
+  const uint8_t *down_q;   /* [n_experts][hidden][inter/2]   (W2) */
+  const float *down_s;     /* [n_experts][hidden][inter/64] */
+  /* the shared expert, same layout for one expert; NULL when n_shared == 0 */
+  const uint8_t *sh_gate_q;
+  const float *sh_gate_s;
+  const uint8_t *sh_up_q;
+  const float *sh_up_s;
+  const uint8_t *sh_down_q;
+  const float *sh_down_s;
+} coli_moe_weights_t;
+
+typedef struct coli_moe coli_moe_t; /* opaque handle */
+
+/*
+ * Bytes of DEVICE workspace a handle with this configuration needs (router
+ * copy, routing and dispatch arrays, expert intermediates for max_tokens).
+ * Returns 0 when the configuration is invalid.
+ */
+size_t coli_moe_workspace_bytes(const coli_moe_config_t *cfg);
+
+/*
+ * Create a handle.  `workspace` is caller-owned DEVICE memory of at least
+ * coli_moe_workspace_bytes(cfg) bytes, 256-byte aligned, used only by this
+ * handle until coli_moe_free.  Enqueues a copy of the router into the
+ * workspace on `stream`.  On success *out receives the handle (host memory
+ * the library owns).
+ * Errors: -4 NULL/misaligned pointer or unsupported dimension, -2 routing
+ * configuration, -1 workspace too small, -3 HIP error.
+ */
+int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe_weights_t *w,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * out[t] = sum_j w[t][j] * FFN_{idx[t][j]}(hidden[t]) + FFN_shared(hidden[t])
+ * for t < T.  `hidden` is DEVICE float32 [T][hidden] (16-byte aligned), `out`
+ * DEVICE float32 [T][hidden] (16-byte aligned, may not alias `hidden`).
+ * Asynchronous on `stream`; the host never reads device data.  T == 0 checks
+ * the arguments and enqueues nothing (dry run).  T < prefill_threshold runs
+ * the float32-accumulate GEMV path, larger T the bf16 MFMA grouped-GEMM path.
+ * Errors: -4 bad handle/pointer, -1 T > max_tokens (or T < 0 gives -4),
+ * -3 HIP launch error.
+ */
+int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, void *stream);
+
+/* Release the handle (host memory only).  NULL is a no-op.  The caller must
+ * make sure no enqueued forward of the handle is still running. */
+void coli_moe_free(coli_moe_t *m);
+
+/*
+ * Copy the routing and dispatch of the handle's last forward (T tokens) into
+ * caller DEVICE buffers, enqueued on `stream` (for parity checks).  Any
+ * pointer may be NULL to skip it.  Sizes: idx and w [T*k] (assignment
+ * a = t*k + j, slot order = selection rank), offsets [E+1], sorted_ids and
+ * inv [T*k], active [E] (experts with tokens, ascending; n_active of them are
+ * valid), n_active [1].  Returns the T of the last forward (>= 0) or -4.
+ */
+int coli_moe_last_routing(const coli_moe_t *m, int32_t *idx, float *w, int32_t *offsets,
+                          int32_t *sorted_ids, int32_t *inv, int32_t *active, int32_t *n_active,
+                          void *stream);
+
+/*
+ * The dispatch kernel alone on caller data: a stable counting sort of the
+ * assignments a = t*k + j of DEVICE idx [T*k] (values in [0, E)) by expert,
+ * written to DEVICE offsets [E+1], sorted_ids [T*k], inv [T*k], active [E],
+ * n_active [1] (same meaning as above).  1 <= E <= 512, 1 <= k <= 32,
+ * 0 <= T*k <= 2^20.  (cf-1.com Colibri article, section 3.3, step 3.)
+ * Errors: -4.  Out-of-range idx values give unspecified (but in-bounds)
+ * results.
+ */
+int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *offsets,
+                           int32_t *sorted_ids, int32_t *inv, int32_t *active, int32_t *n_active,
+                           void *stream);
+
+/*
+ * Kernel timing.  coli_moe_profile_begin makes the next `max_calls` forwards
+ * of the handle record a HIP event pair around each kernel they launch (host
+ * allocations only; events are created here).  coli_moe_profile_end waits
+ * for those events, writes the summed milliseconds and launch counts per
+ * kernel (arrays of COLI_MOE_N_KERNELS entries, either may be NULL) and
+ * stops recording.  Returns the number of forwards recorded, or -4/-3.
+ */
+#define COLI_MOE_N_KERNELS 8
+int coli_moe_profile_begin(coli_moe_t *m, int32_t max_calls);
+int coli_moe_profile_end(coli_moe_t *m, float *kernel_ms, int32_t *kernel_launches);
+/* Name of kernel i (0 <= i < COLI_MOE_N_KERNELS), a static string. */
+const char *coli_moe_kernel_name(int32_t i);
+
+/* Static description of an error code. */
+const char *coli_moe_error_string(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLI_MOE_H */

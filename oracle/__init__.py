@@ -73,6 +73,8 @@ def _load():
         L.coli_oracle_expert_ffn.restype = None
         L.coli_oracle_forward.argtypes = [ctypes.POINTER(Layer), vp, i32, vp, vp, vp]
         L.coli_oracle_forward.restype = i32
+        L.coli_oracle_threads.argtypes = []
+        L.coli_oracle_threads.restype = i32
         _lib = L
     return _lib
 
@@ -83,6 +85,11 @@ def _f32(a):
 
 def _i32(a):
     return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().coli_oracle_threads())
 
 
 def exp_spec(y: float) -> float:

@@ -428,3 +428,15 @@ done:
   free(ysh);
   return rc;
 }
+
+/* Threads the oracle's parallel loops use (for reporting). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int32_t coli_oracle_threads(void) {
+#ifdef _OPENMP
+  return (int32_t)omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

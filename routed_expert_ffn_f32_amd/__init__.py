@@ -1,0 +1,223 @@
+"""Python binding of libcoli_moe, the gfx950 routed-MoE layer library.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels (include/coli_moe.h documents the C ABI).  The functions keep the C
+names; pointers are passed as integers (device addresses, e.g. a torch
+tensor's data_ptr()) and streams as integer hipStream_t handles (e.g.
+torch.cuda.current_stream().cuda_stream).  Non-zero return codes raise
+ColiMoeError.
+
+`MoELayer` is a convenience wrapper that uses PyTorch for what PyTorch is
+here for: device memory (weights, workspace, outputs) and streams.
+
+There is no fallback: if the library is not built, importing works but the
+first call raises, naming the build command.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libcoli_moe.so")
+
+COLI_MOE_OK = 0
+COLI_MOE_ECAPACITY = -1
+COLI_MOE_EROUTING = -2
+COLI_MOE_EDEVICE = -3
+COLI_MOE_EARG = -4
+COLI_MOE_N_KERNELS = 8
+
+
+class ColiMoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: error {code} ({coli_moe_error_string(code)})")
+
+
+class coli_moe_config_t(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("n_group", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("prefill_threshold", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float)]
+
+
+class coli_moe_weights_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "router_w", "sel_bias", "gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s",
+        "sh_gate_q", "sh_gate_s", "sh_up_q", "sh_up_s", "sh_down_q", "sh_down_s")]
+
+
+_lib = None
+
+
+def load_library():
+    """Load the built library (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m routed_expert_ffn_f32_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        cfgp, wp = ctypes.POINTER(coli_moe_config_t), ctypes.POINTER(coli_moe_weights_t)
+        L.coli_moe_workspace_bytes.argtypes = [cfgp]
+        L.coli_moe_workspace_bytes.restype = sz
+        L.coli_moe_init.argtypes = [ctypes.POINTER(vp), cfgp, wp, vp, sz, vp]
+        L.coli_moe_init.restype = ctypes.c_int
+        L.coli_moe_forward.argtypes = [vp, vp, vp, i32, vp]
+        L.coli_moe_forward.restype = ctypes.c_int
+        L.coli_moe_free.argtypes = [vp]
+        L.coli_moe_free.restype = None
+        L.coli_moe_last_routing.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.coli_moe_last_routing.restype = ctypes.c_int
+        L.coli_moe_test_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.coli_moe_test_dispatch.restype = ctypes.c_int
+        L.coli_moe_profile_begin.argtypes = [vp, i32]
+        L.coli_moe_profile_begin.restype = ctypes.c_int
+        L.coli_moe_profile_end.argtypes = [vp, vp, vp]
+        L.coli_moe_profile_end.restype = ctypes.c_int
+        L.coli_moe_kernel_name.argtypes = [i32]
+        L.coli_moe_kernel_name.restype = ctypes.c_char_p
+        L.coli_moe_error_string.argtypes = [i32]
+        L.coli_moe_error_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str) -> int:
+    if rc < 0:
+        raise ColiMoeError(rc, where)
+    return rc
+
+
+def coli_moe_error_string(code: int) -> str:
+    return load_library().coli_moe_error_string(int(code)).decode()
+
+
+def coli_moe_kernel_name(i: int) -> str:
+    return load_library().coli_moe_kernel_name(int(i)).decode()
+
+
+def coli_moe_workspace_bytes(cfg: coli_moe_config_t) -> int:
+    return int(load_library().coli_moe_workspace_bytes(ctypes.byref(cfg)))
+
+
+def coli_moe_init(cfg: coli_moe_config_t, weights: coli_moe_weights_t, workspace: int,
+                  workspace_bytes: int, stream: int = 0) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load_library().coli_moe_init(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(weights),
+                                        workspace, workspace_bytes, stream), "coli_moe_init")
+    return h
+
+
+def coli_moe_forward(handle, hidden: int, out: int, T: int, stream: int = 0) -> int:
+    return _check(load_library().coli_moe_forward(handle, hidden, out, int(T), stream), "coli_moe_forward")
+
+
+def coli_moe_free(handle) -> None:
+    load_library().coli_moe_free(handle)
+
+
+def coli_moe_last_routing(handle, idx=None, w=None, offsets=None, sorted_ids=None, inv=None,
+                          active=None, n_active=None, stream: int = 0) -> int:
+    return _check(load_library().coli_moe_last_routing(handle, idx, w, offsets, sorted_ids, inv, active,
+                                                       n_active, stream), "coli_moe_last_routing")
+
+
+def coli_moe_test_dispatch(idx: int, T: int, k: int, E: int, offsets: int, sorted_ids: int, inv: int,
+                           active: int, n_active: int, stream: int = 0) -> int:
+    return _check(load_library().coli_moe_test_dispatch(idx, int(T), int(k), int(E), offsets, sorted_ids,
+                                                        inv, active, n_active, stream),
+                  "coli_moe_test_dispatch")
+
+
+def coli_moe_profile_begin(handle, max_calls: int) -> int:
+    return _check(load_library().coli_moe_profile_begin(handle, int(max_calls)), "coli_moe_profile_begin")
+
+
+def coli_moe_profile_end(handle):
+    """Returns (calls, {kernel name: (total ms, launches)})."""
+    ms = (ctypes.c_float * COLI_MOE_N_KERNELS)()
+    n = (ctypes.c_int32 * COLI_MOE_N_KERNELS)()
+    calls = _check(load_library().coli_moe_profile_end(handle, ms, n), "coli_moe_profile_end")
+    return calls, {coli_moe_kernel_name(i): (float(ms[i]), int(n[i])) for i in range(COLI_MOE_N_KERNELS)}
+
+
+# ---------------------------------------------------------------------------
+# Convenience wrapper over torch device tensors.
+# ---------------------------------------------------------------------------
+
+_WEIGHT_KEYS = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
+
+
+def make_config(hidden, n_experts, top_k, inter, n_shared, routed_scaling_factor, max_tokens,
+                prefill_threshold=0, group_size=64, n_group=1) -> coli_moe_config_t:
+    return coli_moe_config_t(hidden=hidden, n_experts=n_experts, top_k=top_k, inter=inter, n_shared=n_shared,
+                             group_size=group_size, n_group=n_group, max_tokens=max_tokens,
+                             prefill_threshold=prefill_threshold,
+                             routed_scaling_factor=routed_scaling_factor)
+
+
+class MoELayer:
+    """One layer on the current torch device.
+
+    `tensors` maps names to device tensors: router_w [h,E] f32, sel_bias [E]
+    f32 (optional), gate_q/up_q [E,I,h/2] u8, gate_s/up_s [E,I,h/64] f32,
+    down_q [E,h,I/2] u8, down_s [E,h,I/64] f32, and sh_* for the shared
+    expert.  The tensors are borrowed: keep them alive with the layer.
+    """
+
+    def __init__(self, cfg: coli_moe_config_t, tensors: dict, stream: int | None = None):
+        import torch
+        self.cfg = cfg
+        self.tensors = tensors
+        w = coli_moe_weights_t()
+        for name, _ in coli_moe_weights_t._fields_:
+            t = tensors.get(name)
+            setattr(w, name, None if t is None else t.data_ptr())
+        self.weights = w
+        nbytes = coli_moe_workspace_bytes(cfg)
+        if nbytes == 0:
+            raise ColiMoeError(COLI_MOE_EARG, "coli_moe_workspace_bytes")
+        dev = tensors["router_w"].device
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+        self.handle = coli_moe_init(cfg, w, self.workspace.data_ptr(), nbytes, self.stream)
+
+    def forward(self, hidden, out=None):
+        import torch
+        T = hidden.shape[0]
+        if out is None:
+            out = torch.empty_like(hidden)
+        coli_moe_forward(self.handle, hidden.data_ptr(), out.data_ptr(), T, self.stream)
+        return out
+
+    __call__ = forward
+
+    def last_routing(self):
+        """Device tensors of the last forward's routing and dispatch."""
+        import torch
+        dev = self.workspace.device
+        T, k, E = None, self.cfg.top_k, self.cfg.n_experts
+        T = coli_moe_last_routing(self.handle, stream=self.stream)
+        n = T * k
+        i32 = dict(dtype=torch.int32, device=dev)
+        r = dict(idx=torch.empty(n, **i32), w=torch.empty(n, dtype=torch.float32, device=dev),
+                 offsets=torch.empty(E + 1, **i32), sorted_ids=torch.empty(n, **i32),
+                 inv=torch.empty(n, **i32), active=torch.empty(E, **i32), n_active=torch.empty(1, **i32))
+        coli_moe_last_routing(self.handle, *(r[key].data_ptr() for key in
+                                             ("idx", "w", "offsets", "sorted_ids", "inv", "active",
+                                              "n_active")), stream=self.stream)
+        return T, r
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            coli_moe_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,349 @@
+// Host side of the C ABI declared in include/coli_moe.h: argument checks,
+// workspace layout, and the launch sequence of one layer forward.
+//
+// API shape (init / forward / free, negative error codes, dry run for zero
+// tokens, capacity fixed at init): trdm.cn article "Colibri: a pure-C
+// lightweight inference engine built for MoE models", sections 3.2 (buffers
+// sized once from the maximum batch), 4.2 (return codes), 5.1 (batch above
+// the maximum is an error; one handle per thread) and 5.2 (batch size 0
+// checks the setup without computing).  The per-handle device state (router
+// copy, expert offsets) follows the opaque context of the cf-1.com Colibri
+// article, section 3.2.
+#include <new>
+#include <vector>
+
+#include "coli_moe.h"
+#include "internal.h"
+
+namespace {
+
+enum Kernel {
+  K_ROUTER_LOGITS = 0,
+  K_ROUTER_SELECT = 1,
+  K_DISPATCH = 2,
+  K_GATE_UP = 3,
+  K_DOWN = 4,
+  K_COMBINE = 5,
+  K_MFMA_GATE_UP = 6,
+  K_MFMA_DOWN = 7,
+};
+
+const char *const kKernelNames[COLI_MOE_N_KERNELS] = {
+    "router_logits", "router_select", "dispatch",       "expert_gemv_gate_up",
+    "expert_gemv_down", "combine",    "expert_mfma_gate_up", "expert_mfma_down"};
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+// Byte offsets of the workspace regions.
+struct Layout {
+  size_t wrT, logits, idx, w, offsets, sorted_ids, inv, active, n_active, mid, y, total;
+};
+
+bool config_ok(const coli_moe_config_t &c, int *code) {
+  if (c.hidden < 64 || c.hidden > 16384 || c.hidden % 64 || c.inter < 64 || c.inter > 16384 ||
+      c.inter % 64 || c.n_experts < 1 || c.n_experts > coli::kMaxExperts || c.max_tokens < 1 ||
+      (c.n_shared != 0 && c.n_shared != 1) || c.prefill_threshold < 0) {
+    *code = COLI_MOE_EARG;
+    return false;
+  }
+  if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > coli::kMaxTopK || c.n_group != 1 ||
+      c.group_size != 64) {
+    *code = COLI_MOE_EROUTING;
+    return false;
+  }
+  if ((int64_t)c.max_tokens * c.top_k > (1 << 20)) {
+    *code = COLI_MOE_EARG;
+    return false;
+  }
+  return true;
+}
+
+Layout layout_of(const coli_moe_config_t &c) {
+  Layout L{};
+  const size_t T = (size_t)c.max_tokens, E = (size_t)c.n_experts, k = (size_t)c.top_k;
+  const size_t h = (size_t)c.hidden, I = (size_t)c.inter;
+  const size_t P = T * k + (c.n_shared ? T : 0);  // expert-output rows
+  size_t o = 0;
+  L.wrT = o;        o = align_up(o + E * h * 4);
+  L.logits = o;     o = align_up(o + T * E * 4);
+  L.idx = o;        o = align_up(o + T * k * 4);
+  L.w = o;          o = align_up(o + T * k * 4);
+  L.offsets = o;    o = align_up(o + (E + 1) * 4);
+  L.sorted_ids = o; o = align_up(o + T * k * 4);
+  L.inv = o;        o = align_up(o + T * k * 4);
+  L.active = o;     o = align_up(o + E * 4);
+  L.n_active = o;   o = align_up(o + 4);
+  L.mid = o;        o = align_up(o + P * I * 4);
+  L.y = o;          o = align_up(o + P * h * 4);
+  L.total = o;
+  return L;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct ProfRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct coli_moe {
+  coli_moe_config_t cfg;
+  coli_moe_weights_t w;
+  char *ws;
+  Layout L;
+  int last_T;
+  // profiling
+  int prof_calls_left;
+  int prof_calls_done;
+  std::vector<ProfRecord> prof;
+  size_t prof_used;
+};
+
+namespace {
+
+template <class F>
+hipError_t timed(coli_moe_t *m, int kernel, hipStream_t s, F &&launch) {
+  if (m->prof_calls_left <= 0 || m->prof_used >= m->prof.size()) return launch();
+  ProfRecord &r = m->prof[m->prof_used++];
+  r.kernel = kernel;
+  hipError_t e = hipEventRecord(r.start, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  return hipEventRecord(r.stop, s);
+}
+
+template <class T>
+T *at(coli_moe_t *m, size_t off) {
+  return reinterpret_cast<T *>(m->ws + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t coli_moe_workspace_bytes(const coli_moe_config_t *cfg) {
+  int code;
+  if (!cfg || !config_ok(*cfg, &code)) return 0;
+  return layout_of(*cfg).total;
+}
+
+int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe_weights_t *w,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+  if (!out || !cfg || !w || !workspace) return COLI_MOE_EARG;
+  *out = nullptr;
+  int code = COLI_MOE_OK;
+  if (!config_ok(*cfg, &code)) return code;
+  const void *tabs[] = {w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s};
+  for (const void *p : tabs)
+    if (!p || !aligned(p, 16)) return COLI_MOE_EARG;
+  if (!w->router_w || !aligned(w->router_w, 4) || (w->sel_bias && !aligned(w->sel_bias, 4)))
+    return COLI_MOE_EARG;
+  if (cfg->n_shared) {
+    const void *sh[] = {w->sh_gate_q, w->sh_gate_s, w->sh_up_q, w->sh_up_s, w->sh_down_q, w->sh_down_s};
+    for (const void *p : sh)
+      if (!p || !aligned(p, 16)) return COLI_MOE_EARG;
+  }
+  if (!aligned(workspace, kAlign)) return COLI_MOE_EARG;
+  const Layout L = layout_of(*cfg);
+  if (workspace_bytes < L.total) return COLI_MOE_ECAPACITY;
+
+  coli_moe_t *m = new (std::nothrow) coli_moe_t();
+  if (!m) return COLI_MOE_EARG;
+  m->cfg = *cfg;
+  if (m->cfg.prefill_threshold == 0) m->cfg.prefill_threshold = 256;
+  m->w = *w;
+  m->ws = static_cast<char *>(workspace);
+  m->L = L;
+  m->last_T = 0;
+  m->prof_calls_left = 0;
+  m->prof_calls_done = 0;
+  m->prof_used = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (coli::launch_router_transpose(w->router_w, at<float>(m, L.wrT), cfg->hidden, cfg->n_experts, s) !=
+      hipSuccess) {
+    delete m;
+    return COLI_MOE_EDEVICE;
+  }
+  *out = m;
+  return COLI_MOE_OK;
+}
+
+int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, void *stream) {
+  if (!m || T < 0) return COLI_MOE_EARG;
+  if (T > m->cfg.max_tokens) return COLI_MOE_ECAPACITY;
+  if (T == 0) return COLI_MOE_OK;
+  if (!hidden || !out || !aligned(hidden, 16) || !aligned(out, 16)) return COLI_MOE_EARG;
+  const coli_moe_config_t &c = m->cfg;
+  const Layout &L = m->L;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int E = c.n_experts, k = c.top_k, h = c.hidden, I = c.inter;
+  float *logits = at<float>(m, L.logits);
+  int32_t *idx = at<int32_t>(m, L.idx);
+  float *wsel = at<float>(m, L.w);
+  int32_t *offsets = at<int32_t>(m, L.offsets), *sorted_ids = at<int32_t>(m, L.sorted_ids);
+  int32_t *inv = at<int32_t>(m, L.inv), *active = at<int32_t>(m, L.active);
+  int32_t *n_active = at<int32_t>(m, L.n_active);
+  float *mid = at<float>(m, L.mid), *y = at<float>(m, L.y);
+
+  hipError_t e;
+  e = timed(m, K_ROUTER_LOGITS, s, [&] {
+    return coli::launch_router_logits(hidden, at<float>(m, L.wrT), T, h, E, logits, s);
+  });
+  if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  e = timed(m, K_ROUTER_SELECT, s, [&] {
+    return coli::launch_router_select(logits, m->w.sel_bias, T, E, k, c.routed_scaling_factor, idx, wsel, s);
+  });
+  if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  e = timed(m, K_DISPATCH, s, [&] {
+    return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
+  });
+  if (e != hipSuccess) return COLI_MOE_EDEVICE;
+
+  coli::GemvProblem P{};
+  P.offsets = offsets;
+  P.sorted_ids = sorted_ids;
+  P.active = active;
+  P.n_active = n_active;
+  P.T = T;
+  P.k = k;
+  P.E = E;
+  P.n_routed_slots = E < T * k ? E : T * k;
+  P.has_shared = c.n_shared;
+  // gate and up: [I][h] per expert
+  P.a = {m->w.gate_q, m->w.gate_s};
+  P.b = {m->w.up_q, m->w.up_s};
+  P.sh_a = {m->w.sh_gate_q, m->w.sh_gate_s};
+  P.sh_b = {m->w.sh_up_q, m->w.sh_up_s};
+  P.rows = I;
+  P.cols = h;
+  P.x = hidden;
+  P.out = mid;
+  e = timed(m, K_GATE_UP, s, [&] { return coli::launch_gemv_gate_up(P, s); });
+  if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  // down: [h][I] per expert
+  P.a = {m->w.down_q, m->w.down_s};
+  P.b = {nullptr, nullptr};
+  P.sh_a = {m->w.sh_down_q, m->w.sh_down_s};
+  P.sh_b = {nullptr, nullptr};
+  P.rows = h;
+  P.cols = I;
+  P.x = mid;
+  P.out = y;
+  e = timed(m, K_DOWN, s, [&] { return coli::launch_gemv_down(P, s); });
+  if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  e = timed(m, K_COMBINE, s, [&] { return coli::launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
+  if (e != hipSuccess) return COLI_MOE_EDEVICE;
+
+  m->last_T = T;
+  if (m->prof_calls_left > 0) {
+    --m->prof_calls_left;
+    ++m->prof_calls_done;
+  }
+  return COLI_MOE_OK;
+}
+
+void coli_moe_free(coli_moe_t *m) {
+  if (!m) return;
+  for (ProfRecord &r : m->prof) {
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  delete m;
+}
+
+int coli_moe_last_routing(const coli_moe_t *mc, int32_t *idx, float *w, int32_t *offsets,
+                          int32_t *sorted_ids, int32_t *inv, int32_t *active, int32_t *n_active,
+                          void *stream) {
+  if (!mc) return COLI_MOE_EARG;
+  coli_moe_t *m = const_cast<coli_moe_t *>(mc);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t n = (size_t)m->last_T * m->cfg.top_k, E = (size_t)m->cfg.n_experts;
+  struct Copy {
+    void *dst;
+    size_t off, bytes;
+  } copies[] = {{idx, m->L.idx, n * 4},         {w, m->L.w, n * 4},
+                {offsets, m->L.offsets, (E + 1) * 4}, {sorted_ids, m->L.sorted_ids, n * 4},
+                {inv, m->L.inv, n * 4},         {active, m->L.active, E * 4},
+                {n_active, m->L.n_active, 4}};
+  for (const Copy &c : copies) {
+    if (!c.dst || c.bytes == 0) continue;
+    if (hipMemcpyAsync(c.dst, m->ws + c.off, c.bytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return COLI_MOE_EDEVICE;
+  }
+  return m->last_T;
+}
+
+int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *offsets,
+                           int32_t *sorted_ids, int32_t *inv, int32_t *active, int32_t *n_active,
+                           void *stream) {
+  if (T < 0 || k < 1 || k > coli::kMaxTopK || E < 1 || E > coli::kMaxExperts ||
+      (int64_t)T * k > (1 << 20))
+    return COLI_MOE_EARG;
+  if (!offsets || !active || !n_active || (T > 0 && (!idx || !sorted_ids || !inv))) return COLI_MOE_EARG;
+  if (coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+    return COLI_MOE_EDEVICE;
+  return COLI_MOE_OK;
+}
+
+int coli_moe_profile_begin(coli_moe_t *m, int32_t max_calls) {
+  if (!m || max_calls < 0) return COLI_MOE_EARG;
+  const size_t need = (size_t)max_calls * COLI_MOE_N_KERNELS;
+  while (m->prof.size() < need) {
+    ProfRecord r{};
+    if (hipEventCreate(&r.start) != hipSuccess) return COLI_MOE_EDEVICE;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+      (void)hipEventDestroy(r.start);
+      return COLI_MOE_EDEVICE;
+    }
+    m->prof.push_back(r);
+  }
+  m->prof_used = 0;
+  m->prof_calls_left = max_calls;
+  m->prof_calls_done = 0;
+  return COLI_MOE_OK;
+}
+
+int coli_moe_profile_end(coli_moe_t *m, float *kernel_ms, int32_t *kernel_launches) {
+  if (!m) return COLI_MOE_EARG;
+  float ms[COLI_MOE_N_KERNELS] = {0};
+  int32_t cnt[COLI_MOE_N_KERNELS] = {0};
+  for (size_t i = 0; i < m->prof_used; ++i) {
+    ProfRecord &r = m->prof[i];
+    if (hipEventSynchronize(r.stop) != hipSuccess) return COLI_MOE_EDEVICE;
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return COLI_MOE_EDEVICE;
+    ms[r.kernel] += t;
+    cnt[r.kernel] += 1;
+  }
+  if (kernel_ms)
+    for (int i = 0; i < COLI_MOE_N_KERNELS; ++i) kernel_ms[i] = ms[i];
+  if (kernel_launches)
+    for (int i = 0; i < COLI_MOE_N_KERNELS; ++i) kernel_launches[i] = cnt[i];
+  const int done = m->prof_calls_done;
+  m->prof_calls_left = 0;
+  m->prof_calls_done = 0;
+  m->prof_used = 0;
+  return done;
+}
+
+const char *coli_moe_kernel_name(int32_t i) {
+  return (i >= 0 && i < COLI_MOE_N_KERNELS) ? kKernelNames[i] : "";
+}
+
+const char *coli_moe_error_string(int32_t code) {
+  switch (code) {
+    case COLI_MOE_OK: return "ok";
+    case COLI_MOE_ECAPACITY: return "capacity: more tokens than max_tokens, or workspace too small";
+    case COLI_MOE_EROUTING: return "routing configuration: top_k, n_group or group_size unsupported";
+    case COLI_MOE_EDEVICE: return "HIP launch or runtime error";
+    case COLI_MOE_EARG: return "bad argument: NULL or misaligned pointer, unsupported dimension";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"
