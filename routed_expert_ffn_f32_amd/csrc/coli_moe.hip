@@ -29,15 +29,15 @@ enum Kernel {
 };
 
 const char *const kKernelNames[COLI_MOE_N_KERNELS] = {
-    "router_logits", "router_select", "dispatch",       "expert_gemv_gate_up",
-    "expert_gemv_down", "combine",    "expert_mfma_gate_up", "expert_mfma_down"};
+    "router_logits",    "router_select_dispatch", "dispatch",           "expert_gemv_gate_up",
+    "expert_gemv_down", "combine",                "expert_mfma_gate_up", "expert_mfma_down"};
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 // Byte offsets of the workspace regions.
 struct Layout {
-  size_t wrT, logits, idx, w, offsets, sorted_ids, inv, active, n_active, mid, y, total;
+  size_t wrP, logits, xq, xs, idx, w, offsets, sorted_ids, inv, active, n_active, mq, ms, y, total;
 };
 
 bool config_ok(const coli_moe_config_t &c, int *code) {
@@ -64,9 +64,12 @@ Layout layout_of(const coli_moe_config_t &c) {
   const size_t T = (size_t)c.max_tokens, E = (size_t)c.n_experts, k = (size_t)c.top_k;
   const size_t h = (size_t)c.hidden, I = (size_t)c.inter;
   const size_t P = T * k + (c.n_shared ? T : 0);  // expert-output rows
+  const size_t planes = 6;  // digit planes per activation row
   size_t o = 0;
-  L.wrT = o;        o = align_up(o + E * h * 4);
+  L.wrP = o;        o = align_up(o + coli::router_permuted_floats(c.hidden, c.n_experts) * 4);
   L.logits = o;     o = align_up(o + T * E * 4);
+  L.xq = o;         o = align_up(o + T * planes * (h / 8) * 4);
+  L.xs = o;         o = align_up(o + T * (h / 64) * 4);
   L.idx = o;        o = align_up(o + T * k * 4);
   L.w = o;          o = align_up(o + T * k * 4);
   L.offsets = o;    o = align_up(o + (E + 1) * 4);
@@ -74,7 +77,8 @@ Layout layout_of(const coli_moe_config_t &c) {
   L.inv = o;        o = align_up(o + T * k * 4);
   L.active = o;     o = align_up(o + E * 4);
   L.n_active = o;   o = align_up(o + 4);
-  L.mid = o;        o = align_up(o + P * I * 4);
+  L.mq = o;         o = align_up(o + P * planes * (I / 8) * 4);
+  L.ms = o;         o = align_up(o + P * (I / 64) * 4);
   L.y = o;          o = align_up(o + P * h * 4);
   L.total = o;
   return L;
@@ -163,7 +167,7 @@ int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe
   m->prof_calls_done = 0;
   m->prof_used = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (coli::launch_router_transpose(w->router_w, at<float>(m, L.wrT), cfg->hidden, cfg->n_experts, s) !=
+  if (coli::launch_router_permute(w->router_w, at<float>(m, L.wrP), cfg->hidden, cfg->n_experts, s) !=
       hipSuccess) {
     delete m;
     return COLI_MOE_EDEVICE;
@@ -182,57 +186,66 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int E = c.n_experts, k = c.top_k, h = c.hidden, I = c.inter;
   float *logits = at<float>(m, L.logits);
+  uint32_t *xq = at<uint32_t>(m, L.xq);
+  float *xs = at<float>(m, L.xs);
   int32_t *idx = at<int32_t>(m, L.idx);
   float *wsel = at<float>(m, L.w);
   int32_t *offsets = at<int32_t>(m, L.offsets), *sorted_ids = at<int32_t>(m, L.sorted_ids);
   int32_t *inv = at<int32_t>(m, L.inv), *active = at<int32_t>(m, L.active);
   int32_t *n_active = at<int32_t>(m, L.n_active);
-  float *mid = at<float>(m, L.mid), *y = at<float>(m, L.y);
+  float *y = at<float>(m, L.y);
+  const float *bias = m->w.sel_bias;
+  const float rsf = c.routed_scaling_factor;
 
   hipError_t e;
+  // 1. router logits, and the hidden rows in digit-plane form
   e = timed(m, K_ROUTER_LOGITS, s, [&] {
-    return coli::launch_router_logits(hidden, at<float>(m, L.wrT), T, h, E, logits, s);
+    return coli::launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, xq, xs, s);
   });
   if (e != hipSuccess) return COLI_MOE_EDEVICE;
-  e = timed(m, K_ROUTER_SELECT, s, [&] {
-    return coli::launch_router_select(logits, m->w.sel_bias, T, E, k, c.routed_scaling_factor, idx, wsel, s);
-  });
-  if (e != hipSuccess) return COLI_MOE_EDEVICE;
-  e = timed(m, K_DISPATCH, s, [&] {
-    return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
-  });
-  if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  // 2. selection and dispatch (one workgroup for small batches)
+  if ((int64_t)T * k <= coli::kFusedDispatchMax) {
+    e = timed(m, K_ROUTER_SELECT, s, [&] {
+      return coli::launch_select_dispatch(logits, bias, T, E, k, rsf, idx, wsel, offsets, sorted_ids, inv, active,
+                                          n_active, s);
+    });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  } else {
+    e = timed(m, K_ROUTER_SELECT, s,
+              [&] { return coli::launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    e = timed(m, K_DISPATCH, s, [&] {
+      return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
+    });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  }
 
-  coli::GemvProblem P{};
-  P.offsets = offsets;
-  P.sorted_ids = sorted_ids;
-  P.active = active;
-  P.n_active = n_active;
+  // 3. experts: gate/up with SwiGLU, down, weighted combine
+  coli::DecodeProblem P{};
+  P.gate = {m->w.gate_q, m->w.gate_s};
+  P.up = {m->w.up_q, m->w.up_s};
+  P.down = {m->w.down_q, m->w.down_s};
+  P.sh_gate = {m->w.sh_gate_q, m->w.sh_gate_s};
+  P.sh_up = {m->w.sh_up_q, m->w.sh_up_s};
+  P.sh_down = {m->w.sh_down_q, m->w.sh_down_s};
+  P.h = h;
+  P.I = I;
   P.T = T;
   P.k = k;
   P.E = E;
   P.n_routed_slots = E < T * k ? E : T * k;
   P.has_shared = c.n_shared;
-  // gate and up: [I][h] per expert
-  P.a = {m->w.gate_q, m->w.gate_s};
-  P.b = {m->w.up_q, m->w.up_s};
-  P.sh_a = {m->w.sh_gate_q, m->w.sh_gate_s};
-  P.sh_b = {m->w.sh_up_q, m->w.sh_up_s};
-  P.rows = I;
-  P.cols = h;
-  P.x = hidden;
-  P.out = mid;
+  P.xq = xq;
+  P.xs = xs;
+  P.mq = at<uint32_t>(m, L.mq);
+  P.ms = at<float>(m, L.ms);
+  P.y = y;
+  P.offsets = offsets;
+  P.sorted_ids = sorted_ids;
+  P.active = active;
+  P.n_active = n_active;
   e = timed(m, K_GATE_UP, s, [&] { return coli::launch_gemv_gate_up(P, s); });
   if (e != hipSuccess) return COLI_MOE_EDEVICE;
-  // down: [h][I] per expert
-  P.a = {m->w.down_q, m->w.down_s};
-  P.b = {nullptr, nullptr};
-  P.sh_a = {m->w.sh_down_q, m->w.sh_down_s};
-  P.sh_b = {nullptr, nullptr};
-  P.rows = h;
-  P.cols = I;
-  P.x = mid;
-  P.out = y;
   e = timed(m, K_DOWN, s, [&] { return coli::launch_gemv_down(P, s); });
   if (e != hipSuccess) return COLI_MOE_EDEVICE;
   e = timed(m, K_COMBINE, s, [&] { return coli::launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });

@@ -1,0 +1,133 @@
+// Stable counting sort of (token, slot) assignments by expert, as a device
+// function run by one whole workgroup of kDispatchThreads threads.
+//
+// Source: cf-1.com Colibri article, section 3.3, colibri_forward step 3 --
+// per-expert counts, a prefix sum into per-expert offsets, then a scatter of
+// the tokens by expert id; section 2.2 shows the grouping on six tokens.
+//
+// Output (assignment a = t*k + j, n = T*k):
+//   offsets[E+1]   exclusive prefix sum of the per-expert counts
+//   sorted_ids[n]  assignments grouped by expert ascending, a ascending inside
+//   inv[n]         position of assignment a in sorted_ids
+//   active[E]      experts with at least one assignment, ascending
+//   n_active[1]    how many
+//
+// Wave w owns a contiguous range of assignments.  Within a 64-assignment
+// chunk, lanes with equal keys are found with ballots over the key bits; the
+// rank of a lane among its equals is the popcount of the lower lanes of its
+// match mask.  Pass 1 builds one histogram per wave in LDS; the workgroup
+// then turns them into per-(wave, expert) start positions; pass 2 repeats
+// the chunk walk and scatters.  Positions depend only on the data, so the
+// result is identical on every run.
+#pragma once
+
+#include "internal.h"
+
+namespace coli {
+
+// Lanes of this wave holding the same (valid) key as the calling lane.
+__device__ __forceinline__ uint64_t match_mask(int key, bool valid, int key_bits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < key_bits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t ones = __ballot(valid && bit);
+    m &= bit ? ones : ~ones;
+  }
+  return m;
+}
+
+// `idx` may point to global or shared memory.  Keys outside [0, E) are
+// clamped into it (unspecified but in-bounds result).
+__device__ __forceinline__ void dispatch_block(const int32_t *idx, int n, int E, int32_t *__restrict__ offsets,
+                                               int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv,
+                                               int32_t *__restrict__ active, int32_t *__restrict__ n_active) {
+  constexpr int kWaves = kDispatchThreads / kWave;  // 16
+  __shared__ int32_t hist[kWaves][kMaxExperts];     // counts, then start positions
+  __shared__ int32_t wave_sum[kWaves];
+  __shared__ int32_t wave_act[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int key_bits = 0;
+  while ((1 << key_bits) < E) ++key_bits;
+
+  for (int e = lane; e < E; e += 64) hist[wave][e] = 0;
+  const int per_wave = ((n + kWaves - 1) / kWaves + 63) & ~63;
+  const int lo = min(n, wave * per_wave), hi = min(n, lo + per_wave);
+  __syncthreads();
+
+  // pass 1: per-wave histograms
+  for (int base = lo; base < hi; base += 64) {
+    const int a = base + lane;
+    const bool valid = a < hi;
+    int key = valid ? idx[a] : 0;
+    key = min(max(key, 0), E - 1);
+    const uint64_t m = match_mask(key, valid, key_bits);
+    const bool leader = valid && ((m & ((1ull << lane) - 1)) == 0);
+    if (leader) hist[wave][key] += __popcll(m);
+  }
+  __syncthreads();
+
+  // per expert: start of each wave's share (exclusive over waves), total count
+  int count = 0;
+  if (tid < E) {
+    for (int w = 0; w < kWaves; ++w) {
+      const int v = hist[w][tid];
+      hist[w][tid] = count;
+      count += v;
+    }
+  }
+  // exclusive scan of the counts over experts (one expert per thread)
+  const int flag = (tid < E && count > 0) ? 1 : 0;
+  int incl = count, incl_f = flag;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d), vf = __shfl_up(incl_f, d);
+    if (lane >= d) {
+      incl += v;
+      incl_f += vf;
+    }
+  }
+  if (lane == 63) {
+    wave_sum[wave] = incl;
+    wave_act[wave] = incl_f;
+  }
+  __syncthreads();
+  int before = 0, before_f = 0;
+  for (int w = 0; w < wave; ++w) {
+    before += wave_sum[w];
+    before_f += wave_act[w];
+  }
+  const int start = before + incl - count;  // offsets[tid]
+  const int act_pos = before_f + incl_f - flag;
+  if (tid < E) {
+    offsets[tid] = start;
+    if (flag) active[act_pos] = tid;
+    for (int w = 0; w < kWaves; ++w) hist[w][tid] += start;
+  }
+  if (tid == E - 1) {
+    offsets[E] = start + count;
+    *n_active = act_pos + flag;
+  }
+  __syncthreads();
+
+  // pass 2: scatter; equal keys of a chunk take consecutive positions in lane
+  // order, chunks in order, waves in order
+  for (int base = lo; base < hi; base += 64) {
+    const int a = base + lane;
+    const bool valid = a < hi;
+    int key = valid ? idx[a] : 0;
+    key = min(max(key, 0), E - 1);
+    const uint64_t m = match_mask(key, valid, key_bits);
+    const int rank = __popcll(m & ((1ull << lane) - 1));
+    const int pos = hist[wave][key] + rank;
+    if (valid) {
+      sorted_ids[pos] = a;
+      inv[a] = pos;
+    }
+    // every lane has read its start before the leader moves it on
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == 0) hist[wave][key] = pos + __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace coli

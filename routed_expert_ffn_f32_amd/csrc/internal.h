@@ -9,29 +9,39 @@
 
 namespace coli {
 
-constexpr int kWave = 64;           // CDNA wavefront width
-constexpr int kMaxExperts = 512;    // dispatch keeps per-wave histograms of E bins in LDS
+constexpr int kWave = 64;              // CDNA wavefront width
+constexpr int kMaxExperts = 512;       // dispatch keeps per-wave histograms of E bins in LDS
 constexpr int kMaxTopK = 32;
 constexpr int kDispatchThreads = 1024;
+constexpr int kFusedDispatchMax = 4096;  // T*k up to which selection and dispatch share a launch
 
 // ---------------------------------------------------------------------------
 // Routing (router.hip)
 // ---------------------------------------------------------------------------
 
-// wrT[e][i] = wr[i][e]: the router stored expert-major so that lane l of a
-// wave reads element l + 64m of expert e with a coalesced load.
-hipError_t launch_router_transpose(const float *wr, float *wrT, int h, int E, hipStream_t s);
+// Floats of the lane-permuted router copy for (h, E).
+size_t router_permuted_floats(int h, int E);
+
+// wrP[e][b][l][i] = wr[l + 64(4b + i)][e]: the router stored so that lane l
+// of a wave reads its four consecutive chain elements as one float4.
+hipError_t launch_router_permute(const float *wr, float *wrP, int h, int E, hipStream_t s);
 
 // logits[t][e] = sum_i x[t][i] wr[i][e] in the fixed float32 order: lane l of
 // the wave owning (t, e) keeps p_l = fma(x[l+64m], w[l+64m], p_l) over
 // m = 0..h/64-1, then the 64 partials meet in an xor butterfly (32,16,..,1).
-hipError_t launch_router_logits(const float *x, const float *wrT, int T, int h, int E, float *logits,
-                                hipStream_t s);
+// The same launch writes the digit-plane form of x (xq, xs) for the experts.
+hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits,
+                                uint32_t *xq, float *xs, hipStream_t s);
 
 // One wave per token: sigmoid scores, biased key, top-k (key desc, index
 // asc), renormalised weights times rsf.
 hipError_t launch_router_select(const float *logits, const float *bias, int T, int E, int k, float rsf,
                                 int32_t *idx, float *w, hipStream_t s);
+
+// Selection of T tokens and the dispatch in one workgroup (T*k <= kFusedDispatchMax).
+hipError_t launch_select_dispatch(const float *logits, const float *bias, int T, int E, int k, float rsf,
+                                  int32_t *idx, float *w, int32_t *offsets, int32_t *sorted_ids, int32_t *inv,
+                                  int32_t *active, int32_t *n_active, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Dispatch (dispatch.hip): stable counting sort of assignments by expert.
@@ -47,26 +57,25 @@ struct ExpertTables {
   const float *s;    // [rows][cols/64] per expert
 };
 
-struct GemvProblem {
-  // Matrix A (gate in gate/up mode, down in down mode) and B (up; gate/up mode only).
-  ExpertTables a, b;          // routed, stacked over experts
-  ExpertTables sh_a, sh_b;    // shared expert (used when has_shared)
-  int rows, cols;             // of each matrix
-  const float *x;             // gate/up: hidden [T][h]; down: mid [P][I]
-  float *out;                 // gate/up: mid [P][I]; down: y [P][h]
-  const int32_t *offsets;     // [E+1]
-  const int32_t *sorted_ids;  // [T*k]
-  const int32_t *active;      // [E]
-  const int32_t *n_active;    // [1]
-  int T, k, E;
-  int n_routed_slots;         // min(E, T*k): grid slots for routed experts
+struct DecodeProblem {
+  ExpertTables gate, up, down;           // routed experts, stacked
+  ExpertTables sh_gate, sh_up, sh_down;  // shared expert
+  int h, I, T, k, E;
+  int n_routed_slots;  // min(E, T*k): grid slots for routed experts
   int has_shared;
+  const uint32_t *xq;  // hidden rows as digit planes [T][6][h/8]
+  const float *xs;     // and group scales [T][h/64]
+  uint32_t *mq;        // expert intermediates as digit planes [P][6][I/8], P = T*k + T*has_shared
+  float *ms;           // and group scales [P][I/64]
+  float *y;            // expert outputs [P][h]
+  const int32_t *offsets, *sorted_ids, *active, *n_active;
 };
 
-// gate/up: mid[p][i] = silu(g) * u for every assignment position p (routed:
-// p = sorted position; shared: p = T*k + t).  down: y[p][r] = Wd[r] . mid[p].
-hipError_t launch_gemv_gate_up(const GemvProblem &P, hipStream_t s);
-hipError_t launch_gemv_down(const GemvProblem &P, hipStream_t s);
+// gate/up: mid = silu(Wg x) * (Wu x) for every assignment position p
+// (routed: p = sorted position; shared: p = T*k + t), written as digit planes.
+hipError_t launch_gemv_gate_up(const DecodeProblem &P, hipStream_t s);
+// down: y[p] = Wd mid[p].
+hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s);
 
 // out[t] = sum_j w[t*k+j] y[inv[t*k+j]] + (shared ? y[T*k + t] : 0)
 hipError_t launch_combine(const float *y, const float *w, const int32_t *inv, int T, int k, int h,

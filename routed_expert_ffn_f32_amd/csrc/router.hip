@@ -12,7 +12,9 @@
 //
 // Compiled with -ffp-contract=off and correctly rounded float32 division, so
 // the only fused multiply-adds are the explicit __builtin_fmaf calls.
+#include "dispatch_block.h"
 #include "internal.h"
+#include "wave.h"
 
 namespace coli {
 namespace {
@@ -55,55 +57,81 @@ __device__ float exp_spec(float y) {
 
 __device__ __forceinline__ float sigmoid_spec(float z) { return 1.0f / (1.0f + exp_spec(-z)); }
 
-__global__ __launch_bounds__(256) void router_transpose_kernel(const float *__restrict__ wr,
-                                                               float *__restrict__ wrT, int h, int E) {
-  __shared__ float tile[32][33];
-  const int e0 = blockIdx.x * 32, i0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  for (int r = ty; r < 32; r += 8) {
-    const int i = i0 + r, e = e0 + tx;
-    tile[r][tx] = (i < h && e < E) ? wr[(size_t)i * E + e] : 0.0f;
-  }
-  __syncthreads();
-  for (int r = ty; r < 32; r += 8) {
-    const int e = e0 + r, i = i0 + tx;
-    if (e < E && i < h) wrT[(size_t)e * h + i] = tile[tx][r];
+// wrP[e][b][l][i] = wr[l + 64 (4b + i)][e] (0 where 4b + i >= h/64): lane l's
+// four consecutive chain elements form one float4.
+__global__ __launch_bounds__(256) void router_permute_kernel(const float *__restrict__ wr,
+                                                             float *__restrict__ wrP, int h, int E) {
+  const int M = h >> 6, MB = (M + 3) >> 2;
+  const size_t n = (size_t)E * MB * 256;
+  for (size_t o = (size_t)blockIdx.x * 256 + threadIdx.x; o < n; o += (size_t)gridDim.x * 256) {
+    const int i = (int)(o & 3), l = (int)((o >> 2) & 63);
+    const size_t eb = o >> 8;
+    const int b = (int)(eb % MB), e = (int)(eb / MB);
+    const int m = 4 * b + i;
+    wrP[o] = m < M ? wr[(size_t)(l + 64 * m) * E + e] : 0.0f;
   }
 }
 
-// One wave computes TPW tokens x EPW experts.  Lane l owns the chain of
-// elements l + 64m; after the chains, the xor butterfly leaves the full sum
-// in every lane.
+// Logits.  One wave computes TPW tokens x EPW experts.  Lane l owns the chain
+// of elements l + 64m, m ascending; the xor butterfly (32, 16, ..., 1) then
+// leaves the full sum in every lane.
 template <int EPW, int TPW>
-__global__ __launch_bounds__(256) void router_logits_kernel(const float *__restrict__ x,
-                                                            const float *__restrict__ wrT, int T, int h,
-                                                            int E, float *__restrict__ logits) {
+__device__ __forceinline__ void logits_tile(const float *__restrict__ x, const float *__restrict__ wrP, int T,
+                                            int h, int E, int t0, int e0, float *__restrict__ logits) {
+  // blocks of 4 chain steps per float4; CH blocks are loaded before any is used
+  constexpr int CH = (EPW * TPW <= 2) ? 8 : 2;
   const int lane = threadIdx.x & 63;
-  const int e0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * EPW;
-  const int t0 = blockIdx.y * TPW;
-  if (e0 >= E) return;  // uniform over the wave
-  const int M = h >> 6;
+  const int M = h >> 6, MB = (M + 3) >> 2, MBfull = M >> 2;
   const float *xp[TPW];
-  const float *wp[EPW];
+  const float4 *wp[EPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) xp[t] = x + (size_t)min(t0 + t, T - 1) * h + lane;
 #pragma unroll
-  for (int e = 0; e < EPW; ++e) wp[e] = wrT + (size_t)min(e0 + e, E - 1) * h + lane;
+  for (int e = 0; e < EPW; ++e)
+    wp[e] = reinterpret_cast<const float4 *>(wrP) + ((size_t)min(e0 + e, E - 1) * MB) * 64 + lane;
   float acc[TPW][EPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int e = 0; e < EPW; ++e) acc[t][e] = 0.0f;
-  for (int m = 0; m < M; ++m) {
-    float xv[TPW], wv[EPW];
+  int b0 = 0;
+  for (; b0 + CH <= MBfull; b0 += CH) {
+    float4 wv[CH][EPW];
+    float xv[CH][4][TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) xv[t] = xp[t][m * 64];
+    for (int u = 0; u < CH; ++u)
 #pragma unroll
-    for (int e = 0; e < EPW; ++e) wv[e] = wp[e][m * 64];
+      for (int e = 0; e < EPW; ++e) wv[u][e] = wp[e][(size_t)(b0 + u) * 64];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int u = 0; u < CH; ++u)
 #pragma unroll
-      for (int e = 0; e < EPW; ++e) acc[t][e] = __builtin_fmaf(xv[t], wv[e], acc[t][e]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) xv[u][i][t] = xp[t][(4 * (b0 + u) + i) * 64];
+#pragma unroll
+    for (int u = 0; u < CH; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+          for (int e = 0; e < EPW; ++e) {
+            const float w = i == 0 ? wv[u][e].x : i == 1 ? wv[u][e].y : i == 2 ? wv[u][e].z : wv[u][e].w;
+            acc[t][e] = __builtin_fmaf(xv[u][i][t], w, acc[t][e]);
+          }
+  }
+  // remaining chain steps one at a time, in order
+  for (int m = 4 * b0; m < M; ++m) {
+    const int b = m >> 2, i = m & 3;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const float xv = xp[t][m * 64];
+#pragma unroll
+      for (int e = 0; e < EPW; ++e) {
+        const float *w4 = reinterpret_cast<const float *>(wp[e] + (size_t)b * 64);
+        acc[t][e] = __builtin_fmaf(xv, w4[i], acc[t][e]);
+      }
+    }
   }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1)
@@ -120,94 +148,197 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
   }
 }
 
-// (c, e) beats (oc, oe) when c is larger, or equal with a smaller index.
-__device__ __forceinline__ bool beats(float c, int e, float oc, int oe) {
-  return c > oc || (c == oc && e < oe);
+// One launch: blocks [0, n_logit_blocks) compute logits (4 waves, one tile
+// each); the remaining blocks write the digit-plane form of the hidden rows
+// (256 words of 8 columns per block) for the expert kernels.
+template <int EPW, int TPW>
+__global__ __launch_bounds__(256) void router_logits_kernel(const float *__restrict__ x,
+                                                            const float *__restrict__ wrP, int T, int h, int E,
+                                                            float *__restrict__ logits, int n_logit_blocks,
+                                                            uint32_t *__restrict__ xq, float *__restrict__ xs) {
+  const int bid = blockIdx.x;
+  if (bid < n_logit_blocks) {
+    const int egroups = (E + 4 * EPW - 1) / (4 * EPW);
+    const int tg = bid / egroups, eg = bid % egroups;
+    const int e0 = (eg * 4 + (threadIdx.x >> 6)) * EPW;
+    if (e0 >= E) return;  // uniform over the wave
+    logits_tile<EPW, TPW>(x, wrP, T, h, E, tg * TPW, e0, logits);
+    return;
+  }
+  const int words = h >> 3;
+  const size_t wg = (size_t)(bid - n_logit_blocks) * 256 + threadIdx.x;  // word over all rows
+  const bool valid = wg < (size_t)T * words;
+  const size_t t = valid ? wg / words : 0;
+  const int w = valid ? (int)(wg % words) : 0;
+  float v[8];
+  if (valid) {
+    const float4 a = *reinterpret_cast<const float4 *>(x + t * h + 8 * w);
+    const float4 b = *reinterpret_cast<const float4 *>(x + t * h + 8 * w + 4);
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  // groups of 8 words never straddle a row (words % 8 == 0), so the eight
+  // lanes of a group share the row and the group
+  quantize_word(v, (w & 7) == 0, valid, xq + t * kPlanes * words + w, (size_t)words,
+                xs + t * (words >> 3) + (w >> 3));
 }
 
-// One wave per token.  Lane l holds experts l + 64r.  k rounds of a wave-wide
-// arg-max under (key desc, index asc); the winner's lane marks it taken.
+// ---------------------------------------------------------------------------
+// Selection.  Key of expert e: high word = the float key c = s + b mapped to
+// an unsigned integer with the same order (c is never -0: s >= +0), low word =
+// ~e; a larger 64-bit key is a better expert under (c desc, e asc).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ordered_bits(float c) {
+  const uint32_t u = __float_as_uint(c);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ void keep_max(uint32_t &hi, uint32_t &lo, uint32_t ohi, uint32_t olo) {
+  if (ohi > hi || (ohi == hi && olo > lo)) {
+    hi = ohi;
+    lo = olo;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_max64(uint32_t &hi, uint32_t &lo) {
+  const uint32_t ohi = (uint32_t)dpp_i<CTRL>((int)hi), olo = (uint32_t)dpp_i<CTRL>((int)lo);
+  keep_max(hi, lo, ohi, olo);
+}
+
+// Wave-wide max of the 64-bit key, uniform result.
+__device__ __forceinline__ uint64_t wave_max64(uint32_t hi, uint32_t lo) {
+  dpp_max64<kDppQuadXor1>(hi, lo);
+  dpp_max64<kDppQuadXor2>(hi, lo);
+  dpp_max64<kDppRowRor4>(hi, lo);
+  dpp_max64<kDppRowRor8>(hi, lo);
+  uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)hi, 0), bl = (uint32_t)__builtin_amdgcn_readlane((int)lo, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16)
+    keep_max(bh, bl, (uint32_t)__builtin_amdgcn_readlane((int)hi, r), (uint32_t)__builtin_amdgcn_readlane((int)lo, r));
+  return ((uint64_t)bh << 32) | bl;
+}
+
+// One wave selects the experts of one token (logits row l[0..E)): sigmoid
+// scores, biased keys, k rounds of wave arg-max, then den = sum of the
+// selected s in slot order and w_j = (s_j / den) * rsf.  Lane j < k returns
+// slot j in (e_out, w_out).
+__device__ __forceinline__ void select_token(const float *__restrict__ l, const float *__restrict__ bias, int E,
+                                             int k, float rsf, int &e_out, float &w_out) {
+  constexpr int R = kMaxExperts / kWave;
+  const int lane = threadIdx.x & 63;
+  float s[R], lv[R], bv[R];
+  uint32_t khi[R], klo[R];
+  // all loads first (clamped indices, no branches), then the arithmetic
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = min(lane + 64 * r, E - 1);
+    lv[r] = l[e];
+    bv[r] = bias ? bias[e] : 0.0f;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = lane + 64 * r;
+    const bool valid = e < E;
+    s[r] = valid ? sigmoid_spec(lv[r]) : 0.0f;
+    khi[r] = valid ? ordered_bits(s[r] + bv[r]) : 0u;
+    klo[r] = valid ? ~(uint32_t)e : 0u;
+  }
+  int my_e = 0;
+  float my_s = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t bh = 0u, bl = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) keep_max(bh, bl, khi[r], klo[r]);
+    const uint64_t best = wave_max64(bh, bl);
+    const int e = (int)~(uint32_t)best;  // uniform
+    const int owner = e & 63, rr = e >> 6;
+    float sv = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r == rr) {
+        sv = s[r];
+        if (lane == owner) khi[r] = klo[r] = 0u;  // taken
+      }
+    const float s_win = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv), owner));
+    if (lane == j) {
+      my_e = e;
+      my_s = s_win;
+    }
+  }
+  float den = 0.0f;
+  for (int j = 0; j < k; ++j) den = den + __shfl(my_s, j);
+  e_out = my_e;
+  w_out = (my_s / den) * rsf;
+}
+
 __global__ __launch_bounds__(256) void router_select_kernel(const float *__restrict__ logits,
                                                             const float *__restrict__ bias, int T, int E,
                                                             int k, float rsf, int32_t *__restrict__ idx,
                                                             float *__restrict__ wout) {
-  constexpr int R = kMaxExperts / kWave;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float s[R], c[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = lane + 64 * r;
-    if (e < E) {
-      s[r] = sigmoid_spec(logits[(size_t)t * E + e]);
-      c[r] = s[r] + (bias ? bias[e] : 0.0f);
-    } else {
-      s[r] = 0.0f;
-      c[r] = -__int_as_float(0x7f800000);
-    }
-  }
-  uint32_t taken = 0;
-  int my_e = 0;
-  float my_s = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bc = -__int_as_float(0x7f800000), bs = 0.0f;
-    int be = 0x7fffffff;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int e = lane + 64 * r;
-      if (e < E && !((taken >> r) & 1u) && beats(c[r], e, bc, be)) {
-        bc = c[r];
-        be = e;
-        bs = s[r];
-      }
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float oc = __shfl_xor(bc, d);
-      const int oe = __shfl_xor(be, d);
-      const float os = __shfl_xor(bs, d);
-      if (beats(oc, oe, bc, be)) {
-        bc = oc;
-        be = oe;
-        bs = os;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) {
-      my_e = be;
-      my_s = bs;
-    }
-  }
-  // den = ((s_0 + s_1) + s_2) + ... in slot order, identical in every lane
-  float den = 0.0f;
-  for (int j = 0; j < k; ++j) den = den + __shfl(my_s, j);
+  int e;
+  float w;
+  select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w);
   if (lane < k) {
-    idx[(size_t)t * k + lane] = my_e;
-    wout[(size_t)t * k + lane] = (my_s / den) * rsf;
+    idx[(size_t)t * k + lane] = e;
+    wout[(size_t)t * k + lane] = w;
   }
+}
+
+// Small batches: selection of every token and the dispatch in one workgroup
+// (16 waves); the selected ids go through LDS to the counting sort.
+__global__ __launch_bounds__(kDispatchThreads) void select_dispatch_kernel(
+    const float *__restrict__ logits, const float *__restrict__ bias, int T, int E, int k, float rsf,
+    int32_t *__restrict__ idx, float *__restrict__ wout, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int32_t *__restrict__ active,
+    int32_t *__restrict__ n_active) {
+  __shared__ int32_t sel[kFusedDispatchMax];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += kDispatchThreads / kWave) {
+    int e;
+    float w;
+    select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w);
+    if (lane < k) {
+      idx[(size_t)t * k + lane] = e;
+      wout[(size_t)t * k + lane] = w;
+      sel[t * k + lane] = e;
+    }
+  }
+  __syncthreads();
+  dispatch_block(sel, T * k, E, offsets, sorted_ids, inv, active, n_active);
 }
 
 }  // namespace
 
-hipError_t launch_router_transpose(const float *wr, float *wrT, int h, int E, hipStream_t s) {
-  dim3 grid((E + 31) / 32, (h + 31) / 32);
-  router_transpose_kernel<<<grid, 256, 0, s>>>(wr, wrT, h, E);
+hipError_t launch_router_permute(const float *wr, float *wrP, int h, int E, hipStream_t s) {
+  const int MB = ((h >> 6) + 3) >> 2;
+  const size_t n = (size_t)E * MB * 256;
+  const size_t want = (n + 255) / 256;
+  const int blocks = (int)(want < 4096 ? want : 4096);
+  router_permute_kernel<<<blocks, 256, 0, s>>>(wr, wrP, h, E);
   return hipGetLastError();
 }
 
-hipError_t launch_router_logits(const float *x, const float *wrT, int T, int h, int E, float *logits,
-                                hipStream_t s) {
+size_t router_permuted_floats(int h, int E) { return (size_t)E * ((((h >> 6) + 3) >> 2)) * 256; }
+
+hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits, uint32_t *xq,
+                                float *xs, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  const int qblocks = (int)(((size_t)T * (h >> 3) + 255) / 256);
   if (T < 4) {
-    dim3 grid((E + 3) / 4, T);
-    router_logits_kernel<1, 1><<<grid, 256, 0, s>>>(x, wrT, T, h, E, logits);
+    const int nlb = T * ((E + 3) / 4);
+    router_logits_kernel<1, 1><<<nlb + qblocks, 256, 0, s>>>(x, wrP, T, h, E, logits, nlb, xq, xs);
   } else if (T < 64) {
-    dim3 grid((E + 7) / 8, (T + 3) / 4);
-    router_logits_kernel<2, 4><<<grid, 256, 0, s>>>(x, wrT, T, h, E, logits);
+    const int nlb = ((T + 3) / 4) * ((E + 7) / 8);
+    router_logits_kernel<2, 4><<<nlb + qblocks, 256, 0, s>>>(x, wrP, T, h, E, logits, nlb, xq, xs);
   } else {
-    dim3 grid((E + 15) / 16, (T + 3) / 4);
-    router_logits_kernel<4, 4><<<grid, 256, 0, s>>>(x, wrT, T, h, E, logits);
+    const int nlb = ((T + 3) / 4) * ((E + 15) / 16);
+    router_logits_kernel<4, 4><<<nlb + qblocks, 256, 0, s>>>(x, wrP, T, h, E, logits, nlb, xq, xs);
   }
   return hipGetLastError();
 }
@@ -216,6 +347,14 @@ hipError_t launch_router_select(const float *logits, const float *bias, int T, i
                                 int32_t *idx, float *w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   router_select_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, bias, T, E, k, rsf, idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_dispatch(const float *logits, const float *bias, int T, int E, int k, float rsf,
+                                  int32_t *idx, float *w, int32_t *offsets, int32_t *sorted_ids, int32_t *inv,
+                                  int32_t *active, int32_t *n_active, hipStream_t s) {
+  select_dispatch_kernel<<<1, kDispatchThreads, 0, s>>>(logits, bias, T, E, k, rsf, idx, w, offsets, sorted_ids,
+                                                        inv, active, n_active);
   return hipGetLastError();
 }
 
