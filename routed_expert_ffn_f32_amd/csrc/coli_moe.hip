@@ -31,6 +31,7 @@ enum Kernel {
 const char *const kKernelNames[COLI_MOE_N_KERNELS] = {
     "router_logits",    "router_select_dispatch", "dispatch",           "expert_gemv_gate_up",
     "expert_gemv_down", "combine",                "expert_mfma_gate_up", "expert_mfma_down"};
+// (small batches: "expert_gemv_down" is the down projection fused with the combine)
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
@@ -69,7 +70,7 @@ Layout layout_of(const coli_moe_config_t &c) {
   L.wrP = o;        o = align_up(o + coli::router_permuted_floats(c.hidden, c.n_experts) * 4);
   L.logits = o;     o = align_up(o + T * E * 4);
   L.xq = o;         o = align_up(o + T * planes * (h / 8) * 4);
-  L.xs = o;         o = align_up(o + T * (h / 64) * 4);
+  L.xs = o;         o = align_up(o + T * (h / 32) * 4);
   L.idx = o;        o = align_up(o + T * k * 4);
   L.w = o;          o = align_up(o + T * k * 4);
   L.offsets = o;    o = align_up(o + (E + 1) * 4);
@@ -78,7 +79,7 @@ Layout layout_of(const coli_moe_config_t &c) {
   L.active = o;     o = align_up(o + E * 4);
   L.n_active = o;   o = align_up(o + 4);
   L.mq = o;         o = align_up(o + P * planes * (I / 8) * 4);
-  L.ms = o;         o = align_up(o + P * (I / 64) * 4);
+  L.ms = o;         o = align_up(o + P * (I / 32) * 4);
   L.y = o;          o = align_up(o + P * h * 4);
   L.total = o;
   return L;
@@ -203,24 +204,6 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
     return coli::launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, xq, xs, s);
   });
   if (e != hipSuccess) return COLI_MOE_EDEVICE;
-  // 2. selection and dispatch (one workgroup for small batches)
-  if ((int64_t)T * k <= coli::kFusedDispatchMax) {
-    e = timed(m, K_ROUTER_SELECT, s, [&] {
-      return coli::launch_select_dispatch(logits, bias, T, E, k, rsf, idx, wsel, offsets, sorted_ids, inv, active,
-                                          n_active, s);
-    });
-    if (e != hipSuccess) return COLI_MOE_EDEVICE;
-  } else {
-    e = timed(m, K_ROUTER_SELECT, s,
-              [&] { return coli::launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
-    if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    e = timed(m, K_DISPATCH, s, [&] {
-      return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
-    });
-    if (e != hipSuccess) return COLI_MOE_EDEVICE;
-  }
-
-  // 3. experts: gate/up with SwiGLU, down, weighted combine
   coli::DecodeProblem P{};
   P.gate = {m->w.gate_q, m->w.gate_s};
   P.up = {m->w.up_q, m->w.up_s};
@@ -235,21 +218,54 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
   P.E = E;
   P.n_routed_slots = E < T * k ? E : T * k;
   P.has_shared = c.n_shared;
+  P.rsf = rsf;
+  P.logits = logits;
+  P.bias = bias;
   P.xq = xq;
   P.xs = xs;
   P.mq = at<uint32_t>(m, L.mq);
   P.ms = at<float>(m, L.ms);
   P.y = y;
-  P.offsets = offsets;
+  P.idx = idx;
+  P.wsel = wsel;
   P.sorted_ids = sorted_ids;
+  P.inv = inv;
+  P.offsets = offsets;
   P.active = active;
   P.n_active = n_active;
-  e = timed(m, K_GATE_UP, s, [&] { return coli::launch_gemv_gate_up(P, s); });
-  if (e != hipSuccess) return COLI_MOE_EDEVICE;
-  e = timed(m, K_DOWN, s, [&] { return coli::launch_gemv_down(P, s); });
-  if (e != hipSuccess) return COLI_MOE_EDEVICE;
-  e = timed(m, K_COMBINE, s, [&] { return coli::launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
-  if (e != hipSuccess) return COLI_MOE_EDEVICE;
+
+  if (coli::small_batch(T, k)) {
+    // 2. gate/up (each routed block routes the batch itself), 3. down + combine
+    e = timed(m, K_GATE_UP, s, [&] { return coli::launch_gemv_gate_up(P, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    e = timed(m, K_DOWN, s, [&] { return coli::launch_down_combine(P, out, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  } else {
+    // 2. selection and dispatch (one workgroup up to kFusedDispatchMax assignments)
+    if ((int64_t)T * k <= coli::kFusedDispatchMax) {
+      e = timed(m, K_ROUTER_SELECT, s, [&] {
+        return coli::launch_select_dispatch(logits, bias, T, E, k, rsf, idx, wsel, offsets, sorted_ids, inv,
+                                            active, n_active, s);
+      });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    } else {
+      e = timed(m, K_ROUTER_SELECT, s,
+                [&] { return coli::launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+      e = timed(m, K_DISPATCH, s, [&] {
+        return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
+      });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    }
+    // 3. gate/up, down, weighted combine
+    e = timed(m, K_GATE_UP, s, [&] { return coli::launch_gemv_gate_up(P, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    e = timed(m, K_DOWN, s, [&] { return coli::launch_gemv_down(P, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    e = timed(m, K_COMBINE, s,
+              [&] { return coli::launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  }
 
   m->last_T = T;
   if (m->prof_calls_left > 0) {

@@ -14,6 +14,8 @@ constexpr int kMaxExperts = 512;       // dispatch keeps per-wave histograms of 
 constexpr int kMaxTopK = 32;
 constexpr int kDispatchThreads = 1024;
 constexpr int kFusedDispatchMax = 4096;  // T*k up to which selection and dispatch share a launch
+constexpr int kSmallT = 4;               // small batches: routing recomputed inside each expert block
+constexpr int kSmallAssign = 64;         // and T*k at most one wave of assignments
 
 // ---------------------------------------------------------------------------
 // Routing (router.hip)
@@ -63,21 +65,32 @@ struct DecodeProblem {
   int h, I, T, k, E;
   int n_routed_slots;  // min(E, T*k): grid slots for routed experts
   int has_shared;
-  const uint32_t *xq;  // hidden rows as digit planes [T][6][h/8]
-  const float *xs;     // and group scales [T][h/64]
-  uint32_t *mq;        // expert intermediates as digit planes [P][6][I/8], P = T*k + T*has_shared
-  float *ms;           // and group scales [P][I/64]
-  float *y;            // expert outputs [P][h]
-  const int32_t *offsets, *sorted_ids, *active, *n_active;
+  float rsf;
+  const float *logits;  // [T][E] router logits (small batches route from them)
+  const float *bias;    // [E] selection bias or NULL
+  const uint32_t *xq;   // hidden rows as digit planes [T][6][h/8]
+  const float *xs;      // and block scales [T][h/32]
+  uint32_t *mq;         // expert intermediates as digit planes [P][6][I/8], P = T*k + T*has_shared
+  float *ms;            // and block scales [P][I/32]
+  float *y;             // expert outputs [P][h] (larger batches)
+  // routing and dispatch: written by the gate/up launch for small batches,
+  // read by it otherwise
+  int32_t *idx, *sorted_ids, *inv, *offsets, *active, *n_active;
+  float *wsel;
 };
+
+// True when the batch takes the small-batch launch structure (routing inside
+// the gate/up blocks, down fused with the combine).
+bool small_batch(int T, int k);
 
 // gate/up: mid = silu(Wg x) * (Wu x) for every assignment position p
 // (routed: p = sorted position; shared: p = T*k + t), written as digit planes.
 hipError_t launch_gemv_gate_up(const DecodeProblem &P, hipStream_t s);
-// down: y[p] = Wd mid[p].
+// Small batches: out[t] = sum_j w[t,j] Wd_e mid[inv(t,j)] + Wd_sh mid[T*k + t].
+hipError_t launch_down_combine(const DecodeProblem &P, float *out, hipStream_t s);
+// Larger batches: y[p] = Wd mid[p] ...
 hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s);
-
-// out[t] = sum_j w[t*k+j] y[inv[t*k+j]] + (shared ? y[T*k + t] : 0)
+// ... then out[t] = sum_j w[t*k+j] y[inv[t*k+j]] + (shared ? y[T*k + t] : 0).
 hipError_t launch_combine(const float *y, const float *w, const int32_t *inv, int T, int k, int h,
                           int has_shared, float *out, hipStream_t s);
 

@@ -14,48 +14,12 @@
 // the only fused multiply-adds are the explicit __builtin_fmaf calls.
 #include "dispatch_block.h"
 #include "internal.h"
+#include "select.h"
 #include "wave.h"
 
 namespace coli {
 namespace {
 
-__device__ __forceinline__ float pow2i(int n) { return __int_as_float((n + 127) << 23); }
-
-// e^y in float32: y = n ln2 + r, n = rint(y log2e), r by two fma steps with
-// ln 2 split into a 16-bit head (exact products n * head) and its float tail;
-// e^r = sum_{i<=7} r^i / i! in Horner form; scale by 2^n through the exponent
-// field, in two steps outside the normal range.
-__device__ float exp_spec(float y) {
-  const float kLog2e = 0x1.715476p+0f;
-  const float kLn2Hi = 0x1.62e4p-1f;
-  const float kLn2Lo = 0x1.7f7d1cp-20f;
-  const float kInv2 = 0x1p-1f;
-  const float kInv6 = 0x1.555556p-3f;
-  const float kInv24 = 0x1.555556p-5f;
-  const float kInv120 = 0x1.111112p-7f;
-  const float kInv720 = 0x1.6c16c2p-10f;
-  const float kInv5040 = 0x1.a01a02p-13f;
-  if (y != y) return y;
-  if (y > 89.0f) return __int_as_float(0x7f800000);
-  if (y < -104.0f) return 0.0f;
-  const float n = __builtin_rintf(y * kLog2e);
-  float r = __builtin_fmaf(-n, kLn2Hi, y);
-  r = __builtin_fmaf(-n, kLn2Lo, r);
-  float p = kInv5040;
-  p = __builtin_fmaf(p, r, kInv720);
-  p = __builtin_fmaf(p, r, kInv120);
-  p = __builtin_fmaf(p, r, kInv24);
-  p = __builtin_fmaf(p, r, kInv6);
-  p = __builtin_fmaf(p, r, kInv2);
-  p = __builtin_fmaf(p, r, 1.0f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  const int ni = (int)n;
-  if (ni > 127) return (p * pow2i(127)) * pow2i(ni - 127);
-  if (ni < -126) return (p * pow2i(ni + 64)) * pow2i(-64);
-  return p * pow2i(ni);
-}
-
-__device__ __forceinline__ float sigmoid_spec(float z) { return 1.0f / (1.0f + exp_spec(-z)); }
 
 // wrP[e][b][l][i] = wr[l + 64 (4b + i)][e] (0 where 4b + i >= h/64): lane l's
 // four consecutive chain elements form one float4.
@@ -179,111 +143,23 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = 0.0f;
   }
-  // groups of 8 words never straddle a row (words % 8 == 0), so the eight
-  // lanes of a group share the row and the group
-  quantize_word(v, (w & 7) == 0, valid, xq + t * kPlanes * words + w, (size_t)words,
-                xs + t * (words >> 3) + (w >> 3));
-}
-
-// ---------------------------------------------------------------------------
-// Selection.  Key of expert e: high word = the float key c = s + b mapped to
-// an unsigned integer with the same order (c is never -0: s >= +0), low word =
-// ~e; a larger 64-bit key is a better expert under (c desc, e asc).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t ordered_bits(float c) {
-  const uint32_t u = __float_as_uint(c);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ void keep_max(uint32_t &hi, uint32_t &lo, uint32_t ohi, uint32_t olo) {
-  if (ohi > hi || (ohi == hi && olo > lo)) {
-    hi = ohi;
-    lo = olo;
-  }
-}
-
-template <int CTRL>
-__device__ __forceinline__ void dpp_max64(uint32_t &hi, uint32_t &lo) {
-  const uint32_t ohi = (uint32_t)dpp_i<CTRL>((int)hi), olo = (uint32_t)dpp_i<CTRL>((int)lo);
-  keep_max(hi, lo, ohi, olo);
-}
-
-// Wave-wide max of the 64-bit key, uniform result.
-__device__ __forceinline__ uint64_t wave_max64(uint32_t hi, uint32_t lo) {
-  dpp_max64<kDppQuadXor1>(hi, lo);
-  dpp_max64<kDppQuadXor2>(hi, lo);
-  dpp_max64<kDppRowRor4>(hi, lo);
-  dpp_max64<kDppRowRor8>(hi, lo);
-  uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)hi, 0), bl = (uint32_t)__builtin_amdgcn_readlane((int)lo, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16)
-    keep_max(bh, bl, (uint32_t)__builtin_amdgcn_readlane((int)hi, r), (uint32_t)__builtin_amdgcn_readlane((int)lo, r));
-  return ((uint64_t)bh << 32) | bl;
-}
-
-// One wave selects the experts of one token (logits row l[0..E)): sigmoid
-// scores, biased keys, k rounds of wave arg-max, then den = sum of the
-// selected s in slot order and w_j = (s_j / den) * rsf.  Lane j < k returns
-// slot j in (e_out, w_out).
-__device__ __forceinline__ void select_token(const float *__restrict__ l, const float *__restrict__ bias, int E,
-                                             int k, float rsf, int &e_out, float &w_out) {
-  constexpr int R = kMaxExperts / kWave;
-  const int lane = threadIdx.x & 63;
-  float s[R], lv[R], bv[R];
-  uint32_t khi[R], klo[R];
-  // all loads first (clamped indices, no branches), then the arithmetic
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = min(lane + 64 * r, E - 1);
-    lv[r] = l[e];
-    bv[r] = bias ? bias[e] : 0.0f;
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = lane + 64 * r;
-    const bool valid = e < E;
-    s[r] = valid ? sigmoid_spec(lv[r]) : 0.0f;
-    khi[r] = valid ? ordered_bits(s[r] + bv[r]) : 0u;
-    klo[r] = valid ? ~(uint32_t)e : 0u;
-  }
-  int my_e = 0;
-  float my_s = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    uint32_t bh = 0u, bl = 0u;
-#pragma unroll
-    for (int r = 0; r < R; ++r) keep_max(bh, bl, khi[r], klo[r]);
-    const uint64_t best = wave_max64(bh, bl);
-    const int e = (int)~(uint32_t)best;  // uniform
-    const int owner = e & 63, rr = e >> 6;
-    float sv = 0.0f;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (r == rr) {
-        sv = s[r];
-        if (lane == owner) khi[r] = klo[r] = 0u;  // taken
-      }
-    const float s_win = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv), owner));
-    if (lane == j) {
-      my_e = e;
-      my_s = s_win;
-    }
-  }
-  float den = 0.0f;
-  for (int j = 0; j < k; ++j) den = den + __shfl(my_s, j);
-  e_out = my_e;
-  w_out = (my_s / den) * rsf;
+  // a 32-column block is 4 words and never straddles a row (words % 8 == 0),
+  // so the four lanes of a quad share the row and the block
+  quantize_word(v, (w & 3) == 0, valid, xq + t * kPlanes * words + w, (size_t)words,
+                xs + t * (words >> 2) + (w >> 2));
 }
 
 __global__ __launch_bounds__(256) void router_select_kernel(const float *__restrict__ logits,
                                                             const float *__restrict__ bias, int T, int E,
                                                             int k, float rsf, int32_t *__restrict__ idx,
                                                             float *__restrict__ wout) {
+  __shared__ SelectScratch sc[4];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   int e;
   float w;
-  select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w);
+  select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w, sc[threadIdx.x >> 6]);
   if (lane < k) {
     idx[(size_t)t * k + lane] = e;
     wout[(size_t)t * k + lane] = w;
@@ -298,11 +174,12 @@ __global__ __launch_bounds__(kDispatchThreads) void select_dispatch_kernel(
     int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int32_t *__restrict__ active,
     int32_t *__restrict__ n_active) {
   __shared__ int32_t sel[kFusedDispatchMax];
+  __shared__ SelectScratch sc[kDispatchThreads / kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int t = wave; t < T; t += kDispatchThreads / kWave) {
     int e;
     float w;
-    select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w);
+    select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w, sc[wave]);
     if (lane < k) {
       idx[(size_t)t * k + lane] = e;
       wout[(size_t)t * k + lane] = w;

@@ -26,6 +26,27 @@ __device__ __forceinline__ int dpp_i(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
 }
 
+// Raw buffer loads: the descriptor covers [base, base + bytes); lanes pass a
+// 32-bit byte offset (VGPR) and the wave a uniform one (SGPR).  Reads past
+// `bytes` return zero instead of faulting.
+using Rsrc = __amdgpu_buffer_rsrc_t;
+constexpr int kRawBufferDword3 = 0x00020000;  // gfx9-family raw buffer, 32-bit elements
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kRawBufferDword3);
+}
+
+__device__ __forceinline__ uint4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float bloadf(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Sum of v over the 64 lanes, returned uniformly (fixed combining order, so
 // the result is the same on every run).
 __device__ __forceinline__ float wave_sum(float v) {
@@ -38,43 +59,42 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// Max of v over lanes 8a..8a+7 (aligned groups of eight), in every lane.
-__device__ __forceinline__ float group8_max(float v) {
+// Max of v over the lanes 4a..4a+3 of a quad, in every lane of the quad.
+__device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
   v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
-  v = fmaxf(v, __shfl_xor(v, 4));
   return v;
 }
 
 // ---------------------------------------------------------------------------
 // Digit-plane activations.
 //
-// A row of `cols` float activations is stored per group of 64 columns as a
-// power-of-two scale s_g = 2^(E_g - 22), 2^E_g > max |x| over the group, and
-// integers N_c = rint(x_c / s_g) with |N_c| <= 2^22 (a 23-bit signed
-// mantissa shared by the group: block floating point).  N_c is written as six
-// balanced base-16 digits d_j in [-8, 7], N_c = sum_j 16^j d_j, and digit j of
-// columns 8w..8w+7 forms word w of plane j, column 8w+i in nibble i -- the
-// nibble order of the int4 weights, so v_dot8_i32_i4 on a weight word and a
-// plane word multiplies matching columns.  sum_c q_c x_c over a 32-column
-// half group is then s_g * sum_j 16^j dot8s_j, exact in int32
+// A row of `cols` float activations is stored per block of 32 columns (half a
+// weight group) as a power-of-two scale s_b = 2^(E_b - 22), 2^E_b > max |x|
+// over the block, and integers N_c = rint(x_c / s_b) with |N_c| <= 2^22 (a
+// 23-bit signed mantissa shared by the block: block floating point).  N_c is
+// written as six balanced base-16 digits d_j in [-8, 7], N_c = sum_j 16^j d_j,
+// and digit j of columns 8w..8w+7 forms word w of plane j, column 8w+i in
+// nibble i -- the nibble order of the int4 weights, so v_dot8_i32_i4 on a
+// weight word and a plane word multiplies matching columns.  sum_c q_c x_c
+// over a block is then s_b * sum_j 16^j dot8s_j, exact in int32
 // (|sum| <= 8 * 2^22 * 32 = 2^30).
-// Layout: planes [row][kPlanes][cols/8] uint32, scales [row][cols/64] float.
+// Layout: planes [row][kPlanes][cols/8] uint32, scales [row][cols/32] float.
 // ---------------------------------------------------------------------------
 constexpr int kPlanes = 6;
 constexpr int kMantBits = 22;
-constexpr int kMinExp = -100;  // groups with max |x| < 2^-101 quantise to zero
+constexpr int kMinExp = -100;  // blocks with max |x| < 2^-101 quantise to zero
 
-// One thread holds 8 consecutive columns (word w); lanes 8a..8a+7 of the wave
-// hold the 64 columns of one group, and every lane of the wave takes part
+// One thread holds 8 consecutive columns (word w); the four lanes of a quad
+// hold the 32 columns of one block, and every lane of the wave takes part
 // (padding lanes pass zeros and store = false).  Writes the plane words and,
-// from the group's first lane, the scale.
-__device__ __forceinline__ void quantize_word(const float v[8], bool first_of_group, bool store,
-                                              uint32_t *planes_w, size_t plane_stride, float *scale_g) {
+// from the block's first lane, the scale.
+__device__ __forceinline__ void quantize_word(const float v[8], bool first_of_block, bool store,
+                                              uint32_t *planes_w, size_t plane_stride, float *scale_b) {
   float m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-  m = group8_max(m);
+  m = quad_max(m);
   int e = 0;
   (void)__builtin_frexpf(m, &e);  // m < 2^e (m = 0 gives e = 0)
   e = m > 0.0f ? max(e, kMinExp) : kMinExp;
@@ -93,7 +113,7 @@ __device__ __forceinline__ void quantize_word(const float v[8], bool first_of_gr
     }
     if (store) planes_w[j * plane_stride] = word;
   }
-  if (store && first_of_group) *scale_g = to_real;
+  if (store && first_of_block) *scale_b = to_real;
 }
 
 // sum over 32 columns of weight codes (4 words) times the digit-plane
