@@ -172,7 +172,7 @@ int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, 
  * kernel (arrays of COLI_MOE_N_KERNELS entries, either may be NULL) and
  * stops recording.  Returns the number of forwards recorded, or -4/-3.
  */
-#define COLI_MOE_N_KERNELS 8
+#define COLI_MOE_N_KERNELS 10
 int coli_moe_profile_begin(coli_moe_t *m, int32_t max_calls);
 int coli_moe_profile_end(coli_moe_t *m, float *kernel_ms, int32_t *kernel_launches);
 /* Name of kernel i (0 <= i < COLI_MOE_N_KERNELS), a static string. */

@@ -28,7 +28,7 @@ COLI_MOE_ECAPACITY = -1
 COLI_MOE_EROUTING = -2
 COLI_MOE_EDEVICE = -3
 COLI_MOE_EARG = -4
-COLI_MOE_N_KERNELS = 8
+COLI_MOE_N_KERNELS = 10
 
 
 class ColiMoeError(RuntimeError):

@@ -26,11 +26,14 @@ enum Kernel {
   K_COMBINE = 5,
   K_MFMA_GATE_UP = 6,
   K_MFMA_DOWN = 7,
+  K_PREFILL_PREP = 8,
+  K_BUILD_TILES = 9,
 };
 
 const char *const kKernelNames[COLI_MOE_N_KERNELS] = {
-    "router_logits",    "router_select_dispatch", "dispatch",           "expert_gemv_gate_up",
-    "expert_gemv_down", "combine",                "expert_mfma_gate_up", "expert_mfma_down"};
+    "router_logits",    "router_select_dispatch", "dispatch",            "expert_gemv_gate_up",
+    "expert_gemv_down", "combine",                "expert_mfma_gate_up", "expert_mfma_down",
+    "prefill_to_bf16",  "build_tiles"};
 // (small batches: "expert_gemv_down" is the down projection fused with the combine)
 
 constexpr size_t kAlign = 256;
@@ -38,8 +41,14 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 // Byte offsets of the workspace regions.
 struct Layout {
-  size_t wrP, logits, xq, xs, idx, w, offsets, sorted_ids, inv, active, n_active, mq, ms, y, total;
+  size_t wrP, logits, xq, xs, idx, w, offsets, sorted_ids, inv, active, n_active, mq, ms, y;
+  size_t xb, midb, tiles, n_tiles;  // prefill path
+  size_t total;
 };
+
+// The prefill (MFMA) path needs 128-aligned h and I; T below the threshold,
+// or other shapes, take the GEMV path.
+bool prefill_shape(const coli_moe_config_t &c) { return c.hidden % 128 == 0 && c.inter % 128 == 0; }
 
 bool config_ok(const coli_moe_config_t &c, int *code) {
   if (c.hidden < 64 || c.hidden > 16384 || c.hidden % 64 || c.inter < 64 || c.inter > 16384 ||
@@ -81,6 +90,12 @@ Layout layout_of(const coli_moe_config_t &c) {
   L.mq = o;         o = align_up(o + P * planes * (I / 8) * 4);
   L.ms = o;         o = align_up(o + P * (I / 32) * 4);
   L.y = o;          o = align_up(o + P * h * 4);
+  const bool pre = prefill_shape(c) && (c.prefill_threshold == 0 ? 256 : c.prefill_threshold) <= c.max_tokens;
+  const size_t tiles = pre ? (size_t)coli::prefill_max_tiles(c.max_tokens, c.top_k, c.n_experts, c.n_shared) : 0;
+  L.xb = o;         o = align_up(o + (pre ? T * h * 2 : 0));
+  L.midb = o;       o = align_up(o + (pre ? P * I * 2 : 0));
+  L.tiles = o;      o = align_up(o + tiles * 8);
+  L.n_tiles = o;    o = align_up(o + 4);
   L.total = o;
   return L;
 }
@@ -198,12 +213,72 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
   const float *bias = m->w.sel_bias;
   const float rsf = c.routed_scaling_factor;
 
+  const bool prefill = T >= c.prefill_threshold && prefill_shape(c);
   hipError_t e;
-  // 1. router logits, and the hidden rows in digit-plane form
+  // 1. router logits (and, for the GEMV path, the hidden rows in digit-plane form)
   e = timed(m, K_ROUTER_LOGITS, s, [&] {
-    return coli::launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, xq, xs, s);
+    return coli::launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill ? nullptr : xq, xs, s);
   });
   if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  if (prefill) {
+    // 2. selection and dispatch, 3. bf16 activations and the tile list,
+    // 4. grouped GEMMs on MFMA, 5. weighted combine
+    if ((int64_t)T * k <= coli::kFusedDispatchMax) {
+      e = timed(m, K_ROUTER_SELECT, s, [&] {
+        return coli::launch_select_dispatch(logits, bias, T, E, k, rsf, idx, wsel, offsets, sorted_ids, inv,
+                                            active, n_active, s);
+      });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    } else {
+      e = timed(m, K_ROUTER_SELECT, s,
+                [&] { return coli::launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+      e = timed(m, K_DISPATCH, s, [&] {
+        return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
+      });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    }
+    coli::PrefillProblem Q{};
+    Q.gate = {m->w.gate_q, m->w.gate_s};
+    Q.up = {m->w.up_q, m->w.up_s};
+    Q.down = {m->w.down_q, m->w.down_s};
+    Q.sh_gate = {m->w.sh_gate_q, m->w.sh_gate_s};
+    Q.sh_up = {m->w.sh_up_q, m->w.sh_up_s};
+    Q.sh_down = {m->w.sh_down_q, m->w.sh_down_s};
+    Q.h = h;
+    Q.I = I;
+    Q.T = T;
+    Q.k = k;
+    Q.E = E;
+    Q.has_shared = c.n_shared;
+    Q.xb = at<__bf16>(m, L.xb);
+    Q.mid = at<__bf16>(m, L.midb);
+    Q.y = y;
+    Q.offsets = offsets;
+    Q.sorted_ids = sorted_ids;
+    Q.active = active;
+    Q.n_active = n_active;
+    Q.tiles = at<int2>(m, L.tiles);
+    Q.n_tiles = at<int32_t>(m, L.n_tiles);
+    e = timed(m, K_PREFILL_PREP, s,
+              [&] { return coli::launch_prefill_prep(hidden, T, h, at<__bf16>(m, L.xb), s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    e = timed(m, K_BUILD_TILES, s, [&] { return coli::launch_build_tiles(Q, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    e = timed(m, K_MFMA_GATE_UP, s, [&] { return coli::launch_gate_up_mfma(Q, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    e = timed(m, K_MFMA_DOWN, s, [&] { return coli::launch_down_mfma(Q, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    e = timed(m, K_COMBINE, s,
+              [&] { return coli::launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    m->last_T = T;
+    if (m->prof_calls_left > 0) {
+      --m->prof_calls_left;
+      ++m->prof_calls_done;
+    }
+    return COLI_MOE_OK;
+  }
   coli::DecodeProblem P{};
   P.gate = {m->w.gate_q, m->w.gate_s};
   P.up = {m->w.up_q, m->w.up_s};

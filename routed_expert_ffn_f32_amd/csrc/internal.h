@@ -3,6 +3,7 @@
 // stream; launchers return hipError_t.
 #pragma once
 
+#include <hip/hip_bf16.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -33,7 +34,7 @@ hipError_t launch_router_permute(const float *wr, float *wrP, int h, int E, hipS
 // m = 0..h/64-1, then the 64 partials meet in an xor butterfly (32,16,..,1).
 // The same launch writes the digit-plane form of x (xq, xs) for the experts.
 hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits,
-                                uint32_t *xq, float *xs, hipStream_t s);
+                                uint32_t *xq, float *xs, hipStream_t s);  // xq == NULL: no planes
 
 // One wave per token: sigmoid scores, biased key, top-k (key desc, index
 // asc), renormalised weights times rsf.
@@ -93,5 +94,30 @@ hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s);
 // ... then out[t] = sum_j w[t*k+j] y[inv[t*k+j]] + (shared ? y[T*k + t] : 0).
 hipError_t launch_combine(const float *y, const float *w, const int32_t *inv, int T, int k, int h,
                           int has_shared, float *out, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Prefill path (expert_mfma.hip): grouped GEMMs on bf16 MFMA.
+// ---------------------------------------------------------------------------
+struct PrefillProblem {
+  ExpertTables gate, up, down;
+  ExpertTables sh_gate, sh_up, sh_down;
+  int h, I, T, k, E, has_shared;
+  const __bf16 *xb;  // [T][h] hidden rows in bf16 (A column order)
+  __bf16 *mid;       // [P][I] intermediate in bf16 (A column order)
+  float *y;          // [P][h] expert outputs
+  const int32_t *offsets, *sorted_ids, *active, *n_active;
+  int2 *tiles;       // (slot or -1 for the shared expert, first token)
+  int32_t *n_tiles;
+};
+
+// Largest tile count of a call (grid size of the GEMM launches).
+int prefill_max_tiles(int T, int k, int E, int has_shared);
+// x [T][h] float -> bf16 in the A column order.
+hipError_t launch_prefill_prep(const float *x, int T, int h, __bf16 *xb, hipStream_t s);
+hipError_t launch_build_tiles(const PrefillProblem &P, hipStream_t s);
+// mid = silu(x Wg^T) * (x Wu^T) per expert tile, bf16.
+hipError_t launch_gate_up_mfma(const PrefillProblem &P, hipStream_t s);
+// y = mid Wd^T per expert tile, float32.
+hipError_t launch_down_mfma(const PrefillProblem &P, hipStream_t s);
 
 }  // namespace coli

@@ -206,7 +206,7 @@ size_t router_permuted_floats(int h, int E) { return (size_t)E * ((((h >> 6) + 3
 hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits, uint32_t *xq,
                                 float *xs, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const int qblocks = (int)(((size_t)T * (h >> 3) + 255) / 256);
+  const int qblocks = xq ? (int)(((size_t)T * (h >> 3) + 255) / 256) : 0;
   if (T < 4) {
     const int nlb = T * ((E + 3) / 4);
     router_logits_kernel<1, 1><<<nlb + qblocks, 256, 0, s>>>(x, wrP, T, h, E, logits, nlb, xq, xs);

@@ -214,6 +214,73 @@ def test_two_runs_bitwise_identical(dev):
 
 
 # ---------------------------------------------------------------------------
+# The bf16 MFMA (prefill) path on small layers: full outputs.
+# ---------------------------------------------------------------------------
+
+MID = synth.LayerShape(hidden=256, n_experts=16, top_k=4, inter=384, n_shared=1, rsf=2.5, bias_sigma=0.05)
+
+
+def check_mfma(shape, seed, T, dev, threshold, max_tokens=None, wr=None, bias=None, rows=None):
+    L = DeviceLayer(shape, seed, 0, dev, max_tokens=max_tokens or T, prefill_threshold=threshold,
+                    keep_host=True, wr=wr, bias=bias)
+    x = synth.hidden(shape, seed, T)
+    out = run(L, x, dev)
+    idx, _ = assert_routing_matches(L, x, T)
+    sel = slice(None) if rows is None else rows
+    ref, _, _ = L.oracle_forward(x[sel])
+    err = rel_err(out[sel], ref)
+    log(f"  rel err {err:.3e}")
+    assert err <= TOL_MFMA, err
+    return L, x, out, idx
+
+
+def test_mfma_path_several_tiles_ragged(dev):
+    """T = 300 tokens, 16 experts, k = 4: about 75 tokens per expert, the
+    shared expert in 3 tiles (128 + 128 + 44 rows), every N tile count > 1."""
+    log("MFMA path T=300 h=256 I=384 E=16 k=4")
+    check_mfma(MID, 21, 300, dev, threshold=64)
+
+
+def test_mfma_path_one_expert_takes_all(dev):
+    """Bias 5.0 on expert 3: all 300 tokens in its first slot, so one expert
+    spans three M tiles and the rest are small or empty."""
+    log("MFMA path, one expert holds every token")
+    wr, b = synth.router(MID, 22)
+    b = b.copy()
+    b[3] = 5.0
+    _, _, _, idx = check_mfma(MID, 22, 300, dev, threshold=64, wr=wr, bias=b)
+    assert np.all(idx[:, 0] == 3)
+
+
+def test_mfma_path_few_tokens(dev):
+    """Threshold 1: T = 5 tokens on the MFMA path (tiles almost all padding)."""
+    log("MFMA path T=5 (threshold 1)")
+    check_mfma(MID, 23, 5, dev, threshold=1)
+
+
+def test_mfma_path_no_shared_expert_olmoe(dev):
+    """OLMoE-like layer (h 2048, E 64, k 8, I 1024, no shared expert) at
+    T = 512 on the MFMA path, outputs of sampled tokens."""
+    log("MFMA path OLMoE-like T=512")
+    check_mfma(synth.OLMOE, 24, 512, dev, threshold=256, rows=[0, 1, 255, 300, 511])
+
+
+def test_threshold_switch_on_one_handle(dev):
+    """One handle: T just below the threshold (GEMV path), at it (MFMA path),
+    decode again; each call against the oracle at its own bar."""
+    log("GEMV / MFMA switch on one handle")
+    L = DeviceLayer(MID, 25, 0, dev, max_tokens=200, prefill_threshold=100, keep_host=True)
+    for T, tol in ((99, TOL_GEMV), (100, TOL_MFMA), (3, TOL_GEMV), (200, TOL_MFMA)):
+        x = synth.hidden(MID, 25, T, batch=T)
+        out = run(L, x, dev)
+        assert_routing_matches(L, x, T)
+        ref, _, _ = L.oracle_forward(x)
+        err = rel_err(out, ref)
+        log(f"  T={T} rel err {err:.3e}")
+        assert err <= tol, (T, err)
+
+
+# ---------------------------------------------------------------------------
 # GLM-5.2-like layer (h=6144, E=256, k=8, I=2048, 1 shared) at full size.
 # ---------------------------------------------------------------------------
 
@@ -264,10 +331,11 @@ def test_glm_prefill_routing_and_sampled_outputs(dev):
     idx, _ = assert_routing_matches(L, x, T)
     counts = np.bincount(idx.reshape(-1), minlength=256)
     log(f"  distinct experts {int((counts > 0).sum())}, head load {int(counts.max())}")
-    rows = [0, 1, 2047, 4095]
+    head = int(np.argmax(counts))
+    on_head = np.nonzero((idx == head).any(axis=1))[0]
+    rows = sorted(set([0, 1, 2047, 4095, int(on_head[0]), int(on_head[-1])]))
     ref, _, _ = L.oracle_forward(x[rows])
     err = rel_err(out[rows], ref)
     log(f"  rel err {err:.3e}")
-    tol = TOL_MFMA if T >= 256 else TOL_GEMV
-    assert err <= tol
+    assert err <= TOL_MFMA
     L.close()
