@@ -46,9 +46,15 @@ struct Layout {
   size_t total;
 };
 
-// The prefill (MFMA) path needs 128-aligned h and I; T below the threshold,
-// or other shapes, take the GEMV path.
-bool prefill_shape(const coli_moe_config_t &c) { return c.hidden % 128 == 0 && c.inter % 128 == 0; }
+// The prefill (MFMA) path takes h multiple of 256, I of 128, and bf16
+// activation buffers ([max_tokens][h] and [P][I]) under 4 GiB, since its
+// copies address them with 32-bit offsets; T below the threshold, or other
+// shapes, take the GEMV path.
+bool prefill_shape(const coli_moe_config_t &c) {
+  const uint64_t T = (uint64_t)c.max_tokens, P = T * (uint64_t)(c.top_k + (c.n_shared ? 1 : 0));
+  return coli::prefill_shape_ok(c.hidden, c.inter) && T * (uint64_t)c.hidden * 2 < (1ull << 32) &&
+         P * (uint64_t)c.inter * 2 < (1ull << 32);
+}
 
 bool config_ok(const coli_moe_config_t &c, int *code) {
   if (c.hidden < 64 || c.hidden > 16384 || c.hidden % 64 || c.inter < 64 || c.inter > 16384 ||

@@ -6,31 +6,37 @@
 // Colibri article, section 3.3 step 4 -- every expert with tokens runs one
 // GEMM on its token group, fed by the expert offsets of step 3.  With
 // thousands of tokens the expert FFN is a dense contraction per expert
-// (M = tokens of the expert, N = rows, K = columns), so it runs on
+// (M = tokens of the expert, N = weight rows, K = columns), so it runs on
 // v_mfma_f32_32x32x16_bf16.
 //
 // Operands:
-//  A  activations in bf16 ([T][h] for gate/up, the intermediate [P][I] for
-//     down), stored with the 8 columns of every 8-column word in the order
-//     0,2,4,6,1,3,5,7 (see below);
-//  B  the int4 codes, made bf16 exactly without any arithmetic: the 4-bit
-//     code q becomes u = q + 8 (xor 8) and the bf16 number 128 + u (bits
-//     0x4300 | u, exact since bf16 spacing at 128 is 1), one v_perm_b32 per
-//     pair; the even columns of a word fill the first four elements and the
-//     odd columns the last four, which is why A is stored in that order (K is
-//     a sum index, any order common to A and B gives the same products);
-//  scale per 64-column group g: the MFMAs of one group accumulate
-//     D = A (Q + 136) in float32, then acc += s[n][g] * (D - 136 * sum_k A[m][k]),
-//     with the 64-column sums of A taken while staging A into LDS.
+//  A  activations in bf16 ([T][h] hidden rows for gate/up, the intermediate
+//     [P][I] for down), gathered per tile into LDS;
+//  B  the weights dequantised in registers straight into bf16: code q of a
+//     64-column group with scale s becomes bf16(q * s), computed as
+//     fma(u, s, -8 s) with u = q + 8 taken as an unsigned byte (exact before
+//     the one rounding to bf16).  Each weight is dequantised once per tile
+//     and feeds the 8 MFMA blocks of the tile's 256 tokens.
 //
-// Tiles: 128 rows of A (tokens of one expert) x 128 weight rows, 4 waves;
-// wave w owns weight rows 32w..32w+31 and all 128 tokens (4 MFMA blocks of 32
-// tokens).  gate/up: the tile holds the same 128 rows of gate and of up, so
-// the epilogue applies SwiGLU and writes the intermediate in bf16 (in the A
-// order of the down GEMM); down: y[p][r] in float32, followed by the
-// deterministic combine.  The tile list (expert, first token) is built on the
-// device from the dispatch offsets; the grid is launched for the largest
-// possible list and surplus blocks leave at once.
+// Tiles: 256 rows of A (tokens of one expert) x 256 weight rows (gate/up:
+// 128 intermediate rows of gate and the same 128 of up; down: 256 output
+// rows); 8 waves, two per SIMD so that one wave's dequantisation overlaps the
+// other's MFMAs.  Wave w owns one 32-row MFMA block of B (gate/up: pair
+// w / 2, gate for even w, up for odd w) and all 256 tokens (8 blocks of 32
+// tokens, those wholly past the expert's last token skipped).  K runs in
+// steps of 64 columns (one scale group); each lane owns 32 of the 64
+// columns, so the 4 MFMAs of a step cover columns {8j..8j+7} and
+// {32+8j..32+8j+7} -- K is a sum index, any order common to A and B gives
+// the same products.  A rows and weights are copied into LDS rings ahead of
+// use.  For SwiGLU the up waves hand their accumulators to the gate waves
+// through LDS.
+//
+// The tile list (expert slot, first token) is built on the device from the
+// dispatch offsets.  The grid is launched for the largest possible list; each
+// block maps its hardware index to a (tile, column block) pair so that the
+// column blocks of one tile run on one XCD (hardware block i runs on XCD
+// i mod 8), where they share the tile's activation rows in that XCD's L2, and
+// blocks past the real list leave at once.
 #include "internal.h"
 #include "wave.h"
 
@@ -38,254 +44,400 @@ namespace coli {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128;       // tokens per tile
-constexpr int BN = 128;       // weight rows per tile (per matrix)
-constexpr int BK = 64;        // columns per K step = one scale group
-constexpr int kLdsRow = BK + 8;  // bf16 per LDS row (16-byte pad against bank conflicts)
+constexpr int BM = 256;          // tokens per tile
+constexpr int BK = 64;           // columns per K step = one scale group
+constexpr int kWaves = 8;        // waves per block
+constexpr int kThreads = 64 * kWaves;
+constexpr int kXcds = 8;
 
-// Column c of a word (c = 0..7) sits at position c/2 + 4 (c & 1) of the
-// stored word: even columns first.
-__device__ __forceinline__ int word_pos(int c) { return (c >> 1) + 4 * (c & 1); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
 
-// 8 int4 codes (nibble i = column i) -> 8 bf16 values 136 + q in the stored
-// column order (0,2,4,6,1,3,5,7).
-__device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t w) {
-  const uint32_t v = w ^ 0x88888888u;
-  const uint32_t lo = v & 0x0F0F0F0Fu;         // u of columns 0, 2, 4, 6 (bytes 0..3)
-  const uint32_t hi = (v >> 4) & 0x0F0F0F0Fu;  // u of columns 1, 3, 5, 7
-  const uint32_t k43 = 0x43434343u;
-  // perm(a, b, sel): byte i of the result is byte sel_i of {b (0..3), a (4..7)}
+__device__ __forceinline__ float ubyte(uint32_t v, int j) {
+  float f;
+  switch (j) {
+    case 0: asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v)); break;
+    case 1: asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v)); break;
+    case 2: asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v)); break;
+    default: asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v)); break;
+  }
+  return f;
+}
+
+// 8 int4 codes (nibble c = column c, two's complement) -> bf16(q * s) in
+// column order.  m8s = -8 s.
+__device__ __forceinline__ bf16x8 dequant_word(uint32_t w, float s, float m8s) {
+  const uint32_t v = w ^ 0x88888888u;  // u = q + 8 in every nibble
+  const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
   uint32_t p[4];
-  p[0] = __builtin_amdgcn_perm(k43, lo, 0x04010400u);  // [u0, 43, u2, 43]
-  p[1] = __builtin_amdgcn_perm(k43, lo, 0x04030402u);  // [u4, 43, u6, 43]
-  p[2] = __builtin_amdgcn_perm(k43, hi, 0x04010400u);  // [u1, 43, u3, 43]
-  p[3] = __builtin_amdgcn_perm(k43, hi, 0x04030402u);  // [u5, 43, u7, 43]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    p[j] = pack_bf16(__builtin_fmaf(ubyte(lo, j), s, m8s), __builtin_fmaf(ubyte(hi, j), s, m8s));
   return __builtin_bit_cast(bf16x8, p);
 }
 
-struct TileRows {
-  int p_begin, cnt;   // sorted positions of the expert's tokens
-  bool shared;
-  int e;
+struct Tile {
+  int p_begin, rows;  // first sorted position of the tile, valid rows (1..BM)
+  int e;              // expert, -1 = shared
 };
 
-__device__ __forceinline__ bool tile_rows(const PrefillProblem &P, int tile, int &m0, TileRows &R) {
-  if (tile >= *P.n_tiles) return false;
-  const int2 t = P.tiles[tile];
-  m0 = t.y;
-  if (t.x < 0) {
-    R.shared = true;
-    R.e = -1;
-    R.p_begin = P.T * P.k;
-    R.cnt = P.T;
+// Maps the hardware block index to (tile, column block); false for surplus
+// blocks.  nb = column blocks per tile.
+__device__ __forceinline__ bool tile_of_block(const PrefillProblem &P, int nb, Tile &t, int &n_blk) {
+  const int n_tiles = *P.n_tiles;
+  const int total = n_tiles * nb;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int b = blockIdx.x;
+  const int logical = (b % kXcds) * per + b / kXcds;
+  if (b >= per * kXcds || logical >= total) return false;
+  const int tile = logical / nb;
+  n_blk = logical - tile * nb;
+  const int2 d = P.tiles[tile];
+  int cnt;
+  if (d.x < 0) {
+    t.e = -1;
+    t.p_begin = P.T * P.k + d.y;
+    cnt = P.T;
   } else {
-    R.shared = false;
-    R.e = P.active[t.x];
-    R.p_begin = P.offsets[R.e];
-    R.cnt = P.offsets[R.e + 1] - R.p_begin;
+    t.e = P.active[d.x];
+    const int o = P.offsets[t.e];
+    t.p_begin = o + d.y;
+    cnt = P.offsets[t.e + 1] - o;
   }
+  t.rows = min(BM, cnt - d.y);
   return true;
 }
 
-// Stage one K step of A (BM rows x 64 columns) into LDS and the 64-column sums
-// times 136: thread t copies 32 columns (64 bytes) of row t/2 and the pair of
-// threads of a row adds its sums.
-__device__ __forceinline__ void stage_a(const __bf16 *const *rowp, int g, __bf16 (*xs)[kLdsRow], float *xc) {
-  const int t = threadIdx.x, m = t >> 1, part = t & 1;
-  const uint4 *src = reinterpret_cast<const uint4 *>(rowp[m] + (size_t)g * BK + 32 * part);
-  uint4 v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = src[i];
-  float sum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, v[i]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sum += (float)b[j];
-  }
-  sum += __shfl_xor(sum, 1);
-  uint4 *dst = reinterpret_cast<uint4 *>(&xs[m][32 * part]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = v[i];
-  if (part == 0) xc[m] = 136.0f * sum;
+// LDS rings, filled by LDS-DMA loads (global_load_lds, 16 or 4 bytes per
+// lane, lane-linear in LDS):
+//  A ring, 4 slots = two pairs of K steps (the pair being computed and the
+//    next pair in flight): the tile's rows of 64 bf16 (128 bytes = 8 chunks
+//    of 16 bytes); chunk c of row r sits in slot c ^ ((r >> 1) & 7), so that
+//    the 16 rows read by 16 neighbouring lanes fall in 16 different bank
+//    groups (64 banks).  One block barrier per pair of steps publishes a
+//    pair and frees the previous one.
+//  W ring, 3 slots, private to each wave (no barrier): 256 weight rows x 32
+//    bytes of codes (row b = 32 w + l of wave w, lane row l; the two 16-byte
+//    halves of rows with bit 3 set swapped, again for the banks), then the
+//    256 rows' scales.
+// Per step and wave: (NMB + 1) / 2 copies of A rows (copy i of wave w holds
+// tile rows 8 c .. 8 c + 7, c = 8 i + w, or c - 4 where that passes the
+// NMB * 32 rows: an identical second copy), 1 of codes, 1 of scales.  Copies
+// past the last step re-fetch the last step into a slot no later step reads,
+// so the issue pattern never changes and the waits are constants.
+constexpr int kASlots = 4, kWSlots = 3;
+constexpr int kASlotBytes = BM * 128;                                 // 32 KB
+constexpr int kWQBytes = 256 * 32, kWSlotBytes = kWQBytes + 256 * 4;  // 9 KB
+constexpr int kWRingOff = kASlots * kASlotBytes;
+constexpr int kLdsBytes = kWRingOff + kWSlots * kWSlotBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS rings exceed the 160 KB of a CU");
+
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
 }
 
-// ---------------------------------------------------------------------------
-// gate/up
-// ---------------------------------------------------------------------------
+// LDS-DMA loads: M0 holds the LDS address of lane 0's data (one wait state
+// between the M0 write and the load).  Issued from inline assembly so that
+// the compiler does not fold them into its own vmcnt bookkeeping; their
+// completion is awaited explicitly (dma_wait).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t lds, const void *base, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const void *addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void dma_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-// grid = (I / BN, max tiles), 256 threads.
-__global__ __launch_bounds__(256) void gate_up_mfma_kernel(PrefillProblem P) {
-  __shared__ __bf16 xs[2][BM][kLdsRow];
-  __shared__ float xc[2][BM];
-  __shared__ const __bf16 *rowp[BM];
-  int m0;
-  TileRows R;
-  if (!tile_rows(P, blockIdx.y, m0, R)) return;  // uniform over the block
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = P.h, I = P.I, G = h / BK;
-  const int n0 = blockIdx.x * BN + wave * 32;  // this wave's 32 rows
-  const int nl = lane & 31, half = lane >> 5;
-  const int rows_here = min(BM, R.cnt - m0);
-  if (threadIdx.x < BM) {
-    const int m = min((int)threadIdx.x, rows_here - 1);  // padding rows repeat a valid token
-    const int p = R.p_begin + m0 + m;
-    const int tok = R.shared ? p - P.T * P.k : P.sorted_ids[p] / P.k;
-    rowp[threadIdx.x] = P.xb + (size_t)tok * h;
+// Barrier without the compiler's memory-model waits (which would also wait
+// for the copies still in flight): this wave's LDS accesses are complete
+// (lgkmcnt 0) and kept on their side of it by the memory clobber.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Where this lane's copies come from.
+struct Sources {
+  const char *a_base;    // A rows (byte base)
+  uint32_t a_off[4];     // copy i: byte offset of its row for this lane plus this lane's chunk
+  const uint8_t *q_base; // codes of this wave's 32 rows
+  uint32_t q_off;        // row lane / 2 of the 32, this lane's 16 bytes
+  const float *s_row;    // scales of row 32 w + lane (lanes 0..31)
+};
+
+template <int NMB>
+struct ACopies {
+  static constexpr int kPerWave = (NMB + 1) / 2;
+  // A copy index (8 rows each) of copy i of wave w
+  __device__ static __forceinline__ int index(int i, int w) {
+    const int c = 8 * i + w;
+    return c < 4 * NMB ? c : c - 4;
   }
-  // this lane's weight row n0 + nl: 16 bytes (32 columns) of each group
+};
+
+// Byte offset of row r's chunk for copy lane `lane` (row r = 8 c + lane / 8).
+__device__ __forceinline__ uint32_t a_chunk(int r, int lane) { return (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 16); }
+
+template <int NMB>
+__device__ __forceinline__ void stage_a(const Sources &S, int g, char *lds, int slot) {
+  const int wave = wave_id();
+  const uint32_t base = lds_addr(lds) + slot * kASlotBytes;
+  const char *src = S.a_base + (size_t)g * (BK * 2);
+#pragma unroll
+  for (int i = 0; i < ACopies<NMB>::kPerWave; ++i) dma16(base + 8 * ACopies<NMB>::index(i, wave) * 128, src, S.a_off[i]);
+}
+
+__device__ __forceinline__ void stage_w(const Sources &S, int g, char *lds, int slot) {
+  const int wave = wave_id();
+  const uint32_t base = lds_addr(lds) + kWRingOff + slot * kWSlotBytes;
+  dma16(base + 32 * wave * 32, S.q_base + (size_t)g * 32, S.q_off);
+  if ((threadIdx.x & 63) < 32) dma4(base + kWQBytes + 32 * wave * 4, S.s_row + g);
+}
+
+// The copies of one pair of steps, issued one or two at a time between the
+// MFMA groups of the first step so that no wave stalls on a burst of them:
+// copy x < kA: A(ga) copy x; x < 2 kA: A(ga + 1) copy x - kA; then the codes
+// and the scales of W(gw).
+template <int NMB>
+struct PairCopies {
+  static constexpr int kA = ACopies<NMB>::kPerWave, kCount = 2 * kA + 2;
+  const Sources &S;
+  char *lds;
+  int ga0, ga1, sa0, sa1, gw, sw;
+  __device__ __forceinline__ void copy(int x) const {
+    const int wave = wave_id();
+    if (x < 2 * kA) {
+      const int i = x < kA ? x : x - kA;
+      const uint32_t base = lds_addr(lds) + (x < kA ? sa0 : sa1) * kASlotBytes;
+      const char *src = S.a_base + (size_t)(x < kA ? ga0 : ga1) * (BK * 2);
+      dma16(base + 8 * ACopies<NMB>::index(i, wave) * 128, src, S.a_off[i]);
+    } else {
+      const uint32_t base = lds_addr(lds) + kWRingOff + sw * kWSlotBytes;
+      if (x == 2 * kA)
+        dma16(base + 32 * wave * 32, S.q_base + (size_t)gw * 32, S.q_off);
+      else if ((threadIdx.x & 63) < 32)
+        dma4(base + kWQBytes + 32 * wave * 4, S.s_row + gw);
+    }
+  }
+  // copies issued after MFMA group j (0..3) of the step
+  __device__ __forceinline__ void after(int j) const {
+#pragma unroll
+    for (int x = j * kCount / 4; x < (j + 1) * kCount / 4; ++x) copy(x);
+  }
+};
+
+struct NoCopies {
+  __device__ __forceinline__ void after(int) const {}
+};
+
+// One wave's share of a tile: acc = A x B^T for its 32 weight rows over the
+// K columns of the tile (G steps of 64), for the first NMB token blocks of
+// the tile (NMB is uniform over the block, so the MFMA sequence is
+// straight-line code).
+template <int NMB>
+struct WaveGemm {
+  f32x16 acc[NMB];
+
+  template <class C>
+  __device__ __forceinline__ void compute(const char *lds, int sa, int sw, const C &copies) {
+    const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
+    const char *A = lds + sa * kASlotBytes;
+    const char *W = lds + kWRingOff + sw * kWSlotBytes;
+    const uint4 q = *reinterpret_cast<const uint4 *>(W + 32 * wave * 32 + 16 * (2 * nl + (half ^ ((nl >> 3) & 1))));
+    const float c = *reinterpret_cast<const float *>(W + kWQBytes + (32 * wave + nl) * 4);
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+    const float m8c = -8.0f * c;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 b = dequant_word(qw[j], c, m8c);
+      const int slot = (4 * half + j) ^ ((nl >> 1) & 7);  // row r = 32 mb + nl: (r >> 1) & 7 = (nl >> 1) & 7
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(A + ((32 * mb + nl) * 8 + slot) * 16);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[mb], 0, 0, 0);
+      }
+      copies.after(j);
+    }
+  }
+
+  // Issue order, per pair u of steps (2u, 2u + 1):
+  //   [barrier] A(2u+2) A(2u+3) W(2u+2) | step 2u | W(2u+3) | step 2u+1
+  // (indices past G - 1 re-fetch G - 1).  Before step 2u, A(2u), A(2u+1)
+  // and W(2u) are done once at most W(2u+1) is pending; before step 2u+1,
+  // W(2u+1) is done once at most the 2 A copies and W(2u+2) are pending.
+  static constexpr int kA = ACopies<NMB>::kPerWave, kW = 2;
+  static constexpr int kWaitEven = kW, kWaitOdd = 2 * kA + kW;
+
+  __device__ __forceinline__ void run(const Sources &S, int G, char *lds) {  // G >= 2
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
+    stage_a<NMB>(S, 0, lds, 0);
+    stage_a<NMB>(S, 1, lds, 1);
+    stage_w(S, 0, lds, 0);
+    stage_w(S, 1, lds, 1);
+    int sw = 0;  // W slot of step 2u
+    for (int g = 0; g < G; g += 2) {
+      const int sa = g & 3;  // A slots of the pair: sa, sa + 1
+      dma_wait<kWaitEven>();
+      block_barrier();  // pair visible to all waves; all waves done with the previous pair
+      const int sw1 = sw == 2 ? 0 : sw + 1, sw2 = sw1 == 2 ? 0 : sw1 + 1;
+      const PairCopies<NMB> pc{S, lds, min(g + 2, G - 1), min(g + 3, G - 1), (sa + 2) & 3, (sa + 3) & 3,
+                               min(g + 2, G - 1), sw2};
+      compute(lds, sa, sw, pc);
+      if (g + 1 < G) {
+        dma_wait<kWaitOdd>();
+        stage_w(S, min(g + 3, G - 1), lds, sw);  // step g's slot: this wave is done with it
+        compute(lds, sa + 1, sw1, NoCopies{});
+      }
+      sw = sw2;
+    }
+    dma_wait<0>();    // no copy may land in LDS after this point
+    block_barrier();  // every wave done with the rings (free for the epilogue)
+  }
+};
+
+// Row m of the tile held by register i of an MFMA block (token-block mb).
+__device__ __forceinline__ int acc_row(int mb, int half, int i) { return 32 * mb + 4 * half + 8 * (i >> 2) + (i & 3); }
+
+// ---------------------------------------------------------------------------
+// gate/up: mid[p][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), bf16.
+// Column blocks of 128 intermediate rows.
+// ---------------------------------------------------------------------------
+template <int NMB>
+__device__ __forceinline__ void a_sources(Sources &S, const PrefillProblem &P, const Tile &t, bool gather, int row_bytes) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+#pragma unroll
+  for (int i = 0; i < ACopies<NMB>::kPerWave; ++i) {
+    // tile row of this lane in copy i (padding rows repeat the last valid row)
+    const int r = 8 * ACopies<NMB>::index(i, wave) + (lane >> 3);
+    const int p = t.p_begin + min(r, t.rows - 1);
+    const int row = !gather ? p : (t.e < 0 ? p - P.T * P.k : P.sorted_ids[p] / P.k);
+    S.a_off[i] = (uint32_t)row * (uint32_t)row_bytes + a_chunk(r, lane);
+  }
+}
+
+template <int NMB>
+__device__ __forceinline__ void gate_up_tile(const PrefillProblem &P, const Tile &t, int n_blk, char *lds) {
+  const int h = P.h, I = P.I;
+  const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
+  const int pair = wave >> 1, up = wave & 1;
+  Sources S;
+  S.a_base = reinterpret_cast<const char *>(P.xb);
+  a_sources<NMB>(S, P, t, true, h * 2);
   const size_t qstride = (size_t)I * (h >> 1), sstride = (size_t)I * (h >> 6);
-  const uint8_t *gq = (R.shared ? P.sh_gate.q : P.gate.q + (size_t)R.e * qstride) + (size_t)(n0 + nl) * (h >> 1);
-  const uint8_t *uq = (R.shared ? P.sh_up.q : P.up.q + (size_t)R.e * qstride) + (size_t)(n0 + nl) * (h >> 1);
-  const float *gs = (R.shared ? P.sh_gate.s : P.gate.s + (size_t)R.e * sstride) + (size_t)(n0 + nl) * (h >> 6);
-  const float *us = (R.shared ? P.sh_up.s : P.up.s + (size_t)R.e * sstride) + (size_t)(n0 + nl) * (h >> 6);
-  __syncthreads();
+  const ExpertTables &M = t.e < 0 ? (up ? P.sh_up : P.sh_gate) : (up ? P.up : P.gate);
+  const size_t eq = t.e < 0 ? 0 : (size_t)t.e * qstride, es = t.e < 0 ? 0 : (size_t)t.e * sstride;
+  const int row0 = n_blk * 128 + pair * 32;  // this wave's gate or up rows row0 .. row0 + 31
+  S.q_base = M.q + eq + (size_t)row0 * (h >> 1);
+  S.q_off = (uint32_t)((lane >> 1) * (h >> 1) + ((lane & 1) ^ ((lane >> 4) & 1)) * 16);
+  S.s_row = M.s + es + (size_t)(row0 + nl) * (h >> 6);
 
-  f32x16 accg[4], accu[4];
+  WaveGemm<NMB> W;
+  W.run(S, h / BK, lds);
+
+  // up waves hand their accumulators to the gate wave of their pair, lane by
+  // lane (the same lane holds the same (token, row) in both waves)
+  float *xchg = reinterpret_cast<float *>(lds) + (size_t)pair * (NMB * 16 * 64);
+  if (up) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) accg[mb] = accu[mb] = f32x16{};
-  stage_a(rowp, 0, xs[0], xc[0]);
-  uint4 wg = *reinterpret_cast<const uint4 *>(gq + 16 * half);
-  uint4 wu = *reinterpret_cast<const uint4 *>(uq + 16 * half);
-  float sg = gs[0], su = us[0];
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    // next step's weights and scales in flight during this step
-    uint4 wg_n = wg, wu_n = wu;
-    float sg_n = sg, su_n = su;
-    if (g + 1 < G) {
-      wg_n = *reinterpret_cast<const uint4 *>(gq + (size_t)(g + 1) * 32 + 16 * half);
-      wu_n = *reinterpret_cast<const uint4 *>(uq + (size_t)(g + 1) * 32 + 16 * half);
-      sg_n = gs[g + 1];
-      su_n = us[g + 1];
-    }
-    f32x16 dg[4], du[4];
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) dg[mb] = du[mb] = f32x16{};
-    const uint32_t wgs[4] = {wg.x, wg.y, wg.z, wg.w}, wus[4] = {wu.x, wu.y, wu.z, wu.w};
+      for (int i = 0; i < 16; ++i) xchg[(mb * 16 + i) * 64 + lane] = W.acc[mb][i];
+  }
+  block_barrier();
+  if (!up) {
+    const int n = row0 + nl;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 bg = codes_to_bf16(wgs[j]), bu = codes_to_bf16(wus[j]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&xs[buf][32 * mb + nl][32 * half + 8 * j]);
-        dg[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bg, dg[mb], 0, 0, 0);
-        du[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bu, du[mb], 0, 0, 0);
-      }
-    }
-    if (g + 1 < G) stage_a(rowp, g + 1, xs[buf ^ 1], xc[buf ^ 1]);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float c = xc[buf][32 * mb + 4 * half + 8 * (i >> 2) + (i & 3)];
-        accg[mb][i] = __builtin_fmaf(sg, dg[mb][i] - c, accg[mb][i]);
-        accu[mb][i] = __builtin_fmaf(su, du[mb][i] - c, accu[mb][i]);
+        const int m = acc_row(mb, half, i);
+        if (m < t.rows) {
+          const float gv = W.acc[mb][i], uv = xchg[(mb * 16 + i) * 64 + lane];
+          // silu in float32 with the hardware exp and reciprocal (the result is
+          // rounded to bf16)
+          const float sg = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
+          P.mid[(size_t)(t.p_begin + m) * I + n] = (__bf16)(sg * uv);
+        }
       }
-    wg = wg_n;
-    wu = wu_n;
-    sg = sg_n;
-    su = su_n;
-    __syncthreads();
   }
-  // SwiGLU; the intermediate row p, column n is stored at the A position of
-  // the down GEMM (column order 0,2,4,6,1,3,5,7 within each word)
-  const int n = n0 + nl;
-  const int col = (n & ~7) | word_pos(n & 7);
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = 32 * mb + 4 * half + 8 * (i >> 2) + (i & 3);
-      if (m < rows_here) {
-        const float gv = accg[mb][i], uv = accu[mb][i];
-        const float v = gv / (1.0f + expf(-gv)) * uv;
-        P.mid[(size_t)(R.p_begin + m0 + m) * I + col] = (__bf16)v;
-      }
-    }
 }
 
 // ---------------------------------------------------------------------------
-// down: y[p][r] = sum_i mid[p][i] Wd[r][i]
+// down: y[p][r] = mid[p] . Wd[r], float32.  Column blocks of 256 output rows.
 // ---------------------------------------------------------------------------
-
-// grid = (h / BN, max tiles), 256 threads.
-__global__ __launch_bounds__(256) void down_mfma_kernel(PrefillProblem P) {
-  __shared__ __bf16 xs[2][BM][kLdsRow];
-  __shared__ float xc[2][BM];
-  __shared__ const __bf16 *rowp[BM];
-  int m0;
-  TileRows R;
-  if (!tile_rows(P, blockIdx.y, m0, R)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = P.h, I = P.I, G = I / BK;
-  const int n0 = blockIdx.x * BN + wave * 32;
-  const int nl = lane & 31, half = lane >> 5;
-  const int rows_here = min(BM, R.cnt - m0);
-  if (threadIdx.x < BM) {
-    const int m = min((int)threadIdx.x, rows_here - 1);
-    rowp[threadIdx.x] = P.mid + (size_t)(R.p_begin + m0 + m) * I;
-  }
+template <int NMB>
+__device__ __forceinline__ void down_tile(const PrefillProblem &P, const Tile &t, int n_blk, char *lds) {
+  const int h = P.h, I = P.I;
+  const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
+  Sources S;
+  S.a_base = reinterpret_cast<const char *>(P.mid);
+  a_sources<NMB>(S, P, t, false, I * 2);
   const size_t qstride = (size_t)h * (I >> 1), sstride = (size_t)h * (I >> 6);
-  const uint8_t *dq = (R.shared ? P.sh_down.q : P.down.q + (size_t)R.e * qstride) + (size_t)(n0 + nl) * (I >> 1);
-  const float *ds = (R.shared ? P.sh_down.s : P.down.s + (size_t)R.e * sstride) + (size_t)(n0 + nl) * (I >> 6);
-  __syncthreads();
+  const ExpertTables &D = t.e < 0 ? P.sh_down : P.down;
+  const int row0 = n_blk * 256 + wave * 32;  // this wave's rows row0 .. row0 + 31
+  S.q_base = D.q + (t.e < 0 ? 0 : (size_t)t.e * qstride) + (size_t)row0 * (I >> 1);
+  S.q_off = (uint32_t)((lane >> 1) * (I >> 1) + ((lane & 1) ^ ((lane >> 4) & 1)) * 16);
+  S.s_row = D.s + (t.e < 0 ? 0 : (size_t)t.e * sstride) + (size_t)(row0 + nl) * (I >> 6);
 
-  f32x16 acc[4];
+  WaveGemm<NMB> W;
+  W.run(S, I / BK, lds);
+
+  const int r = row0 + nl;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16{};
-  stage_a(rowp, 0, xs[0], xc[0]);
-  uint4 wd = *reinterpret_cast<const uint4 *>(dq + 16 * half);
-  float sd = ds[0];
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    uint4 wd_n = wd;
-    float sd_n = sd;
-    if (g + 1 < G) {
-      wd_n = *reinterpret_cast<const uint4 *>(dq + (size_t)(g + 1) * 32 + 16 * half);
-      sd_n = ds[g + 1];
-    }
-    f32x16 d[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) d[mb] = f32x16{};
-    const uint32_t wds[4] = {wd.x, wd.y, wd.z, wd.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 b = codes_to_bf16(wds[j]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&xs[buf][32 * mb + nl][32 * half + 8 * j]);
-        d[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, d[mb], 0, 0, 0);
-      }
-    }
-    if (g + 1 < G) stage_a(rowp, g + 1, xs[buf ^ 1], xc[buf ^ 1]);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float c = xc[buf][32 * mb + 4 * half + 8 * (i >> 2) + (i & 3)];
-        acc[mb][i] = __builtin_fmaf(sd, d[mb][i] - c, acc[mb][i]);
-      }
-    wd = wd_n;
-    sd = sd_n;
-    __syncthreads();
-  }
-  const int n = n0 + nl;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int m = 32 * mb + 4 * half + 8 * (i >> 2) + (i & 3);
-      if (m < rows_here) P.y[(size_t)(R.p_begin + m0 + m) * h + n] = acc[mb][i];
+      const int m = acc_row(mb, half, i);
+      if (m < t.rows) P.y[(size_t)(t.p_begin + m) * h + r] = W.acc[mb][i];
     }
 }
 
+#define COLI_NMB_SWITCH(FN)                \
+  switch ((t.rows + 31) / 32) {            \
+    case 1: FN<1>(P, t, n_blk, lds); break; \
+    case 2: FN<2>(P, t, n_blk, lds); break; \
+    case 3: FN<3>(P, t, n_blk, lds); break; \
+    case 4: FN<4>(P, t, n_blk, lds); break; \
+    case 5: FN<5>(P, t, n_blk, lds); break; \
+    case 6: FN<6>(P, t, n_blk, lds); break; \
+    case 7: FN<7>(P, t, n_blk, lds); break; \
+    default: FN<8>(P, t, n_blk, lds); break; \
+  }
+
+// 1-D grids of kThreads threads (see tile_of_block).
+__global__ __launch_bounds__(kThreads, 1) void gate_up_mfma_kernel(PrefillProblem P) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  Tile t;
+  int n_blk;
+  if (!tile_of_block(P, P.I / 128, t, n_blk)) return;  // uniform over the block
+  COLI_NMB_SWITCH(gate_up_tile)
+}
+
+__global__ __launch_bounds__(kThreads, 1) void down_mfma_kernel(PrefillProblem P) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  Tile t;
+  int n_blk;
+  if (!tile_of_block(P, P.h / 256, t, n_blk)) return;
+  COLI_NMB_SWITCH(down_tile)
+}
+#undef COLI_NMB_SWITCH
+
 // ---------------------------------------------------------------------------
-// Tile list: (slot, first token) for every 128 tokens of every active expert,
+// Tile list: (slot, first token) for every BM tokens of every active expert,
 // then of the shared expert.  One workgroup of 1024 threads, one slot per
 // thread (n_active <= 512).
 // ---------------------------------------------------------------------------
@@ -321,21 +473,25 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__rest
   if (tid == 1023) *n_tiles = before + incl;
 }
 
-// x [T][h] float -> bf16 in the stored column order of the A operand.
+// x [T][h] float -> bf16 (round to nearest even), 8 values per thread.
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float *__restrict__ x, size_t n_words,
                                                       __bf16 *__restrict__ xb) {
   const size_t w = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (w >= n_words) return;
   const float4 a = reinterpret_cast<const float4 *>(x)[2 * w];
   const float4 b = reinterpret_cast<const float4 *>(x)[2 * w + 1];
-  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  bf16x8 o;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) o[word_pos(c)] = (__bf16)v[c];
-  reinterpret_cast<bf16x8 *>(xb)[w] = o;
+  const uint4 o = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
+  reinterpret_cast<uint4 *>(xb)[w] = o;
+}
+
+int grid_blocks(int nb, int max_tiles) {
+  const int total = nb * max_tiles;
+  return (total + kXcds - 1) / kXcds * kXcds;
 }
 
 }  // namespace
+
+bool prefill_shape_ok(int h, int I) { return h % 256 == 0 && I % 128 == 0; }
 
 int prefill_max_tiles(int T, int k, int E, int has_shared) {
   const int n = T * k, routed_slots = E < n ? E : n;
@@ -354,14 +510,14 @@ hipError_t launch_build_tiles(const PrefillProblem &P, hipStream_t s) {
 }
 
 hipError_t launch_gate_up_mfma(const PrefillProblem &P, hipStream_t s) {
-  dim3 grid(P.I / BN, prefill_max_tiles(P.T, P.k, P.E, P.has_shared));
-  gate_up_mfma_kernel<<<grid, 256, 0, s>>>(P);
+  const int blocks = grid_blocks(P.I / 128, prefill_max_tiles(P.T, P.k, P.E, P.has_shared));
+  gate_up_mfma_kernel<<<blocks, kThreads, 0, s>>>(P);
   return hipGetLastError();
 }
 
 hipError_t launch_down_mfma(const PrefillProblem &P, hipStream_t s) {
-  dim3 grid(P.h / BN, prefill_max_tiles(P.T, P.k, P.E, P.has_shared));
-  down_mfma_kernel<<<grid, 256, 0, s>>>(P);
+  const int blocks = grid_blocks(P.h / 256, prefill_max_tiles(P.T, P.k, P.E, P.has_shared));
+  down_mfma_kernel<<<blocks, kThreads, 0, s>>>(P);
   return hipGetLastError();
 }
 

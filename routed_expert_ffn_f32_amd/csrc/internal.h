@@ -102,17 +102,19 @@ struct PrefillProblem {
   ExpertTables gate, up, down;
   ExpertTables sh_gate, sh_up, sh_down;
   int h, I, T, k, E, has_shared;
-  const __bf16 *xb;  // [T][h] hidden rows in bf16 (A column order)
-  __bf16 *mid;       // [P][I] intermediate in bf16 (A column order)
+  const __bf16 *xb;  // [T][h] hidden rows in bf16
+  __bf16 *mid;       // [P][I] intermediate in bf16
   float *y;          // [P][h] expert outputs
   const int32_t *offsets, *sorted_ids, *active, *n_active;
   int2 *tiles;       // (slot or -1 for the shared expert, first token)
   int32_t *n_tiles;
 };
 
+// Shapes the prefill path takes (h multiple of 256, I of 128).
+bool prefill_shape_ok(int h, int I);
 // Largest tile count of a call (grid size of the GEMM launches).
 int prefill_max_tiles(int T, int k, int E, int has_shared);
-// x [T][h] float -> bf16 in the A column order.
+// x [T][h] float -> bf16.
 hipError_t launch_prefill_prep(const float *x, int T, int h, __bf16 *xb, hipStream_t s);
 hipError_t launch_build_tiles(const PrefillProblem &P, hipStream_t s);
 // mid = silu(x Wg^T) * (x Wu^T) per expert tile, bf16.

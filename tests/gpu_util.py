@@ -83,6 +83,13 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float((np.abs(got64 - ref64) / den).max())
 
 
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over tokens t of ||got[t] - ref[t]||_2 / ||ref[t]||_2."""
+    ref64 = np.asarray(ref, np.float64)
+    got64 = np.asarray(got, np.float64)
+    return float((np.linalg.norm(got64 - ref64, axis=-1) / np.linalg.norm(ref64, axis=-1)).max())
+
+
 def routing_from_device(r: dict, T: int, k: int):
     f = {key: v.cpu().numpy() for key, v in r.items()}
     n_active = int(f["n_active"][0])

@@ -2,8 +2,18 @@
 the same seeded inputs.
 
 Bar: expert indices, routing weights and every dispatch array bit-exact;
-layer outputs within max relative error 2e-3 on the float32-accumulate GEMV
-path and 2e-2 on the bf16 MFMA path (element-wise, floored at the row RMS).
+layer outputs:
+ - float32-accumulate GEMV path: max relative error 2e-3, element-wise
+   (floored at the row RMS);
+ - bf16 MFMA path: max over tokens of the per-token relative error
+   ||out_t - ref_t|| / ||ref_t|| at most 2e-2, and element-wise (floored at
+   the row RMS) at most 6e-2.  Dequantising to bf16 rounds four operands
+   (hidden rows, gate/up weights, the intermediate, down weights) to 8
+   significant bits, which gives about 4e-3 RMS error relative to the row
+   RMS; the element-wise maximum over a 4096 x 6144 output is then about
+   2.3e-2, so the element-wise bound is set at 6e-2 (about 15 sigma), which
+   any wrong element (error of the order of the row RMS or more) still
+   exceeds by far.
 """
 import json
 import os
@@ -12,14 +22,15 @@ import numpy as np
 import pytest
 
 import synth
-from tests.gpu_util import DeviceLayer, assert_routing_matches, log, rel_err
+from tests.gpu_util import DeviceLayer, assert_routing_matches, log, rel_err, row_rel_err
 
 torch = pytest.importorskip("torch")
 
 pytestmark = pytest.mark.gpu
 
 TOL_GEMV = 2e-3
-TOL_MFMA = 2e-2
+TOL_MFMA = 2e-2        # per-token relative error
+TOL_MFMA_ELEM = 6e-2   # element-wise, floored at the row RMS
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -28,6 +39,13 @@ def dev():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     return torch.device("cuda:0")
+
+
+def assert_mfma_close(out, ref, what=""):
+    nw, ew = row_rel_err(out, ref), rel_err(out, ref)
+    log(f"  {what}per-token rel err {nw:.3e}, element-wise {ew:.3e}")
+    assert nw <= TOL_MFMA, (what, nw)
+    assert ew <= TOL_MFMA_ELEM, (what, ew)
 
 
 def run(layer: DeviceLayer, x: np.ndarray, dev):
@@ -228,9 +246,7 @@ def check_mfma(shape, seed, T, dev, threshold, max_tokens=None, wr=None, bias=No
     idx, _ = assert_routing_matches(L, x, T)
     sel = slice(None) if rows is None else rows
     ref, _, _ = L.oracle_forward(x[sel])
-    err = rel_err(out[sel], ref)
-    log(f"  rel err {err:.3e}")
-    assert err <= TOL_MFMA, err
+    assert_mfma_close(out[sel], ref)
     return L, x, out, idx
 
 
@@ -270,14 +286,17 @@ def test_threshold_switch_on_one_handle(dev):
     decode again; each call against the oracle at its own bar."""
     log("GEMV / MFMA switch on one handle")
     L = DeviceLayer(MID, 25, 0, dev, max_tokens=200, prefill_threshold=100, keep_host=True)
-    for T, tol in ((99, TOL_GEMV), (100, TOL_MFMA), (3, TOL_GEMV), (200, TOL_MFMA)):
+    for T in (99, 100, 3, 200):
         x = synth.hidden(MID, 25, T, batch=T)
         out = run(L, x, dev)
         assert_routing_matches(L, x, T)
         ref, _, _ = L.oracle_forward(x)
-        err = rel_err(out, ref)
-        log(f"  T={T} rel err {err:.3e}")
-        assert err <= tol, (T, err)
+        if T >= 100:
+            assert_mfma_close(out, ref, f"T={T} ")
+        else:
+            err = rel_err(out, ref)
+            log(f"  T={T} rel err {err:.3e}")
+            assert err <= TOL_GEMV, (T, err)
 
 
 # ---------------------------------------------------------------------------
@@ -333,9 +352,8 @@ def test_glm_prefill_routing_and_sampled_outputs(dev):
     log(f"  distinct experts {int((counts > 0).sum())}, head load {int(counts.max())}")
     head = int(np.argmax(counts))
     on_head = np.nonzero((idx == head).any(axis=1))[0]
-    rows = sorted(set([0, 1, 2047, 4095, int(on_head[0]), int(on_head[-1])]))
+    extra = np.random.default_rng(4096).choice(T, 26, replace=False)
+    rows = sorted(set([0, 1, 2047, 4095, int(on_head[0]), int(on_head[-1])] + [int(r) for r in extra]))
     ref, _, _ = L.oracle_forward(x[rows])
-    err = rel_err(out[rows], ref)
-    log(f"  rel err {err:.3e}")
-    assert err <= TOL_MFMA
+    assert_mfma_close(out[rows], ref)
     L.close()
