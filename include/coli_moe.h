@@ -129,8 +129,8 @@ int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe
  * DEVICE float32 [T][hidden] (16-byte aligned, may not alias `hidden`).
  * Asynchronous on `stream`; the host never reads device data.  T == 0 checks
  * the arguments and enqueues nothing (dry run).  T >= prefill_threshold runs
- * the bf16 MFMA grouped-GEMM path when hidden is a multiple of 256, inter of
- * 128 and the bf16 copies of the activations ([max_tokens][hidden] and
+ * the bf16 MFMA grouped-GEMM path when hidden and inter are multiples of 256
+ * and the bf16 copies of the activations ([max_tokens][hidden] and
  * [max_tokens*(top_k+n_shared)][inter]) stay under 4 GiB; every other call
  * runs the float32-accumulate GEMV path.
  * Errors: -4 bad handle/pointer, -1 T > max_tokens (or T < 0 gives -4),

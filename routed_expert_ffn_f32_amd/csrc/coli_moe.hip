@@ -46,7 +46,7 @@ struct Layout {
   size_t total;
 };
 
-// The prefill (MFMA) path takes h multiple of 256, I of 128, and bf16
+// The prefill (MFMA) path takes h and I multiples of 256, and bf16
 // activation buffers ([max_tokens][h] and [P][I]) under 4 GiB, since its
 // copies address them with 32-bit offsets; T below the threshold, or other
 // shapes, take the GEMV path.

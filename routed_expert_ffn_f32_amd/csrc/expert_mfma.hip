@@ -88,16 +88,17 @@ struct Tile {
 };
 
 // Maps the hardware block index to (tile, column block); false for surplus
-// blocks.  nb = column blocks per tile.
+// blocks.  Hardware block b runs on XCD b mod 8; XCD x takes tiles x, x + 8,
+// x + 16, ... in that order (the list is sorted by size, largest first, so
+// every XCD gets a similar share), all column blocks of a tile in a row, so
+// that they share the tile's activation rows in the XCD's L2.
+// nb = column blocks per tile.
 __device__ __forceinline__ bool tile_of_block(const PrefillProblem &P, int nb, Tile &t, int &n_blk) {
   const int n_tiles = *P.n_tiles;
-  const int total = n_tiles * nb;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int b = blockIdx.x;
-  const int logical = (b % kXcds) * per + b / kXcds;
-  if (b >= per * kXcds || logical >= total) return false;
-  const int tile = logical / nb;
-  n_blk = logical - tile * nb;
+  const int b = blockIdx.x, xcd = b % kXcds, j = b / kXcds;
+  const int tile = xcd + kXcds * (j / nb);
+  if (tile >= n_tiles) return false;
+  n_blk = j % nb;
   const int2 d = P.tiles[tile];
   int cnt;
   if (d.x < 0) {
@@ -122,20 +123,25 @@ __device__ __forceinline__ bool tile_of_block(const PrefillProblem &P, int nb, T
 //    the 16 rows read by 16 neighbouring lanes fall in 16 different bank
 //    groups (64 banks).  One block barrier per pair of steps publishes a
 //    pair and frees the previous one.
-//  W ring, 3 slots, private to each wave (no barrier): 256 weight rows x 32
-//    bytes of codes (row b = 32 w + l of wave w, lane row l; the two 16-byte
-//    halves of rows with bit 3 set swapped, again for the banks), then the
-//    256 rows' scales.
-// Per step and wave: (NMB + 1) / 2 copies of A rows (copy i of wave w holds
-// tile rows 8 c .. 8 c + 7, c = 8 i + w, or c - 4 where that passes the
-// NMB * 32 rows: an identical second copy), 1 of codes, 1 of scales.  Copies
-// past the last step re-fetch the last step into a slot no later step reads,
-// so the issue pattern never changes and the waits are constants.
-constexpr int kASlots = 4, kWSlots = 3;
-constexpr int kASlotBytes = BM * 128;                                 // 32 KB
-constexpr int kWQBytes = 256 * 32, kWSlotBytes = kWQBytes + 256 * 4;  // 9 KB
-constexpr int kWRingOff = kASlots * kASlotBytes;
-constexpr int kLdsBytes = kWRingOff + kWSlots * kWSlotBytes;
+//  Q ring, 3 slots of one step of codes: 256 weight rows x 32 bytes (row
+//    b = 32 w + l of wave w, lane row l; the two 16-byte halves of rows with
+//    bit 3 set swapped, again for the banks).
+//  S ring, 2 slots of four steps of scales: 256 rows x 16 bytes, so that a
+//    row's 4 consecutive scales come in one 16-byte copy.
+// The Q and S rows of a wave are copied and read by that wave only (no
+// barrier).  Per pair of steps and wave: 2 (NMB + 1) / 2 copies of A rows
+// (copy i of wave w holds tile rows 8 c .. 8 c + 7, c = 8 i + w, or c - 4
+// where that passes the NMB * 32 rows: an identical second copy), 2 of codes,
+// and every other pair 1 of scales.  Copies past the end re-fetch the last
+// step (chunk) into a slot no later step reads, so the issue pattern never
+// changes and the waits are constants.
+constexpr int kASlots = 4, kQSlots = 3, kSSlots = 2, kSChunk = 4;
+constexpr int kASlotBytes = BM * 128;              // 32 KB
+constexpr int kQSlotBytes = 256 * 32;              // 8 KB
+constexpr int kSSlotBytes = 256 * 4 * kSChunk;     // 4 KB
+constexpr int kQRingOff = kASlots * kASlotBytes;
+constexpr int kSRingOff = kQRingOff + kQSlots * kQSlotBytes;
+constexpr int kLdsBytes = kSRingOff + kSSlots * kSSlotBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS rings exceed the 160 KB of a CU");
 
 __device__ __forceinline__ uint32_t lds_addr(const char *p) {
@@ -152,8 +158,8 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void *base, uint32_t o
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(uint32_t lds, const void *addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(addr)
+__device__ __forceinline__ void dma16v(uint32_t lds, const void *addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -192,55 +198,55 @@ struct ACopies {
 __device__ __forceinline__ uint32_t a_chunk(int r, int lane) { return (uint32_t)(((lane & 7) ^ ((r >> 1) & 7)) * 16); }
 
 template <int NMB>
-__device__ __forceinline__ void stage_a(const Sources &S, int g, char *lds, int slot) {
-  const int wave = wave_id();
+__device__ __forceinline__ void copy_a(const Sources &S, int g, char *lds, int slot, int i) {
   const uint32_t base = lds_addr(lds) + slot * kASlotBytes;
-  const char *src = S.a_base + (size_t)g * (BK * 2);
-#pragma unroll
-  for (int i = 0; i < ACopies<NMB>::kPerWave; ++i) dma16(base + 8 * ACopies<NMB>::index(i, wave) * 128, src, S.a_off[i]);
+  dma16(base + 8 * ACopies<NMB>::index(i, wave_id()) * 128, S.a_base + (size_t)g * (BK * 2), S.a_off[i]);
 }
 
-__device__ __forceinline__ void stage_w(const Sources &S, int g, char *lds, int slot) {
-  const int wave = wave_id();
-  const uint32_t base = lds_addr(lds) + kWRingOff + slot * kWSlotBytes;
-  dma16(base + 32 * wave * 32, S.q_base + (size_t)g * 32, S.q_off);
-  if ((threadIdx.x & 63) < 32) dma4(base + kWQBytes + 32 * wave * 4, S.s_row + g);
+__device__ __forceinline__ void copy_q(const Sources &S, int g, char *lds, int slot) {
+  dma16(lds_addr(lds) + kQRingOff + slot * kQSlotBytes + 32 * wave_id() * 32, S.q_base + (size_t)g * 32, S.q_off);
 }
 
-// The copies of one pair of steps, issued one or two at a time between the
-// MFMA groups of the first step so that no wave stalls on a burst of them:
-// copy x < kA: A(ga) copy x; x < 2 kA: A(ga + 1) copy x - kA; then the codes
-// and the scales of W(gw).
+// scales of steps 4 c .. 4 c + 3 (lanes 0..31, one row each)
+__device__ __forceinline__ void copy_s(const Sources &S, int c, char *lds, int slot) {
+  if ((threadIdx.x & 63) < 32)
+    dma16v(lds_addr(lds) + kSRingOff + slot * kSSlotBytes + 32 * wave_id() * 16, S.s_row + kSChunk * c);
+}
+
+// The copies of a pair of steps issued during its first step, one or two
+// between MFMA groups so that no wave stalls on a burst of them: A(ga) copies,
+// A(ga + 1) copies, the codes of step gq, then (when sc >= 0) the scales of
+// chunk sc.
 template <int NMB>
 struct PairCopies {
-  static constexpr int kA = ACopies<NMB>::kPerWave, kCount = 2 * kA + 2;
+  static constexpr int kA = ACopies<NMB>::kPerWave, kCount = 2 * kA + 1;
   const Sources &S;
   char *lds;
-  int ga0, ga1, sa0, sa1, gw, sw;
+  int ga, sa, gq, sq, sc, ss;
   __device__ __forceinline__ void copy(int x) const {
-    const int wave = wave_id();
-    if (x < 2 * kA) {
-      const int i = x < kA ? x : x - kA;
-      const uint32_t base = lds_addr(lds) + (x < kA ? sa0 : sa1) * kASlotBytes;
-      const char *src = S.a_base + (size_t)(x < kA ? ga0 : ga1) * (BK * 2);
-      dma16(base + 8 * ACopies<NMB>::index(i, wave) * 128, src, S.a_off[i]);
-    } else {
-      const uint32_t base = lds_addr(lds) + kWRingOff + sw * kWSlotBytes;
-      if (x == 2 * kA)
-        dma16(base + 32 * wave * 32, S.q_base + (size_t)gw * 32, S.q_off);
-      else if ((threadIdx.x & 63) < 32)
-        dma4(base + kWQBytes + 32 * wave * 4, S.s_row + gw);
-    }
+    if (x < kA)
+      copy_a<NMB>(S, ga, lds, sa, x);
+    else if (x < 2 * kA)
+      copy_a<NMB>(S, ga + 1, lds, (sa + 1) & 3, x - kA);
+    else
+      copy_q(S, gq, lds, sq);
   }
   // copies issued after MFMA group j (0..3) of the step
   __device__ __forceinline__ void after(int j) const {
 #pragma unroll
     for (int x = j * kCount / 4; x < (j + 1) * kCount / 4; ++x) copy(x);
+    if (j == 3 && sc >= 0) copy_s(S, sc, lds, ss);
   }
 };
 
-struct NoCopies {
-  __device__ __forceinline__ void after(int) const {}
+// The codes of step g into slot sq, issued after the first MFMA group.
+struct QCopies {
+  const Sources &S;
+  char *lds;
+  int g, sq;
+  __device__ __forceinline__ void after(int j) const {
+    if (j == 0) copy_q(S, g, lds, sq);
+  }
 };
 
 // One wave's share of a tile: acc = A x B^T for its 32 weight rows over the
@@ -251,58 +257,90 @@ template <int NMB>
 struct WaveGemm {
   f32x16 acc[NMB];
 
+  // One 64-column step.  Software-pipelined by MFMA group: while the NMB
+  // MFMAs of group j run, the A fragments of group j + 1 are read from LDS
+  // and its weights dequantised, interleaved one MFMA : one LDS read : three
+  // VALU instructions.
+  // Step g from A slot g & 3, Q slot sq.
   template <class C>
-  __device__ __forceinline__ void compute(const char *lds, int sa, int sw, const C &copies) {
+  __device__ __forceinline__ void compute(const char *lds, int g, int sq, const C &copies) {
     const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
-    const char *A = lds + sa * kASlotBytes;
-    const char *W = lds + kWRingOff + sw * kWSlotBytes;
-    const uint4 q = *reinterpret_cast<const uint4 *>(W + 32 * wave * 32 + 16 * (2 * nl + (half ^ ((nl >> 3) & 1))));
-    const float c = *reinterpret_cast<const float *>(W + kWQBytes + (32 * wave + nl) * 4);
+    const char *A = lds + (g & 3) * kASlotBytes;
+    const char *Q = lds + kQRingOff + sq * kQSlotBytes;
+    const uint4 q = *reinterpret_cast<const uint4 *>(Q + 32 * wave * 32 + 16 * (2 * nl + (half ^ ((nl >> 3) & 1))));
+    const float c = *reinterpret_cast<const float *>(lds + kSRingOff + ((g >> 2) & 1) * kSSlotBytes +
+                                                     (32 * wave + nl) * 16 + (g & 3) * 4);
     const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
     const float m8c = -8.0f * c;
+    // row r = 32 mb + nl of group j: chunk slot (4 half + j) ^ ((r >> 1) & 7), (r >> 1) & 7 = (nl >> 1) & 7
+    const char *arow = A + nl * 128;
+    const int sw_ = (nl >> 1) & 7;
+    bf16x8 af[2][NMB], bf[2];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      af[0][mb] = *reinterpret_cast<const bf16x8 *>(arow + mb * 4096 + (((4 * half) ^ sw_) * 16));
+    bf[0] = dequant_word(qw[0], c, m8c);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16x8 b = dequant_word(qw[j], c, m8c);
-      const int slot = (4 * half + j) ^ ((nl >> 1) & 7);  // row r = 32 mb + nl: (r >> 1) & 7 = (nl >> 1) & 7
+      const int cur = j & 1, nxt = cur ^ 1;
+      if (j < 3) {
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(A + ((32 * mb + nl) * 8 + slot) * 16);
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[mb], 0, 0, 0);
+        for (int mb = 0; mb < NMB; ++mb)
+          af[nxt][mb] = *reinterpret_cast<const bf16x8 *>(arow + mb * 4096 + (((4 * half + j + 1) ^ sw_) * 16));
+        bf[nxt] = dequant_word(qw[j + 1], c, m8c);
+      }
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][mb], bf[cur], acc[mb], 0, 0, 0);
+      if (j < 3) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        }
       }
       copies.after(j);
     }
   }
 
-  // Issue order, per pair u of steps (2u, 2u + 1):
-  //   [barrier] A(2u+2) A(2u+3) W(2u+2) | step 2u | W(2u+3) | step 2u+1
-  // (indices past G - 1 re-fetch G - 1).  Before step 2u, A(2u), A(2u+1)
-  // and W(2u) are done once at most W(2u+1) is pending; before step 2u+1,
-  // W(2u+1) is done once at most the 2 A copies and W(2u+2) are pending.
-  static constexpr int kA = ACopies<NMB>::kPerWave, kW = 2;
-  static constexpr int kWaitEven = kW, kWaitOdd = 2 * kA + kW;
+  // Issue order (pair of steps g, g + 1, g even):
+  //   [barrier] A(g+2) A(g+3) Q(g+2) (S(g/4 + 1) when g % 4 == 0) | step g |
+  //   Q(g+3) | step g + 1
+  // (indices past the end re-fetch the last one).  Before step g: A(g),
+  // A(g+1), Q(g) and S(g/4) are done once at most Q(g+1) and, when g % 4 ==
+  // 2, S(g/4) are pending; before step g + 1, Q(g+1) is done once at most the
+  // pair's own copies are pending.
+  static constexpr int kA = ACopies<NMB>::kPerWave;
 
-  __device__ __forceinline__ void run(const Sources &S, int G, char *lds) {  // G >= 2
+  __device__ __forceinline__ void run(const Sources &S, int G, char *lds) {  // G >= 4, G % 4 == 0
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
-    stage_a<NMB>(S, 0, lds, 0);
-    stage_a<NMB>(S, 1, lds, 1);
-    stage_w(S, 0, lds, 0);
-    stage_w(S, 1, lds, 1);
-    int sw = 0;  // W slot of step 2u
+    const int last_chunk = G / kSChunk - 1;
+#pragma unroll
+    for (int i = 0; i < kA; ++i) copy_a<NMB>(S, 0, lds, 0, i);
+#pragma unroll
+    for (int i = 0; i < kA; ++i) copy_a<NMB>(S, 1, lds, 1, i);
+    copy_s(S, 0, lds, 0);
+    copy_q(S, 0, lds, 0);
+    copy_q(S, 1, lds, 1);
+    int sq = 0;  // Q slot of step g (g % 3)
     for (int g = 0; g < G; g += 2) {
-      const int sa = g & 3;  // A slots of the pair: sa, sa + 1
-      dma_wait<kWaitEven>();
+      if (g % 4 == 2)
+        dma_wait<2>();
+      else
+        dma_wait<1>();
       block_barrier();  // pair visible to all waves; all waves done with the previous pair
-      const int sw1 = sw == 2 ? 0 : sw + 1, sw2 = sw1 == 2 ? 0 : sw1 + 1;
-      const PairCopies<NMB> pc{S, lds, min(g + 2, G - 1), min(g + 3, G - 1), (sa + 2) & 3, (sa + 3) & 3,
-                               min(g + 2, G - 1), sw2};
-      compute(lds, sa, sw, pc);
-      if (g + 1 < G) {
-        dma_wait<kWaitOdd>();
-        stage_w(S, min(g + 3, G - 1), lds, sw);  // step g's slot: this wave is done with it
-        compute(lds, sa + 1, sw1, NoCopies{});
-      }
-      sw = sw2;
+      const int sq1 = sq == 2 ? 0 : sq + 1, sq2 = sq1 == 2 ? 0 : sq1 + 1;
+      const bool chunk = g % 4 == 0;
+      const PairCopies<NMB> pc{S,  lds, min(g + 2, G - 2), (g + 2) & 3, min(g + 2, G - 1), sq2,
+                               chunk ? min(g / 4 + 1, last_chunk) : -1, (g / 4 + 1) & 1};
+      compute(lds, g, sq, pc);
+      if (chunk)
+        dma_wait<2 * kA + 2>();
+      else
+        dma_wait<2 * kA + 1>();
+      compute(lds, g + 1, sq1, QCopies{S, lds, min(g + 3, G - 1), sq});  // Q(g+3) into step g's slot
+      sq = sq2;
     }
     dma_wait<0>();    // no copy may land in LDS after this point
     block_barrier();  // every wave done with the rings (free for the epilogue)
@@ -438,15 +476,18 @@ __global__ __launch_bounds__(kThreads, 1) void down_mfma_kernel(PrefillProblem P
 
 // ---------------------------------------------------------------------------
 // Tile list: (slot, first token) for every BM tokens of every active expert,
-// then of the shared expert.  One workgroup of 1024 threads, one slot per
-// thread (n_active <= 512).
+// then of the shared expert (slot -1), ordered by the tile's count of 32-token
+// blocks, largest first, and by slot within a count.  One workgroup of 1024 threads, one slot per thread
+// (n_active <= 512).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ offsets,
                                                            const int32_t *__restrict__ active,
                                                            const int32_t *__restrict__ n_active, int T,
                                                            int has_shared, int2 *__restrict__ tiles,
                                                            int32_t *__restrict__ n_tiles) {
-  __shared__ int32_t wave_sum[16];
+  constexpr int kB = BM / 32;  // token-block counts 1..kB
+  __shared__ int32_t wave_sum[16][kB + 1];
+  __shared__ int32_t bucket_start[kB + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int na = *n_active;
   int cnt = 0;
@@ -456,21 +497,47 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__rest
   } else if (tid == na && has_shared) {
     cnt = T;
   }
-  const int mt = (cnt + BM - 1) / BM;
-  int incl = mt;
+  const int full = cnt / BM, rest = cnt - full * BM;
+  const int part_nb = (rest + 31) / 32;  // 0 = no partial tile
+  // per bucket: full tiles go to bucket kB, the partial one to bucket part_nb;
+  // exclusive scans over threads for each bucket (bucket kB counts full tiles)
+  int mine[kB + 1], before[kB + 1];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(incl, d);
-    if (lane >= d) incl += v;
+  for (int k = 0; k <= kB; ++k) {
+    mine[k] = (k == kB ? full : 0) + (k == part_nb && k > 0 ? 1 : 0);
+    int incl = mine[k];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    before[k] = incl - mine[k];
+    if (lane == 63) wave_sum[wave][k] = incl;
   }
-  if (lane == 63) wave_sum[wave] = incl;
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_sum[w];
-  const int start = before + incl - mt;
+  if (tid == 0) {
+    int o = 0;
+    for (int k = kB; k >= 1; --k) {  // largest first
+      bucket_start[k] = o;
+      for (int w = 0; w < 16; ++w) o += wave_sum[w][k];
+    }
+    bucket_start[0] = o;
+    *n_tiles = o;
+  }
+  __syncthreads();
   const int slot = tid < na ? tid : -1;
-  for (int i = 0; i < mt; ++i) tiles[start + i] = make_int2(slot, i * BM);
-  if (tid == 1023) *n_tiles = before + incl;
+#pragma unroll
+  for (int k = 1; k <= kB; ++k) {
+    if (!mine[k]) continue;
+    int o = bucket_start[k] + before[k];
+    for (int w = 0; w < wave; ++w) o += wave_sum[w][k];
+    if (k == kB) {
+      for (int i = 0; i < full; ++i) tiles[o + i] = make_int2(slot, i * BM);
+      if (part_nb == kB) tiles[o + full] = make_int2(slot, full * BM);
+    } else {
+      tiles[o] = make_int2(slot, full * BM);
+    }
+  }
 }
 
 // x [T][h] float -> bf16 (round to nearest even), 8 values per thread.
@@ -484,14 +551,11 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const float *__restrict__ 
   reinterpret_cast<uint4 *>(xb)[w] = o;
 }
 
-int grid_blocks(int nb, int max_tiles) {
-  const int total = nb * max_tiles;
-  return (total + kXcds - 1) / kXcds * kXcds;
-}
+int grid_blocks(int nb, int max_tiles) { return kXcds * nb * ((max_tiles + kXcds - 1) / kXcds); }
 
 }  // namespace
 
-bool prefill_shape_ok(int h, int I) { return h % 256 == 0 && I % 128 == 0; }
+bool prefill_shape_ok(int h, int I) { return h % 256 == 0 && I % 256 == 0; }
 
 int prefill_max_tiles(int T, int k, int E, int has_shared) {
   const int n = T * k, routed_slots = E < n ? E : n;

@@ -110,7 +110,7 @@ struct PrefillProblem {
   int32_t *n_tiles;
 };
 
-// Shapes the prefill path takes (h multiple of 256, I of 128).
+// Shapes the prefill path takes (h and I multiples of 256).
 bool prefill_shape_ok(int h, int I);
 // Largest tile count of a call (grid size of the GEMM launches).
 int prefill_max_tiles(int T, int k, int E, int has_shared);

@@ -235,7 +235,7 @@ def test_two_runs_bitwise_identical(dev):
 # The bf16 MFMA (prefill) path on small layers: full outputs.
 # ---------------------------------------------------------------------------
 
-MID = synth.LayerShape(hidden=256, n_experts=16, top_k=4, inter=384, n_shared=1, rsf=2.5, bias_sigma=0.05)
+MID = synth.LayerShape(hidden=256, n_experts=16, top_k=4, inter=512, n_shared=1, rsf=2.5, bias_sigma=0.05)
 
 
 def check_mfma(shape, seed, T, dev, threshold, max_tokens=None, wr=None, bias=None, rows=None):
@@ -253,7 +253,7 @@ def check_mfma(shape, seed, T, dev, threshold, max_tokens=None, wr=None, bias=No
 def test_mfma_path_several_tiles_ragged(dev):
     """T = 300 tokens, 16 experts, k = 4: about 75 tokens per expert, the
     shared expert in 3 tiles (128 + 128 + 44 rows), every N tile count > 1."""
-    log("MFMA path T=300 h=256 I=384 E=16 k=4")
+    log("MFMA path T=300 h=256 I=512 E=16 k=4")
     check_mfma(MID, 21, 300, dev, threshold=64)
 
 
