@@ -128,18 +128,23 @@ struct coli_moe {
   size_t prof_used;
 };
 
+namespace coli {
+thread_local LaunchEvents launch_events = {nullptr, nullptr};
+}
+
 namespace {
 
+// Runs `launch` (one kernel launch); while profiling, that kernel records the
+// next event pair of the handle at its start and end.
 template <class F>
 hipError_t timed(coli_moe_t *m, int kernel, hipStream_t s, F &&launch) {
   if (m->prof_calls_left <= 0 || m->prof_used >= m->prof.size()) return launch();
   ProfRecord &r = m->prof[m->prof_used++];
   r.kernel = kernel;
-  hipError_t e = hipEventRecord(r.start, s);
-  if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  return hipEventRecord(r.stop, s);
+  coli::launch_events = coli::LaunchEvents{r.start, r.stop};  // taken by the launch
+  const hipError_t e = launch();
+  coli::launch_events = coli::LaunchEvents{nullptr, nullptr};
+  return e;
 }
 
 template <class T>

@@ -18,8 +18,7 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_kernel(const int32_
 
 hipError_t launch_dispatch(const int32_t *idx, int n, int E, int32_t *offsets, int32_t *sorted_ids,
                            int32_t *inv, int32_t *active, int32_t *n_active, hipStream_t s) {
-  dispatch_kernel<<<1, kDispatchThreads, 0, s>>>(idx, n, E, offsets, sorted_ids, inv, active, n_active);
-  return hipGetLastError();
+  return launch(dispatch_kernel, 1, kDispatchThreads, 0, s, idx, n, E, offsets, sorted_ids, inv, active, n_active);
 }
 
 }  // namespace coli

@@ -509,24 +509,22 @@ hipError_t launch_gemv_gate_up(const DecodeProblem &P, hipStream_t s) {
   const bool route = small_batch(P.T, P.k);
   if (P.T == 1) {
     if (route)
-      gate_up_kernel<1, true><<<grid, kGuWaves * 64, 0, s>>>(P);
+      return launch(gate_up_kernel<1, true>, grid, kGuWaves * 64, 0, s, P);
     else
-      gate_up_kernel<1, false><<<grid, kGuWaves * 64, 0, s>>>(P);
+      return launch(gate_up_kernel<1, false>, grid, kGuWaves * 64, 0, s, P);
   } else {
     if (route)
-      gate_up_kernel<2, true><<<grid, kGuWaves * 64, 0, s>>>(P);
+      return launch(gate_up_kernel<2, true>, grid, kGuWaves * 64, 0, s, P);
     else
-      gate_up_kernel<2, false><<<grid, kGuWaves * 64, 0, s>>>(P);
+      return launch(gate_up_kernel<2, false>, grid, kGuWaves * 64, 0, s, P);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_down_combine(const DecodeProblem &P, float *out, hipStream_t s) {
   if (P.T == 0) return hipSuccess;
   const int n_slots = P.T * P.k + (P.has_shared ? P.T : 0);
   const int waves = n_slots < 16 ? n_slots : 16;
-  down_combine_kernel<<<P.h / kDcRows, waves * 64, 0, s>>>(P, out);
-  return hipGetLastError();
+  return launch(down_combine_kernel, P.h / kDcRows, waves * 64, 0, s, P, out);
 }
 
 hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s) {
@@ -534,20 +532,18 @@ hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s) {
   if (slots == 0 || P.T == 0) return hipSuccess;
   dim3 grid(P.h / (kDnWaves * kDnRows), slots);
   if (P.T == 1)
-    down_kernel<1><<<grid, kDnWaves * 64, 0, s>>>(P);
+    return launch(down_kernel<1>, grid, kDnWaves * 64, 0, s, P);
   else if (P.T < 4)
-    down_kernel<2><<<grid, kDnWaves * 64, 0, s>>>(P);
+    return launch(down_kernel<2>, grid, kDnWaves * 64, 0, s, P);
   else
-    down_kernel<4><<<grid, kDnWaves * 64, 0, s>>>(P);
-  return hipGetLastError();
+    return launch(down_kernel<4>, grid, kDnWaves * 64, 0, s, P);
 }
 
 hipError_t launch_combine(const float *y, const float *w, const int32_t *inv, int T, int k, int h,
                           int has_shared, float *out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   dim3 grid((h / 4 + 255) / 256, T);
-  combine_kernel<<<grid, 256, 0, s>>>(y, w, inv, T, k, h, has_shared, out);
-  return hipGetLastError();
+  return launch(combine_kernel, grid, 256, 0, s, y, w, inv, T, k, h, has_shared, out);
 }
 
 }  // namespace coli

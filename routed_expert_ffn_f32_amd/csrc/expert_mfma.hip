@@ -564,25 +564,21 @@ int prefill_max_tiles(int T, int k, int E, int has_shared) {
 
 hipError_t launch_prefill_prep(const float *x, int T, int h, __bf16 *xb, hipStream_t s) {
   const size_t n_words = (size_t)T * h / 8;
-  to_bf16_kernel<<<(unsigned)((n_words + 255) / 256), 256, 0, s>>>(x, n_words, xb);
-  return hipGetLastError();
+  return launch(to_bf16_kernel, (unsigned)((n_words + 255) / 256), 256, 0, s, x, n_words, xb);
 }
 
 hipError_t launch_build_tiles(const PrefillProblem &P, hipStream_t s) {
-  build_tiles_kernel<<<1, 1024, 0, s>>>(P.offsets, P.active, P.n_active, P.T, P.has_shared, P.tiles, P.n_tiles);
-  return hipGetLastError();
+  return launch(build_tiles_kernel, 1, 1024, 0, s, P.offsets, P.active, P.n_active, P.T, P.has_shared, P.tiles, P.n_tiles);
 }
 
 hipError_t launch_gate_up_mfma(const PrefillProblem &P, hipStream_t s) {
   const int blocks = grid_blocks(P.I / 128, prefill_max_tiles(P.T, P.k, P.E, P.has_shared));
-  gate_up_mfma_kernel<<<blocks, kThreads, 0, s>>>(P);
-  return hipGetLastError();
+  return launch(gate_up_mfma_kernel, blocks, kThreads, 0, s, P);
 }
 
 hipError_t launch_down_mfma(const PrefillProblem &P, hipStream_t s) {
   const int blocks = grid_blocks(P.h / 256, prefill_max_tiles(P.T, P.k, P.E, P.has_shared));
-  down_mfma_kernel<<<blocks, kThreads, 0, s>>>(P);
-  return hipGetLastError();
+  return launch(down_mfma_kernel, blocks, kThreads, 0, s, P);
 }
 
 }  // namespace coli

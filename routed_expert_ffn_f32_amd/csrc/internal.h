@@ -4,11 +4,33 @@
 #pragma once
 
 #include <hip/hip_bf16.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace coli {
+
+// Kernel launch.  When the library's profiling wrapper has set an event pair,
+// the launch records it at the kernel's own start and end (AMD's extended
+// launch), so that the measured time is the kernel's duration alone.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+extern thread_local LaunchEvents launch_events;
+
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args &&...args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+  if (launch_events.start) {
+    const LaunchEvents ev = launch_events;
+    launch_events = LaunchEvents{nullptr, nullptr};
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0u, static_cast<KArgs>(args)...);
+  } else {
+    kernel<<<grid, block, shmem, s>>>(static_cast<KArgs>(args)...);
+  }
+  return hipGetLastError();
+}
 
 constexpr int kWave = 64;              // CDNA wavefront width
 constexpr int kMaxExperts = 512;       // dispatch keeps per-wave histograms of E bins in LDS

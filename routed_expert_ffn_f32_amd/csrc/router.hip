@@ -197,8 +197,7 @@ hipError_t launch_router_permute(const float *wr, float *wrP, int h, int E, hipS
   const size_t n = (size_t)E * MB * 256;
   const size_t want = (n + 255) / 256;
   const int blocks = (int)(want < 4096 ? want : 4096);
-  router_permute_kernel<<<blocks, 256, 0, s>>>(wr, wrP, h, E);
-  return hipGetLastError();
+  return launch(router_permute_kernel, blocks, 256, 0, s, wr, wrP, h, E);
 }
 
 size_t router_permuted_floats(int h, int E) { return (size_t)E * ((((h >> 6) + 3) >> 2)) * 256; }
@@ -209,30 +208,27 @@ hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, 
   const int qblocks = xq ? (int)(((size_t)T * (h >> 3) + 255) / 256) : 0;
   if (T < 4) {
     const int nlb = T * ((E + 3) / 4);
-    router_logits_kernel<1, 1><<<nlb + qblocks, 256, 0, s>>>(x, wrP, T, h, E, logits, nlb, xq, xs);
+    return launch(router_logits_kernel<1, 1>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
   } else if (T < 64) {
     const int nlb = ((T + 3) / 4) * ((E + 7) / 8);
-    router_logits_kernel<2, 4><<<nlb + qblocks, 256, 0, s>>>(x, wrP, T, h, E, logits, nlb, xq, xs);
+    return launch(router_logits_kernel<2, 4>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
   } else {
     const int nlb = ((T + 3) / 4) * ((E + 15) / 16);
-    router_logits_kernel<4, 4><<<nlb + qblocks, 256, 0, s>>>(x, wrP, T, h, E, logits, nlb, xq, xs);
+    return launch(router_logits_kernel<4, 4>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_router_select(const float *logits, const float *bias, int T, int E, int k, float rsf,
                                 int32_t *idx, float *w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  router_select_kernel<<<(T + 3) / 4, 256, 0, s>>>(logits, bias, T, E, k, rsf, idx, w);
-  return hipGetLastError();
+  return launch(router_select_kernel, (T + 3) / 4, 256, 0, s, logits, bias, T, E, k, rsf, idx, w);
 }
 
 hipError_t launch_select_dispatch(const float *logits, const float *bias, int T, int E, int k, float rsf,
                                   int32_t *idx, float *w, int32_t *offsets, int32_t *sorted_ids, int32_t *inv,
                                   int32_t *active, int32_t *n_active, hipStream_t s) {
-  select_dispatch_kernel<<<1, kDispatchThreads, 0, s>>>(logits, bias, T, E, k, rsf, idx, w, offsets, sorted_ids,
+  return launch(select_dispatch_kernel, 1, kDispatchThreads, 0, s, logits, bias, T, E, k, rsf, idx, w, offsets, sorted_ids,
                                                         inv, active, n_active);
-  return hipGetLastError();
 }
 
 }  // namespace coli
