@@ -9,6 +9,7 @@
 // checks the setup without computing).  The per-handle device state (router
 // copy, expert offsets) follows the opaque context of the cf-1.com Colibri
 // article, section 3.2.
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -41,7 +42,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 // Byte offsets of the workspace regions.
 struct Layout {
-  size_t wrP, logits, xq, xs, idx, w, offsets, sorted_ids, inv, active, n_active, mq, ms, y;
+  size_t wrP, logits, xq, xs, idx, w, offsets, sorted_ids, inv, active, n_active, mq, ms, midf, y;
   size_t xb, midb, tiles, n_tiles;  // prefill path
   size_t total;
 };
@@ -95,6 +96,7 @@ Layout layout_of(const coli_moe_config_t &c) {
   L.n_active = o;   o = align_up(o + 4);
   L.mq = o;         o = align_up(o + P * planes * (I / 8) * 4);
   L.ms = o;         o = align_up(o + P * (I / 32) * 4);
+  L.midf = o;       o = align_up(o + P * I * 4);
   L.y = o;          o = align_up(o + P * h * 4);
   const bool pre = prefill_shape(c) && (c.prefill_threshold == 0 ? 256 : c.prefill_threshold) <= c.max_tokens;
   const size_t tiles = pre ? (size_t)coli::prefill_max_tiles(c.max_tokens, c.top_k, c.n_experts, c.n_shared) : 0;
@@ -225,8 +227,10 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
   const float rsf = c.routed_scaling_factor;
 
   const bool prefill = T >= c.prefill_threshold && prefill_shape(c);
+  const bool small = !prefill && coli::small_batch(T, k, h, I);
   hipError_t e;
-  // 1. router logits (and, for the GEMV path, the hidden rows in digit-plane form)
+  // 1. router logits (and, for the GEMV path, the hidden rows in digit-plane
+  // form); small batches compute both inside their gate/up launch
   e = timed(m, K_ROUTER_LOGITS, s, [&] {
     return coli::launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill ? nullptr : xq, xs, s);
   });
@@ -311,6 +315,7 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
   P.xs = xs;
   P.mq = at<uint32_t>(m, L.mq);
   P.ms = at<float>(m, L.ms);
+  P.midf = at<float>(m, L.midf);
   P.y = y;
   P.idx = idx;
   P.wsel = wsel;
@@ -320,8 +325,8 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
   P.active = active;
   P.n_active = n_active;
 
-  if (coli::small_batch(T, k)) {
-    // 2. gate/up (each routed block routes the batch itself), 3. down + combine
+  if (small) {
+    // 2. gate/up (each block routes the batch itself), 3. down + combine
     e = timed(m, K_GATE_UP, s, [&] { return coli::launch_gemv_gate_up(P, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     e = timed(m, K_DOWN, s, [&] { return coli::launch_down_combine(P, out, s); });

@@ -18,21 +18,19 @@
 // activation scale.  Results accumulate in float32.
 //
 // Launch structure of one decode call (T tokens):
-//   gate/up   grid (I/32, slots): slot 0 is the shared expert, which needs no
-//             routing and starts streaming at once; the other slots are the
-//             active routed experts.  For small batches every routed block
-//             selects the experts of all T tokens and sorts the assignments
-//             itself in LDS (a few microseconds, identical in every block)
-//             instead of waiting for a separate launch; one block publishes
-//             the routing.  A block owns 32 rows of I for one expert and
-//             writes the SwiGLU result as digit planes.
-//   down      small batches: grid (h/8): one wave per (token, slot) and per
-//             shared-expert token computes 8 rows of its expert's output into
-//             LDS; the block sums w_j * y_j in slot order plus the shared row
-//             into the output (the weighted combine fused, no intermediate y
-//             in HBM); larger batches: y per assignment, then a combine kernel.
+//   small batches (T <= 4): gate/up with the routing computed inside every
+//             block (a few microseconds, identical in every block; one block
+//             publishes it) and the (slot, row) pairs split evenly over the
+//             waves of the grid; then down fused with the weighted combine
+//             (no intermediate y in HBM).  See the kernels' own comments.
+//   larger batches: selection and dispatch in their own launch, gate/up over
+//             grid (I/32, slots) -- slot 0 the shared expert, the others the
+//             active routed experts, a block owning 32 rows of I and writing
+//             the SwiGLU result as digit planes -- then y per assignment and
+//             a combine kernel.
 #include "internal.h"
 #include "select.h"
+#include "small_route.h"
 #include "wave.h"
 
 namespace coli {
@@ -48,94 +46,8 @@ constexpr int kGuRows = COLI_GU_ROWS;      // gate/up rows per wave
 constexpr int kGuWaves = 32 / kGuRows;     // a block owns 32 rows of I
 constexpr int kDnWaves = 4;  // down block (larger batches): 4 waves x 8 rows
 constexpr int kDnRows = 8;
-#ifndef COLI_DC_ROWS
-#define COLI_DC_ROWS 8
-#endif
-constexpr int kDcRows = COLI_DC_ROWS;  // fused down + combine block: rows, one wave per slot
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
-
-// ---------------------------------------------------------------------------
-// Routing of a small batch inside one block (T <= kSmallT tokens, T*k <= 64).
-// ---------------------------------------------------------------------------
-struct SmallRouting {
-  SelectScratch sc[kSmallT];
-  int32_t idx[kSmallAssign];
-  float w[kSmallAssign];
-  int32_t sorted_ids[kSmallAssign];
-  int32_t inv[kSmallAssign];
-  int32_t sorted_key[kSmallAssign];
-  int32_t active[kSmallAssign];
-  int32_t seg_begin[kSmallAssign + 1];
-  int32_t n_active;
-};
-
-// Waves 0..T-1 select one token each; wave 0 then sorts the n = T*k
-// assignments by expert, stably (position = smaller keys + equal keys of
-// lower a), and lists the segments.  Ends with the block synchronised.
-__device__ __forceinline__ void route_small(const float *__restrict__ logits, const float *__restrict__ bias, int T,
-                                            int E, int k, float rsf, SmallRouting &R) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave < T) {
-    int e;
-    float w;
-    select_token(logits + (size_t)wave * E, bias, E, k, rsf, e, w, R.sc[wave]);
-    if (lane < k) {
-      R.idx[wave * k + lane] = e;
-      R.w[wave * k + lane] = w;
-    }
-  }
-  __syncthreads();
-  const int n = T * k;
-  if (wave == 0) {
-    const bool valid = lane < n;
-    const int key = valid ? R.idx[lane] : 0;
-    int before = 0;
-    for (int b = 0; b < n; ++b) {
-      const int kb = R.idx[b];
-      before += (kb < key) || (kb == key && b < lane);
-    }
-    if (valid) {
-      R.sorted_ids[before] = lane;
-      R.inv[lane] = before;
-      R.sorted_key[before] = key;
-    }
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const bool start = lane < n && (lane == 0 || R.sorted_key[lane] != R.sorted_key[lane > 0 ? lane - 1 : 0]);
-    const uint64_t m = __ballot(start);
-    const int slot = __popcll(m & ((1ull << lane) - 1));
-    if (start) {
-      R.active[slot] = R.sorted_key[lane];
-      R.seg_begin[slot] = lane;
-    }
-    if (lane == 0) {
-      R.n_active = __popcll(m);
-      R.seg_begin[__popcll(m)] = n;
-    }
-  }
-  __syncthreads();
-}
-
-// The routing of the call in the layout of the C ABI (idx, w, offsets[E+1],
-// sorted_ids, inv, active, n_active), written by one block.
-__device__ __forceinline__ void publish_routing(const SmallRouting &R, const DecodeProblem &P) {
-  const int n = P.T * P.k;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    P.idx[i] = R.idx[i];
-    P.wsel[i] = R.w[i];
-    P.sorted_ids[i] = R.sorted_ids[i];
-    P.inv[i] = R.inv[i];
-  }
-  for (int e = threadIdx.x; e <= P.E; e += blockDim.x) {
-    int c = 0;
-    for (int a = 0; a < n; ++a) c += R.idx[a] < e;
-    P.offsets[e] = c;
-  }
-  for (int s = threadIdx.x; s < R.n_active; s += blockDim.x) P.active[s] = R.active[s];
-  if (threadIdx.x == 0) *P.n_active = R.n_active;
-}
 
 struct Slot {
   const uint8_t *qa, *qb;
@@ -274,13 +186,11 @@ __device__ __forceinline__ Slot expert_slot(const DecodeProblem &P, int e, int p
   return S;
 }
 
-// grid = (I / 32, has_shared + n_routed_slots), 256 threads.  ROUTE: the
-// small-batch routing is computed in the block (and published by block
-// (0, has_shared)); otherwise it is read from the dispatch arrays.
-template <int NTMAX, bool ROUTE>
+// grid = (I / 32, has_shared + n_routed_slots), 256 threads; the routing
+// and dispatch arrays come from the selection launch.
+template <int NTMAX>
 __global__ __launch_bounds__(kGuWaves * 64, COLI_GU_MIN_WAVES) void gate_up_kernel(DecodeProblem P) {
   __shared__ float mid_lds[kGuWaves * kGuRows][4];
-  __shared__ SmallRouting R;
   const int row0 = blockIdx.x * (kGuWaves * kGuRows);
   const int slot = (int)blockIdx.y - P.has_shared;
   if (slot < 0) {  // shared expert: every token, weight 1
@@ -295,91 +205,485 @@ __global__ __launch_bounds__(kGuWaves * 64, COLI_GU_MIN_WAVES) void gate_up_kern
     return;
   }
   const int k = P.k;
-  if (ROUTE) {
-    route_small(P.logits, P.bias, P.T, P.E, k, P.rsf, R);
-    if (blockIdx.x == 0 && slot == 0) publish_routing(R, P);
-    if (slot >= R.n_active) return;  // uniform over the block
-    const int b = R.seg_begin[slot];
-    const Slot S = expert_slot(P, R.active[slot], b, R.seg_begin[slot + 1] - b);
-    gate_up_slot<NTMAX>(P, S, row0, [&](int i) { return R.sorted_ids[b + i] / k; }, mid_lds);
-  } else {
-    if (slot >= *P.n_active) return;
-    const int e = P.active[slot];
-    const int b = P.offsets[e];
-    const Slot S = expert_slot(P, e, b, P.offsets[e + 1] - b);
-    const int32_t *sid = P.sorted_ids;
-    gate_up_slot<NTMAX>(P, S, row0, [&](int i) { return sid[b + i] / k; }, mid_lds);
-  }
+  if (slot >= *P.n_active) return;
+  const int e = P.active[slot];
+  const int b = P.offsets[e];
+  const Slot S = expert_slot(P, e, b, P.offsets[e + 1] - b);
+  const int32_t *sid = P.sorted_ids;
+  gate_up_slot<NTMAX>(P, S, row0, [&](int i) { return sid[b + i] / k; }, mid_lds);
 }
 
 // ---------------------------------------------------------------------------
-// down + combine, small batches: out[t][r] = sum_j w[t,j] y_(t,j)[r] + y_sh[t][r]
+// Small batches (T <= kSmallT): row-streaming kernels.
+//
+// gate/up: the (slot, row) pairs of the call -- slot 0 the shared expert,
+// then the active routed experts in ascending order, I rows each -- are split
+// into equal contiguous runs, one per wave of the grid, so every wave streams
+// the same number of gate and up rows whatever the routing.  A row is h/32
+// chunks of 32 columns (16 bytes of codes each); lane l takes chunks
+// l, l + 64, ..., so one wave-load covers 1 KB of a row.  kSbDepth rows are
+// in flight per wave.  The hidden rows' digit planes are held in registers
+// (T = 1) or in LDS (T = 2..4).  Each row ends in two wave reductions per
+// token and one float32 store of silu(g) * u.
+//
+// down + combine: block b owns output rows [b R, b R + R).  Wave w takes the
+// slots w, w + waves, ... (slot a < T*k: assignment a; T*k + t: the shared
+// expert on token t).  For its slot it first quantises the float32
+// intermediate into digit planes -- lane l owns the 32-column block l, so the
+// block scale is lane-local -- and keeps them in registers, then streams the
+// R down rows of the slot's expert, kDcDepth rows in flight, into LDS.  The
+// block then sums w_j * y_j in slot order plus the shared row into `out`.
 // ---------------------------------------------------------------------------
+#ifndef COLI_SB_DEPTH
+#define COLI_SB_DEPTH 2
+#endif
+#ifndef COLI_SB_BLOCKS
+#define COLI_SB_BLOCKS 512
+#endif
+#ifndef COLI_DC_WAVES
+#define COLI_DC_WAVES 8
+#endif
+#ifndef COLI_DC_BLOCKS
+#define COLI_DC_BLOCKS 256
+#endif
+constexpr int kSbDepth = COLI_SB_DEPTH;     // gate/up rows in flight per wave
+constexpr int kSbBlocks = COLI_SB_BLOCKS;   // gate/up grid, T = 1 (4 waves per block)
+constexpr int kSbBlocksLds = kSbBlocks / 2; // gate/up grid, T = 2..4 (8 waves per block)
+constexpr int kDcWaves = COLI_DC_WAVES;     // down: waves per block
+constexpr int kDcBlocks = COLI_DC_BLOCKS;   // down: blocks (at most; fewer when h is small)
+constexpr int kDcLds = 64 * 1024;           // down: LDS for the digit planes of a slot group
+constexpr int kSbMaxXChunks = 4;            // T = 1 keeps the planes of h <= 64*32*4 columns in registers
+constexpr int kSbMaxXLds = 96 * 1024;       // bytes of hidden-row planes staged in LDS
+constexpr int kDcMaxChunks = 4;             // down: I <= 64*32*4
 
-// grid = h / kDcRows, blockDim = 64 * min(16, S) with S = T*k + T*has_shared
-// "slots": slot a < T*k is assignment a (expert idx[a], intermediate row
-// inv[a]), slot T*k + t the shared expert on token t.  Wave w computes the
-// kDcRows output rows of the block for slots w, w + waves, ... (one memory
-// round trip per slot) into LDS; the block then sums, per token and row,
-// w_j * y_j in slot order and the shared row last.
-__global__ __launch_bounds__(1024) void down_combine_kernel(DecodeProblem P, float *__restrict__ out) {
-  __shared__ float part[kSmallT * (kMaxTopK + 1)][kDcRows];
-  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), waves = blockDim.x >> 6;
-  const int r0 = blockIdx.x * kDcRows;
-  const int h = P.h, I = P.I, k = P.k, T = P.T;
-  const int rowq = I >> 1, groups = I >> 6, words = I >> 3, blocks = I >> 5, nch = I >> 5;
-  const int n_slots = T * k + (P.has_shared ? T : 0);
-  const size_t qstride = (size_t)h * (I >> 1), sstride = (size_t)h * (I >> 6);
-  const uint32_t qbytes = (uint32_t)h * rowq, sbytes = (uint32_t)h * groups * 4;
-  const int n_rows_mid = T * k + (P.has_shared ? T : 0);
-  const Rsrc rm = make_rsrc(P.mq, (uint32_t)n_rows_mid * kPlanes * words * 4);
-  const Rsrc rms = make_rsrc(P.ms, (uint32_t)n_rows_mid * blocks * 4);
-  for (int sl = wave; sl < n_slots; sl += waves) {
-    const uint8_t *q;
-    const float *sc;
-    int p;
-    if (sl < T * k) {
-      const int e = uniform(P.idx[sl]);
-      q = P.down.q + e * qstride;
-      sc = P.down.s + e * sstride;
-      p = uniform(P.inv[sl]);
-    } else {
-      q = P.sh_down.q;
-      sc = P.sh_down.s;
-      p = sl;  // T*k + t
-    }
-    const Rsrc rq = make_rsrc(q, qbytes), rs = make_rsrc(sc, sbytes);
-    float acc[kDcRows];
+// Where the gate/up rows of a slot come from, and its assignment positions.
+struct GuCursor {
+  int slot, r;              // slot and row of I
+  const uint8_t *qg, *qu;   // gate and up codes of the slot's expert
+  const float *sg, *su;     // and scales
+  int p_begin, cnt;         // positions p_begin .. p_begin + cnt - 1 of mid
+};
+
+__device__ __forceinline__ void gu_set_slot(const DecodeProblem &P, const SmallRouting &R, GuCursor &c) {
+  const int hs = P.has_shared;
+  if (c.slot < hs) {
+    c.qg = P.sh_gate.q;
+    c.sg = P.sh_gate.s;
+    c.qu = P.sh_up.q;
+    c.su = P.sh_up.s;
+    c.p_begin = P.T * P.k;
+    c.cnt = P.T;
+    return;
+  }
+  const int s = min(c.slot - hs, kSmallAssign - 1);
+  const int e = uniform(R.active[s]);
+  const size_t qstride = (size_t)P.I * (P.h >> 1), sstride = (size_t)P.I * (P.h >> 6);
+  c.qg = P.gate.q + e * qstride;
+  c.sg = P.gate.s + e * sstride;
+  c.qu = P.up.q + e * qstride;
+  c.su = P.up.s + e * sstride;
+  c.p_begin = uniform(R.seg_begin[s]);
+  c.cnt = uniform(R.seg_begin[s + 1]) - c.p_begin;
+}
+
+// A wave's rows: na rows of the shared expert starting at row a0 (known
+// before the routing), then routed rows from flat index b0 over the active
+// experts' rows (expert slot s covers flat indices s*I .. s*I + I - 1), n rows
+// in all.
+struct GuSeq {
+  int na, a0, b0, n;
+};
+
+__device__ __forceinline__ void seq_seek(const DecodeProblem &P, const SmallRouting &R, const GuSeq &q, int i,
+                                         GuCursor &c) {
+  if (i < q.na) {
+    c.slot = 0;
+    c.r = q.a0 + i;
+  } else {
+    const int f = q.b0 + (i - q.na);
+    c.slot = P.has_shared + f / P.I;
+    c.r = f % P.I;
+  }
+  gu_set_slot(P, R, c);
+}
+
+// Moves c from row i to row i + 1 of the sequence (i + 1 < q.n).
+__device__ __forceinline__ void seq_next(const DecodeProblem &P, const SmallRouting &R, const GuSeq &q, int i,
+                                         GuCursor &c) {
+  if (i + 1 == q.na) {
+    seq_seek(P, R, q, i + 1, c);
+  } else if (++c.r == P.I) {
+    c.r = 0;
+    ++c.slot;
+    gu_set_slot(P, R, c);
+  }
+}
+
+template <int NCH>
+struct GuBuf {
+  uint4 g[NCH], u[NCH];
+  float gs[NCH], us[NCH];
+};
+
+// Codes and scales of row c.r of the slot's gate and up matrices for this
+// lane's chunks; an invalid row (or chunks past the row) reads zeros.
+template <int NCH>
+__device__ __forceinline__ void gu_load(GuBuf<NCH> &b, const GuCursor &c, bool valid, int h) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t rowq = (uint32_t)h >> 1, rows = (uint32_t)(h >> 6) * 4;
+  const size_t r = (size_t)c.r;
+  const Rsrc qg = make_rsrc(c.qg + r * rowq, valid ? rowq : 0u);
+  const Rsrc qu = make_rsrc(c.qu + r * rowq, valid ? rowq : 0u);
+  const Rsrc sg = make_rsrc(c.sg + r * (h >> 6), valid ? rows : 0u);
+  const Rsrc su = make_rsrc(c.su + r * (h >> 6), valid ? rows : 0u);
 #pragma unroll
-    for (int r = 0; r < kDcRows; ++r) acc[r] = 0.0f;
-    for (int lc = lane; lc < nch; lc += 64) {
-      uint4 dw[kDcRows];
-      float ds[kDcRows];
+  for (int cc = 0; cc < NCH; ++cc) {
+    const uint32_t lc = (uint32_t)(lane + 64 * cc);
+    b.g[cc] = bload16(qg, lc * 16, 0);
+    b.u[cc] = bload16(qu, lc * 16, 0);
+  }
 #pragma unroll
-      for (int r = 0; r < kDcRows; ++r) {
-        dw[r] = bload16(rq, (uint32_t)lc * 16, (uint32_t)(r0 + r) * rowq);
-        ds[r] = bloadf(rs, (uint32_t)(lc >> 1) * 4, (uint32_t)(r0 + r) * groups * 4);
+  for (int cc = 0; cc < NCH; ++cc) {
+    const uint32_t lc = (uint32_t)(lane + 64 * cc);
+    b.gs[cc] = bloadf(sg, (lc >> 1) * 4, 0);
+    b.us[cc] = bloadf(su, (lc >> 1) * 4, 0);
+  }
+}
+
+// silu(g) * u of one row for every token of the slot, stored as float32.
+// XREG: the single token's planes are xr/xsr; otherwise they are read from
+// LDS (planes [T][6][nch] as uint4, then scales [T][nch]), one token at a
+// time.
+template <int NCH, bool XREG>
+__device__ __forceinline__ void gu_consume(const GuBuf<NCH> &b, const GuCursor &c, bool valid,
+                                           const uint4 (&xr)[XREG ? NCH : 1][kPlanes],
+                                           const float (&xsr)[XREG ? NCH : 1], const uint4 *xl, int nch,
+                                           const SmallRouting &R, const DecodeProblem &P) {
+  const int lane = threadIdx.x & 63;
+  const int cnt = XREG ? 1 : c.cnt, n_routed = P.T * P.k;
+  for (int t = 0; t < cnt; ++t) {
+    float g = 0.0f, u = 0.0f;
+    const int pos = c.p_begin + t;
+    const int tok = XREG ? 0 : pos < n_routed ? uniform(R.sorted_ids[pos]) / P.k : pos - n_routed;
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+      uint4 xt[kPlanes];
+      float sx;
+      if (XREG) {
+#pragma unroll
+        for (int j = 0; j < kPlanes; ++j) xt[j] = xr[XREG ? cc : 0][j];
+        sx = xsr[XREG ? cc : 0];
+      } else {
+        const int lc = min(lane + 64 * cc, nch - 1);  // lanes past the row meet zero weights
+#pragma unroll
+        for (int j = 0; j < kPlanes; ++j) xt[j] = xl[(tok * kPlanes + j) * nch + lc];
+        sx = reinterpret_cast<const float *>(xl + P.T * kPlanes * nch)[tok * nch + lc];
       }
-      uint4 xp[kPlanes];
-#pragma unroll
-      for (int j = 0; j < kPlanes; ++j) xp[j] = bload16(rm, (uint32_t)lc * 16, (uint32_t)(p * kPlanes + j) * words * 4);
-      const float sx = bloadf(rms, (uint32_t)lc * 4, (uint32_t)p * blocks * 4);
-#pragma unroll
-      for (int r = 0; r < kDcRows; ++r) acc[r] = __builtin_fmaf((float)dot_planes(dw[r], xp), ds[r] * sx, acc[r]);
+      g = __builtin_fmaf((float)dot_planes(b.g[cc], xt), b.gs[cc] * sx, g);
+      u = __builtin_fmaf((float)dot_planes(b.u[cc], xt), b.us[cc] * sx, u);
     }
-#pragma unroll
-    for (int r = 0; r < kDcRows; ++r) {
-      const float v = wave_sum(acc[r]);
-      if (lane == r) part[sl][r] = v;  // kDcRows <= 64
+    if (valid) {
+      const float gg = wave_sum(g);
+      const float uu = wave_sum(u);
+      if (lane == 0) P.midf[(size_t)(c.p_begin + t) * P.I + c.r] = gg / (1.0f + expf(-gg)) * uu;
     }
   }
+}
+
+// grid = kSbBlocks (XREG: 4 waves) or kSbBlocksLds (8 waves) blocks.  Dynamic
+// LDS (!XREG): the hidden rows' digit planes [T][6][h/32] uint4, then scales
+// [T][h/32].
+template <int NCH, bool XREG>
+__global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodeProblem P) {
+  extern __shared__ uint4 xl[];
+  __shared__ SmallRouting R;
+  constexpr int kWaves = XREG ? 4 : 8;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int h = P.h, I = P.I, T = P.T, nch = h >> 5;
+  uint4 xr[XREG ? NCH : 1][kPlanes];
+  float xsr[XREG ? NCH : 1];
+  // 1. the routing waves' logits first in the load queue
+  SelectInput sel;
+  if (wave < T) select_load(P.logits + (size_t)wave * P.E, P.bias, P.E, sel);
+  // 2. the hidden rows' digit planes (written by the router launch): token
+  // 0's chunks of this lane into registers, or every token's into LDS
+  if (XREG) {
+    const Rsrc rx = make_rsrc(P.xq, (uint32_t)kPlanes * (h >> 3) * 4);
+    const Rsrc rxs = make_rsrc(P.xs, (uint32_t)nch * 4);
+#pragma unroll
+    for (int cc = 0; cc < (XREG ? NCH : 1); ++cc) {
+      const uint32_t lc = (uint32_t)(lane + 64 * cc);
+      const bool in = (int)lc < nch;
+#pragma unroll
+      for (int j = 0; j < kPlanes; ++j) xr[cc][j] = bload16(rx, in ? lc * 16 : 0x7fffffffu, (uint32_t)j * (h >> 3) * 4);
+      xsr[cc] = bloadf(rxs, lc * 4, 0);
+    }
+  } else {
+    const int n = T * kPlanes * nch;
+    const uint4 *src = reinterpret_cast<const uint4 *>(P.xq);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) xl[i] = src[i];
+    float *xsl = reinterpret_cast<float *>(xl + n);
+    for (int i = threadIdx.x; i < T * nch; i += blockDim.x) xsl[i] = P.xs[i];
+  }
+  // 3. this wave's share of the shared expert's rows needs no routing: its
+  // first rows are requested before the routing is known
+  const int64_t W = (int64_t)gridDim.x * kWaves, gw = (int64_t)blockIdx.x * kWaves + wave;
+  GuSeq q;
+  q.a0 = P.has_shared ? (int)((int64_t)I * gw / W) : 0;
+  q.na = P.has_shared ? (int)((int64_t)I * (gw + 1) / W) - q.a0 : 0;
+  constexpr int D = NCH > 4 ? 1 : kSbDepth;  // wide rows: one in flight (register file)
+  GuBuf<NCH> buf[D];
+  GuCursor pre{};
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (d < q.na) {
+      pre.slot = 0;
+      pre.r = q.a0 + d;
+      gu_set_slot(P, R, pre);  // the shared expert: no routing needed
+      gu_load(buf[d], pre, true, h);
+    }
+  }
+  // 4. the routing of the batch (one block barrier inside)
+  route_small(sel, T, P.E, P.k, P.rsf, R);
+  if (blockIdx.x == 0) {
+    const RoutingOut o{P.idx, P.wsel, P.sorted_ids, P.inv, P.offsets, P.active, P.n_active};
+    publish_routing(R, T, P.k, P.E, o);
+  }
+  const int64_t Nr = (int64_t)R.n_active * I;
+  q.b0 = (int)(Nr * gw / W);
+  q.n = q.na + (int)(Nr * (gw + 1) / W) - q.b0;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (d >= q.na) {
+      const bool v = d < q.n;
+      if (v) seq_seek(P, R, q, d, pre);
+      gu_load(buf[d], pre, v, h);
+    }
+  }
+  if (D < q.n) seq_seek(P, R, q, D, pre);
+  GuCursor cur{};
+  seq_seek(P, R, q, 0, cur);
+  for (int i = 0; i < q.n; i += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int ic = i + d;
+      const bool v = ic < q.n;
+      gu_consume<NCH, XREG>(buf[d], cur, v, xr, xsr, xl, nch, R, P);
+      if (ic + 1 < q.n) seq_next(P, R, q, ic, cur);
+      const int ip = ic + D;
+      const bool pv = ip < q.n;
+      gu_load(buf[d], pre, pv, h);
+      if (ip + 1 < q.n) seq_next(P, R, q, ip, pre);
+    }
+  }
+}
+
+// Digit planes of 32 consecutive float32 values (a lane-owned block): scale
+// 2^(e - 22) with 2^e > max |v|, N = rint(v / scale), |N| <= 2^22, and the
+// balanced base-16 digits of N read off M = N + 0x888888 (0 <= M < 2^24):
+// digit j is ((M >> 4j) & 15) - 8, whose 4-bit code is ((M >> 4j) & 15) ^ 8.
+__device__ __forceinline__ float quantize_block32(const float (&v)[32], uint4 (&planes)[kPlanes]) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
+  int e = 0;
+  (void)__builtin_frexpf(m, &e);
+  e = m > 0.0f ? max(e, kMinExp) : kMinExp;
+  const float to_int = __int_as_float((127 + kMantBits - e) << 23);
+  const float to_real = __int_as_float((127 - kMantBits + e) << 23);
+  uint32_t M[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) M[i] = (uint32_t)((int)__builtin_rintf(v[i] * to_int) + 0x888888);
+#pragma unroll
+  for (int j = 0; j < kPlanes; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= ((M[8 * q + i] >> (4 * j)) & 15u) << (4 * i);
+      w[q] = word ^ 0x88888888u;
+    }
+    planes[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return to_real;
+}
+
+template <int NCHD>
+struct DnBuf {
+  uint4 w[NCHD];
+  float s[NCHD];
+};
+
+template <int NCHD>
+__device__ __forceinline__ void dn_load(DnBuf<NCHD> &b, const uint8_t *q, const float *sc, int row, bool valid,
+                                        int I) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t rowq = (uint32_t)I >> 1, rows = (uint32_t)(I >> 6) * 4;
+  const Rsrc rq = make_rsrc(q + (size_t)row * rowq, valid ? rowq : 0u);
+  const Rsrc rs = make_rsrc(sc + (size_t)row * (I >> 6), valid ? rows : 0u);
+#pragma unroll
+  for (int cc = 0; cc < NCHD; ++cc) b.w[cc] = bload16(rq, (uint32_t)(lane + 64 * cc) * 16, 0);
+#pragma unroll
+  for (int cc = 0; cc < NCHD; ++cc) b.s[cc] = bloadf(rs, (uint32_t)((lane + 64 * cc) >> 1) * 4, 0);
+}
+
+// Slot q of the down sequence: tokens in order, each token's k routed
+// assignments in slot order and then its shared-expert slot.  The block
+// reads the routing once into LDS (expert, or -1 for the shared expert;
+// position of the intermediate row; combine weight).
+struct DnTable {
+  int32_t e[kSmallAssign + kSmallT];
+  int32_t p[kSmallAssign + kSmallT];
+  float w[kSmallAssign + kSmallT];
+};
+
+struct DnSlot {
+  const uint8_t *q;
+  const float *s;
+  int t;
+  float w;
+};
+
+__device__ __forceinline__ void dn_table(const DecodeProblem &P, DnTable &D) {
+  const int ks = P.k + P.has_shared, n_slots = P.T * ks;
+  for (int qs = threadIdx.x; qs < n_slots; qs += blockDim.x) {
+    const int t = qs / ks, j = qs % ks;
+    if (j < P.k) {
+      const int a = t * P.k + j;
+      D.e[qs] = P.idx[a];
+      D.p[qs] = P.inv[a];
+      D.w[qs] = P.wsel[a];
+    } else {
+      D.e[qs] = -1;
+      D.p[qs] = P.T * P.k + t;
+      D.w[qs] = 1.0f;
+    }
+  }
+}
+
+__device__ __forceinline__ DnSlot dn_slot(const DecodeProblem &P, const DnTable &D, int qs) {
+  DnSlot d;
+  d.t = qs / (P.k + P.has_shared);
+  const int e = uniform(D.e[qs]);
+  if (e >= 0) {
+    d.q = P.down.q + e * ((size_t)P.h * (P.I >> 1));
+    d.s = P.down.s + e * ((size_t)P.h * (P.I >> 6));
+  } else {
+    d.q = P.sh_down.q;
+    d.s = P.sh_down.s;
+  }
+  d.w = __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, D.w[qs])));
+  return d;
+}
+
+__device__ __forceinline__ int dn_slot_token(const DecodeProblem &P, int qs) { return qs / (P.k + P.has_shared); }
+
+// Down projection fused with the weighted combine, small batches.
+// grid = Gd blocks of kDcWaves waves; wave w of the grid owns output rows
+// [w h / W, (w + 1) h / W) (at most RM).  The slots are taken in groups of
+// gs: the block first writes the digit planes of the group's intermediate
+// rows into LDS (one thread per 32-column block: [slot][plane][chunk] uint4,
+// then [slot][chunk] scales), then every wave streams, slot by slot, its rows
+// of the slot's down matrix (two slots in flight; gs is even unless one
+// group holds every slot, so slots pair up the same way in every group) and
+// keeps per lane
+// acc[r] += w_slot * (partial dot product of row r).  When the token changes
+// the 64 lane partials of each row are summed (one wave reduction per row
+// and token) into out -- the weighted sum over the token's slots is formed
+// before the reduction over lanes instead of after it.
+template <int NCHD, int RM>
+__global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(DecodeProblem P, float *__restrict__ out,
+                                                                         int gs) {
+  extern __shared__ uint4 ml[];
+  __shared__ DnTable tab;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int h = P.h, I = P.I, nchd = I >> 5;
+  const int n_slots = P.T * (P.k + P.has_shared);
+  const int64_t W = (int64_t)gridDim.x * kDcWaves, gw = (int64_t)blockIdx.x * kDcWaves + wave;
+  const int r0 = (int)((int64_t)h * gw / W), nr = (int)((int64_t)h * (gw + 1) / W) - r0;
+  float *msc = reinterpret_cast<float *>(ml + (size_t)gs * kPlanes * nchd);
+  const Rsrc rmid = make_rsrc(P.midf, (uint32_t)n_slots * I * 4);
+  float acc[RM];
+#pragma unroll
+  for (int r = 0; r < RM; ++r) acc[r] = 0.0f;
+  DnBuf<NCHD> ba[RM], bb[RM];
+  dn_table(P, tab);
   __syncthreads();
-  for (int i = threadIdx.x; i < T * kDcRows; i += blockDim.x) {
-    const int t = i / kDcRows, r = i % kDcRows;
-    float o = 0.0f;
-    for (int j = 0; j < k; ++j) o = __builtin_fmaf(P.wsel[t * k + j], part[t * k + j][r], o);
-    if (P.has_shared) o += part[T * k + t][r];
-    out[(size_t)t * h + r0 + r] = o;
+  // rows of the first slot in flight before the first group is quantised
+  DnSlot sa = dn_slot(P, tab, 0);
+#pragma unroll
+  for (int r = 0; r < RM; ++r) dn_load(ba[r], sa.q, sa.s, r0 + r, r < nr, I);
+  for (int g0 = 0; g0 < n_slots; g0 += gs) {
+    const int gn = min(gs, n_slots - g0);
+    if (g0 > 0) __syncthreads();  // the previous group's planes are no longer read
+    for (int c = threadIdx.x; c < gn * nchd; c += blockDim.x) {
+      const int sl = c / nchd, lc = c % nchd;
+      const int p = tab.p[g0 + sl];
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 f = bload16(rmid, (uint32_t)(((size_t)p * I + 32 * lc + 4 * i) * 4), 0);
+        v[4 * i + 0] = __uint_as_float(f.x);
+        v[4 * i + 1] = __uint_as_float(f.y);
+        v[4 * i + 2] = __uint_as_float(f.z);
+        v[4 * i + 3] = __uint_as_float(f.w);
+      }
+      uint4 pl[kPlanes];
+      msc[sl * nchd + lc] = quantize_block32(v, pl);
+#pragma unroll
+      for (int j2 = 0; j2 < kPlanes; ++j2) ml[(sl * kPlanes + j2) * nchd + lc] = pl[j2];
+    }
+    __syncthreads();
+    if (nr == 0) continue;  // uniform over the wave; the block barriers are still reached
+    // slots g0 .. g0 + gn - 1, two in flight: ba holds slot qs, bb slot qs + 1
+    for (int qs = g0; qs < g0 + gn; qs += 2) {
+      const bool has_b = qs + 1 < n_slots;
+      DnSlot sb{};
+      if (has_b) sb = dn_slot(P, tab, qs + 1);
+#pragma unroll
+      for (int r = 0; r < RM; ++r) dn_load(bb[r], sb.q, sb.s, r0 + r, has_b && r < nr, I);
+      // consume slot qs (rows in ba)
+      for (int half = 0; half < 2; ++half) {
+        const int qc = qs + half;
+        if (qc >= g0 + gn) break;  // uniform
+        const DnSlot sc = half == 0 ? sa : sb;
+        const int sl = qc - g0;
+#pragma unroll
+        for (int cc = 0; cc < NCHD; ++cc) {
+          const int lc = min(lane + 64 * cc, nchd - 1);  // lanes past the row meet zero weights
+          uint4 xp[kPlanes];
+#pragma unroll
+          for (int j2 = 0; j2 < kPlanes; ++j2) xp[j2] = ml[(sl * kPlanes + j2) * nchd + lc];
+          const float sx = msc[sl * nchd + lc] * sc.w;
+#pragma unroll
+          for (int r = 0; r < RM; ++r) {
+            const DnBuf<NCHD> &bf = half == 0 ? ba[r] : bb[r];
+            acc[r] = __builtin_fmaf((float)dot_planes(bf.w[cc], xp), bf.s[cc] * sx, acc[r]);
+          }
+        }
+        // the token's last slot: reduce and store
+        if (qc + 1 == n_slots || dn_slot_token(P, qc + 1) != sc.t) {
+#pragma unroll
+          for (int r = 0; r < RM; ++r) {
+            if (r < nr) {
+              const float v = wave_sum(acc[r]);
+              if (lane == 0) out[(size_t)sc.t * h + r0 + r] = v;
+            }
+            acc[r] = 0.0f;
+          }
+        }
+        if (half == 0) {
+          // slot qs + 2 into ba
+          const bool has_n = qs + 2 < n_slots;
+          DnSlot sn{};
+          if (has_n) sn = dn_slot(P, tab, qs + 2);
+#pragma unroll
+          for (int r = 0; r < RM; ++r) dn_load(ba[r], sn.q, sn.s, r0 + r, has_n && r < nr, I);
+          sa = sn;
+        }
+      }
+    }
   }
 }
 
@@ -499,32 +803,105 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-bool small_batch(int T, int k) { return T <= kSmallT && T * k <= kSmallAssign; }
+namespace {
+__global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+}  // namespace
+
+hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  return launch(fill_i32_kernel, (n + 255) / 256, 256, 0, s, p, n, v);
+}
+
+bool small_batch(int T, int k, int h, int I) {
+  if (T > kSmallT || T * k > kSmallAssign || I > 64 * 32 * kDcMaxChunks) return false;
+  return T * (kPlanes * 4 * (h >> 3) + 4 * (h >> 5)) <= kSbMaxXLds;
+}
+
+namespace {
+
+template <int NCH, bool XREG>
+hipError_t launch_gu_rows_n(const DecodeProblem &P, hipStream_t s) {
+  const uint32_t lds = XREG ? 0u : (uint32_t)(P.T * (kPlanes * 4 * (P.h >> 3) + 4 * (P.h >> 5)));
+  {
+    static bool attr_set = false;  // LDS above 64 KB must be allowed once per kernel
+    if (!attr_set) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gate_up_rows_kernel<NCH, XREG>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kSbMaxXLds);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+  }
+  return launch(gate_up_rows_kernel<NCH, XREG>, XREG ? kSbBlocks : kSbBlocksLds, XREG ? 256 : 512, lds, s, P);
+}
+
+template <int NCHD, int RM>
+hipError_t launch_dc_rows_n(const DecodeProblem &P, float *out, int blocks, hipStream_t s) {
+  const int nchd = P.I >> 5, per_slot = nchd * (kPlanes * 16 + 4);
+  const int n_slots = P.T * (P.k + P.has_shared);
+  int gs = kDcLds / per_slot;  // >= 2: small batches have I <= 8192
+  if (gs >= n_slots)
+    gs = n_slots;
+  else
+    gs &= ~1;
+  return launch(down_combine_rows_kernel<NCHD, RM>, blocks, kDcWaves * 64, (uint32_t)(gs * per_slot), s, P, out, gs);
+}
+
+template <int NCHD>
+hipError_t launch_dc_rows_r(const DecodeProblem &P, float *out, hipStream_t s) {
+  const int blocks = min(kDcBlocks, (P.h + kDcWaves - 1) / kDcWaves);
+  const int rm = (P.h + blocks * kDcWaves - 1) / (blocks * kDcWaves);  // rows per wave, at most
+  switch (rm) {
+    case 1: return launch_dc_rows_n<NCHD, 1>(P, out, blocks, s);
+    case 2: return launch_dc_rows_n<NCHD, 2>(P, out, blocks, s);
+    case 3: return launch_dc_rows_n<NCHD, 3>(P, out, blocks, s);
+    case 4: return launch_dc_rows_n<NCHD, 4>(P, out, blocks, s);
+    default: return launch_dc_rows_n<NCHD, 8>(P, out, blocks, s);
+  }
+}
+
+}  // namespace
 
 hipError_t launch_gemv_gate_up(const DecodeProblem &P, hipStream_t s) {
+  if (P.T == 0) return hipSuccess;
+  if (small_batch(P.T, P.k, P.h, P.I)) {
+    const int nchl = (P.h + 2047) / 2048;  // 32-column chunks per lane of a row
+    if (P.T == 1 && nchl <= kSbMaxXChunks) {
+      switch (nchl) {
+        case 1: return launch_gu_rows_n<1, true>(P, s);
+        case 2: return launch_gu_rows_n<2, true>(P, s);
+        case 3: return launch_gu_rows_n<3, true>(P, s);
+        default: return launch_gu_rows_n<4, true>(P, s);
+      }
+    }
+    switch (nchl) {
+      case 1: return launch_gu_rows_n<1, false>(P, s);
+      case 2: return launch_gu_rows_n<2, false>(P, s);
+      case 3: return launch_gu_rows_n<3, false>(P, s);
+      case 4: return launch_gu_rows_n<4, false>(P, s);
+      case 5:
+      case 6: return launch_gu_rows_n<6, false>(P, s);
+      default: return launch_gu_rows_n<8, false>(P, s);
+    }
+  }
   const int slots = P.n_routed_slots + (P.has_shared ? 1 : 0);
-  if (slots == 0 || P.T == 0) return hipSuccess;
+  if (slots == 0) return hipSuccess;
   dim3 grid(P.I / (kGuWaves * kGuRows), slots);
   // passes of at most two tokens: wider passes do not fit the register file
-  const bool route = small_batch(P.T, P.k);
-  if (P.T == 1) {
-    if (route)
-      return launch(gate_up_kernel<1, true>, grid, kGuWaves * 64, 0, s, P);
-    else
-      return launch(gate_up_kernel<1, false>, grid, kGuWaves * 64, 0, s, P);
-  } else {
-    if (route)
-      return launch(gate_up_kernel<2, true>, grid, kGuWaves * 64, 0, s, P);
-    else
-      return launch(gate_up_kernel<2, false>, grid, kGuWaves * 64, 0, s, P);
-  }
+  if (P.T == 1) return launch(gate_up_kernel<1>, grid, kGuWaves * 64, 0, s, P);
+  return launch(gate_up_kernel<2>, grid, kGuWaves * 64, 0, s, P);
 }
 
 hipError_t launch_down_combine(const DecodeProblem &P, float *out, hipStream_t s) {
   if (P.T == 0) return hipSuccess;
-  const int n_slots = P.T * P.k + (P.has_shared ? P.T : 0);
-  const int waves = n_slots < 16 ? n_slots : 16;
-  return launch(down_combine_kernel, P.h / kDcRows, waves * 64, 0, s, P, out);
+  switch ((P.I + 2047) / 2048) {
+    case 1: return launch_dc_rows_r<1>(P, out, s);
+    case 2: return launch_dc_rows_r<2>(P, out, s);
+    case 3: return launch_dc_rows_r<3>(P, out, s);
+    default: return launch_dc_rows_r<4>(P, out, s);
+  }
 }
 
 hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s) {

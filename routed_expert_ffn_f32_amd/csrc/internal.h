@@ -37,7 +37,7 @@ constexpr int kMaxExperts = 512;       // dispatch keeps per-wave histograms of 
 constexpr int kMaxTopK = 32;
 constexpr int kDispatchThreads = 1024;
 constexpr int kFusedDispatchMax = 4096;  // T*k up to which selection and dispatch share a launch
-constexpr int kSmallT = 4;               // small batches: routing recomputed inside each expert block
+constexpr int kSmallT = 4;               // small batches: routing computed inside each gate/up block
 constexpr int kSmallAssign = 64;         // and T*k at most one wave of assignments
 
 // ---------------------------------------------------------------------------
@@ -54,7 +54,9 @@ hipError_t launch_router_permute(const float *wr, float *wrP, int h, int E, hipS
 // logits[t][e] = sum_i x[t][i] wr[i][e] in the fixed float32 order: lane l of
 // the wave owning (t, e) keeps p_l = fma(x[l+64m], w[l+64m], p_l) over
 // m = 0..h/64-1, then the 64 partials meet in an xor butterfly (32,16,..,1).
-// The same launch writes the digit-plane form of x (xq, xs) for the experts.
+// The same launch writes the digit-plane form of x (xq, xs) for the experts
+// (xq == NULL: no planes).  One token with h in {2048, 4096, 6144} takes a
+// launch that issues every load of a chain before its first fma.
 hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits,
                                 uint32_t *xq, float *xs, hipStream_t s);  // xq == NULL: no planes
 
@@ -94,7 +96,8 @@ struct DecodeProblem {
   const uint32_t *xq;   // hidden rows as digit planes [T][6][h/8]
   const float *xs;      // and block scales [T][h/32]
   uint32_t *mq;         // expert intermediates as digit planes [P][6][I/8], P = T*k + T*has_shared
-  float *ms;            // and block scales [P][I/32]
+  float *ms;            // and block scales [P][I/32] (larger batches)
+  float *midf;          // expert intermediates as float32 [P][I] (small batches)
   float *y;             // expert outputs [P][h] (larger batches)
   // routing and dispatch: written by the gate/up launch for small batches,
   // read by it otherwise
@@ -102,9 +105,11 @@ struct DecodeProblem {
   float *wsel;
 };
 
-// True when the batch takes the small-batch launch structure (routing inside
-// the gate/up blocks, down fused with the combine).
-bool small_batch(int T, int k);
+// True when the batch takes the small-batch launch structure (router and
+// routing in one launch, gate/up, then down fused with the combine).
+bool small_batch(int T, int k, int h, int I);
+// Fill n int32 values.
+hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
 
 // gate/up: mid = silu(Wg x) * (Wu x) for every assignment position p
 // (routed: p = sorted position; shared: p = T*k + t), written as digit planes.

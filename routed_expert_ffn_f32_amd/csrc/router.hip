@@ -14,6 +14,7 @@
 // the only fused multiply-adds are the explicit __builtin_fmaf calls.
 #include "dispatch_block.h"
 #include "internal.h"
+#include "router_tile.h"
 #include "select.h"
 #include "wave.h"
 
@@ -33,82 +34,6 @@ __global__ __launch_bounds__(256) void router_permute_kernel(const float *__rest
     const int b = (int)(eb % MB), e = (int)(eb / MB);
     const int m = 4 * b + i;
     wrP[o] = m < M ? wr[(size_t)(l + 64 * m) * E + e] : 0.0f;
-  }
-}
-
-// Logits.  One wave computes TPW tokens x EPW experts.  Lane l owns the chain
-// of elements l + 64m, m ascending; the xor butterfly (32, 16, ..., 1) then
-// leaves the full sum in every lane.
-template <int EPW, int TPW>
-__device__ __forceinline__ void logits_tile(const float *__restrict__ x, const float *__restrict__ wrP, int T,
-                                            int h, int E, int t0, int e0, float *__restrict__ logits) {
-  // blocks of 4 chain steps per float4; CH blocks are loaded before any is used
-  constexpr int CH = (EPW * TPW <= 2) ? 8 : 2;
-  const int lane = threadIdx.x & 63;
-  const int M = h >> 6, MB = (M + 3) >> 2, MBfull = M >> 2;
-  const float *xp[TPW];
-  const float4 *wp[EPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) xp[t] = x + (size_t)min(t0 + t, T - 1) * h + lane;
-#pragma unroll
-  for (int e = 0; e < EPW; ++e)
-    wp[e] = reinterpret_cast<const float4 *>(wrP) + ((size_t)min(e0 + e, E - 1) * MB) * 64 + lane;
-  float acc[TPW][EPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int e = 0; e < EPW; ++e) acc[t][e] = 0.0f;
-  int b0 = 0;
-  for (; b0 + CH <= MBfull; b0 += CH) {
-    float4 wv[CH][EPW];
-    float xv[CH][4][TPW];
-#pragma unroll
-    for (int u = 0; u < CH; ++u)
-#pragma unroll
-      for (int e = 0; e < EPW; ++e) wv[u][e] = wp[e][(size_t)(b0 + u) * 64];
-#pragma unroll
-    for (int u = 0; u < CH; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) xv[u][i][t] = xp[t][(4 * (b0 + u) + i) * 64];
-#pragma unroll
-    for (int u = 0; u < CH; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < TPW; ++t)
-#pragma unroll
-          for (int e = 0; e < EPW; ++e) {
-            const float w = i == 0 ? wv[u][e].x : i == 1 ? wv[u][e].y : i == 2 ? wv[u][e].z : wv[u][e].w;
-            acc[t][e] = __builtin_fmaf(xv[u][i][t], w, acc[t][e]);
-          }
-  }
-  // remaining chain steps one at a time, in order
-  for (int m = 4 * b0; m < M; ++m) {
-    const int b = m >> 2, i = m & 3;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const float xv = xp[t][m * 64];
-#pragma unroll
-      for (int e = 0; e < EPW; ++e) {
-        const float *w4 = reinterpret_cast<const float *>(wp[e] + (size_t)b * 64);
-        acc[t][e] = __builtin_fmaf(xv, w4[i], acc[t][e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1)
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int e = 0; e < EPW; ++e) acc[t][e] = acc[t][e] + __shfl_xor(acc[t][e], d);
-  if (lane == 0) {
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int e = 0; e < EPW; ++e)
-        if (t0 + t < T && e0 + e < E) logits[(size_t)(t0 + t) * E + e0 + e] = acc[t][e];
   }
 }
 
@@ -153,13 +78,12 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float *__restr
                                                             const float *__restrict__ bias, int T, int E,
                                                             int k, float rsf, int32_t *__restrict__ idx,
                                                             float *__restrict__ wout) {
-  __shared__ SelectScratch sc[4];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   int e;
   float w;
-  select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w, sc[threadIdx.x >> 6]);
+  select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w);
   if (lane < k) {
     idx[(size_t)t * k + lane] = e;
     wout[(size_t)t * k + lane] = w;
@@ -174,12 +98,11 @@ __global__ __launch_bounds__(kDispatchThreads) void select_dispatch_kernel(
     int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int32_t *__restrict__ active,
     int32_t *__restrict__ n_active) {
   __shared__ int32_t sel[kFusedDispatchMax];
-  __shared__ SelectScratch sc[kDispatchThreads / kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int t = wave; t < T; t += kDispatchThreads / kWave) {
     int e;
     float w;
-    select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w, sc[wave]);
+    select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w);
     if (lane < k) {
       idx[(size_t)t * k + lane] = e;
       wout[(size_t)t * k + lane] = w;
@@ -188,6 +111,56 @@ __global__ __launch_bounds__(kDispatchThreads) void select_dispatch_kernel(
   }
   __syncthreads();
   dispatch_block(sel, T * k, E, offsets, sorted_ids, inv, active, n_active);
+}
+
+// One token: grid = ceil(E / 4) blocks of 4 waves, wave w of block b owns
+// expert 4b + w.  Every load of its chain (MB float4 blocks of the permuted
+// router, the token's h/64 values for this lane) is issued before the first
+// fma, so the launch costs one memory round trip; the arithmetic is
+// logits_tile's, element for element.
+template <int MB>
+__global__ __launch_bounds__(256) void router_logits_t1_kernel(const float *__restrict__ x,
+                                                               const float *__restrict__ wrP, int E,
+                                                               float *__restrict__ logits, int n_logit_blocks,
+                                                               uint32_t *__restrict__ xq, float *__restrict__ xs) {
+  constexpr int M = 4 * MB;  // chain length h / 64
+  const int lane = threadIdx.x & 63;
+  if ((int)blockIdx.x >= n_logit_blocks) {  // the token's digit planes, 256 words per block
+    const int words = M * 8;  // h / 8
+    const int w = (blockIdx.x - n_logit_blocks) * 256 + threadIdx.x;
+    const bool valid = w < words;
+    float v[8];
+    if (valid) {
+      const float4 a = *reinterpret_cast<const float4 *>(x + 8 * w);
+      const float4 b = *reinterpret_cast<const float4 *>(x + 8 * w + 4);
+      v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    quantize_word(v, (w & 3) == 0, valid, xq + (valid ? w : 0), (size_t)words, xs + (valid ? (w >> 2) : 0));
+    return;
+  }
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;  // uniform over the wave
+  const float4 *wp = reinterpret_cast<const float4 *>(wrP) + (size_t)e * MB * 64 + lane;
+  float4 wv[MB];
+  float xv[M];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) wv[b] = wp[(size_t)b * 64];
+#pragma unroll
+  for (int m = 0; m < M; ++m) xv[m] = x[lane + 64 * m];
+  float acc = 0.0f;
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    acc = __builtin_fmaf(xv[4 * b + 0], wv[b].x, acc);
+    acc = __builtin_fmaf(xv[4 * b + 1], wv[b].y, acc);
+    acc = __builtin_fmaf(xv[4 * b + 2], wv[b].z, acc);
+    acc = __builtin_fmaf(xv[4 * b + 3], wv[b].w, acc);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d);
+  if (lane == 0) logits[e] = acc;
 }
 
 }  // namespace
@@ -206,6 +179,12 @@ hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, 
                                 float *xs, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int qblocks = xq ? (int)(((size_t)T * (h >> 3) + 255) / 256) : 0;
+  if (T == 1 && (h == 2048 || h == 4096 || h == 6144)) {
+    const int nlb = (E + 3) / 4;
+    if (h == 2048) return launch(router_logits_t1_kernel<8>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs);
+    if (h == 4096) return launch(router_logits_t1_kernel<16>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs);
+    return launch(router_logits_t1_kernel<24>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs);
+  }
   if (T < 4) {
     const int nlb = T * ((E + 3) / 4);
     return launch(router_logits_kernel<1, 1>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);

@@ -62,120 +62,114 @@ __device__ __forceinline__ uint32_t ordered_bits(float c) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One wave selects the experts of one token (logits row l[0..E)): sigmoid
-// scores, biased keys c = s + b, then the k best under (c desc, e asc), then
-// den = sum of the selected s in slot order and w_j = (s_j / den) * rsf.
-// Lane j < k returns slot j in (e_out, w_out).
-//
-// Top-k by ballots: with the order-preserving integer image u(c), the k-th
-// largest value th is found bit by bit from the top (th grows while at least
-// k keys are >= th | bit), 32 compare + popcount steps on SGPR lane masks.
-// Keys above th are taken, and of the keys equal to th the lowest expert
-// indices fill the remaining places.  The k chosen keys are then ranked among
-// themselves (slot = number of chosen keys that beat it) through LDS.
-template <int R>
-__device__ __forceinline__ void select_token_r(const float *__restrict__ l, const float *__restrict__ bias, int E,
-                                               int k, float rsf, int &e_out, float &w_out, uint32_t *lds_key,
-                                               int32_t *lds_e, float *lds_s) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t lt = (1ull << lane) - 1;
-  float s[R], lv[R], bv[R];
-  uint32_t u[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int e = min(lane + 64 * r, E - 1);
-    lv[r] = l[e];
-    bv[r] = bias ? bias[e] : 0.0f;
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const bool valid = lane + 64 * r < E;
-    s[r] = valid ? sigmoid_spec(lv[r]) : 0.0f;
-    u[r] = valid ? ordered_bits(s[r] + bv[r]) : 0u;  // invalid keys sort below every real key
-  }
-  // threshold: the k-th largest u
-  uint32_t th = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = th | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(u[r] >= cand));
-    if (cnt >= k) th = cand;
-  }
-  // keys above th, then the lowest-index keys equal to th
-  int n_above = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) n_above += __popcll(__ballot(u[r] > th && lane + 64 * r < E));
-  const int need = k - n_above;
-  int eq_before = 0, sel_before = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const bool valid = lane + 64 * r < E;
-    const uint64_t eq = __ballot(valid && u[r] == th);
-    const bool pick_eq = valid && u[r] == th && eq_before + __popcll(eq & lt) < need;
-    const bool pick = (valid && u[r] > th) || pick_eq;
-    const uint64_t sel = __ballot(pick);
-    if (pick) {
-      const int pos = sel_before + __popcll(sel & lt);  // position in expert order
-      lds_key[pos] = u[r];
-      lds_e[pos] = lane + 64 * r;
-      lds_s[pos] = s[r];
-    }
-    eq_before += __popcll(eq);
-    sel_before += __popcll(sel);
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // slot of chosen entry i: how many chosen entries beat it
-  int my_slot = k, my_e = 0;
-  float my_s = 0.0f;
-  if (lane < k) {
-    const uint32_t ku = lds_key[lane];
-    my_e = lds_e[lane];
-    my_s = lds_s[lane];
-    int beat = 0;
-    for (int j = 0; j < k; ++j) {
-      const uint32_t kj = lds_key[j];
-      beat += (kj > ku) || (kj == ku && lds_e[j] < my_e);
-    }
-    my_slot = beat;
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (lane < k) {
-    lds_e[k + my_slot] = my_e;
-    lds_s[k + my_slot] = my_s;
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // den = ((s_0 + s_1) + s_2) + ... in slot order, identical in every lane
-  float den = 0.0f;
-  for (int j = 0; j < k; ++j) den = den + lds_s[k + j];
-  e_out = lane < k ? lds_e[k + lane] : 0;
-  w_out = lane < k ? (lds_s[k + lane] / den) * rsf : 0.0f;
-}
+constexpr int kSelMaxKeys = kMaxExperts / kWave;  // keys per lane
 
-// Per-wave LDS scratch of the selection: keys, experts and scores of the k
-// chosen entries in expert order, then in slot order.
-struct SelectScratch {
-  uint32_t key[kMaxTopK];
-  int32_t e[2 * kMaxTopK];
-  float s[2 * kMaxTopK];
+// The logits and selection biases of one token, lane l holding experts
+// l + 64 i (i < kSelMaxKeys; zeros past E).  Issued early by callers that
+// want the loads in flight while they do other work.
+struct SelectInput {
+  float l[kSelMaxKeys], b[kSelMaxKeys];
 };
 
+__device__ __forceinline__ void select_load(const float *__restrict__ l, const float *__restrict__ bias, int E,
+                                            SelectInput &in) {
+  const int lane = threadIdx.x & 63, nk = (E + 63) >> 6;
+  const Rsrc rl = make_rsrc(l, (uint32_t)E * 4), rb = make_rsrc(bias, bias ? (uint32_t)E * 4 : 0u);
+#pragma unroll
+  for (int i = 0; i < kSelMaxKeys; ++i) {
+    if (i >= nk) break;  // uniform
+    const uint32_t off = (uint32_t)(lane + 64 * i) * 4;
+    in.l[i] = bloadf(rl, off, 0);
+    in.b[i] = bloadf(rb, off, 0);  // no bias: zeros
+  }
+}
+
+// Largest unsigned value over the 64 lanes, returned uniformly.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<kDppQuadXor1>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppQuadXor2>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppRowRor4>((int)v));
+  v = max(v, (uint32_t)dpp_i<kDppRowRor8>((int)v));           // every lane: its row's max
+  v = max(v, (uint32_t)dpp_i<kDppRowBcast15, 0xA>((int)v));   // rows 1, 3 take rows 0, 2
+  v = max(v, (uint32_t)dpp_i<kDppRowBcast31, 0xC>((int)v));   // rows 2, 3 take lane 31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// One wave selects the experts of one token: sigmoid scores s, biased keys
+// c = s + b, then the k best under (c desc, e asc), then den = sum of the
+// selected s in slot order and w_j = (s_j / den) * rsf.  Lane j < k returns
+// slot j in (e_out, w_out).
+//
+// Tournament on the order-preserving integer image u(c): every lane keeps
+// its best remaining key (ties to its lower expert, e = lane + 64 i rises
+// with i), round j takes the largest over the lanes (wave max; ties to the
+// lowest expert among the lanes holding it) and removes it from its lane, so
+// the rounds yield the slots in rank order.  Every real key is >= 0x00800000
+// (the image of -FLT_MAX), removed or invalid keys count as 0.
+__device__ __forceinline__ void select_token_regs(const SelectInput &in, int E, int k, float rsf, int &e_out,
+                                                  float &w_out) {
+  const int lane = threadIdx.x & 63, nk = (E + 63) >> 6;
+  float s[kSelMaxKeys];
+  uint32_t u[kSelMaxKeys];
+#pragma unroll
+  for (int i = 0; i < kSelMaxKeys; ++i) {
+    s[i] = 0.0f;
+    u[i] = 0u;
+    if (i >= nk) continue;  // uniform
+    const bool valid = lane + 64 * i < E;
+    s[i] = valid ? sigmoid_spec(in.l[i]) : 0.0f;
+    u[i] = valid ? ordered_bits(s[i] + in.b[i]) : 0u;
+  }
+  float den = 0.0f, my_s = 0.0f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    uint32_t bu = 0u;
+    int bi = 0;
+    float bs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kSelMaxKeys; ++i)
+      if (i < nk && u[i] > bu) {  // strict: the lower expert of equal keys stays
+        bu = u[i];
+        bi = i;
+        bs = s[i];
+      }
+    const uint32_t m = wave_max_u32(bu);
+    uint64_t cand = __ballot(bu == m);
+    int wl = __builtin_ctzll(cand);
+    int e_win = __builtin_amdgcn_readlane(lane + 64 * bi, wl);
+    if (__popcll(cand) > 1) {  // equal keys on several lanes: the lowest expert wins
+      cand &= cand - 1;
+      while (cand) {
+        const int l2 = __builtin_ctzll(cand);
+        const int e2 = __builtin_amdgcn_readlane(lane + 64 * bi, l2);
+        if (e2 < e_win) {
+          e_win = e2;
+          wl = l2;
+        }
+        cand &= cand - 1;
+      }
+    }
+    const float s_win = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs), wl));
+    den = den + s_win;
+    if (lane == j) {
+      my_e = e_win;
+      my_s = s_win;
+    }
+    if (lane == wl) {
+#pragma unroll
+      for (int i = 0; i < kSelMaxKeys; ++i)
+        if (i == bi) u[i] = 0u;
+    }
+  }
+  e_out = lane < k ? my_e : 0;
+  w_out = lane < k ? (my_s / den) * rsf : 0.0f;
+}
+
 __device__ __forceinline__ void select_token(const float *__restrict__ l, const float *__restrict__ bias, int E,
-                                             int k, float rsf, int &e_out, float &w_out, SelectScratch &sc) {
-  if (E <= 64)
-    select_token_r<1>(l, bias, E, k, rsf, e_out, w_out, sc.key, sc.e, sc.s);
-  else if (E <= 128)
-    select_token_r<2>(l, bias, E, k, rsf, e_out, w_out, sc.key, sc.e, sc.s);
-  else if (E <= 256)
-    select_token_r<4>(l, bias, E, k, rsf, e_out, w_out, sc.key, sc.e, sc.s);
-  else
-    select_token_r<8>(l, bias, E, k, rsf, e_out, w_out, sc.key, sc.e, sc.s);
+                                             int k, float rsf, int &e_out, float &w_out) {
+  SelectInput in;
+  select_load(l, bias, E, in);
+  select_token_regs(in, E, k, rsf, e_out, w_out);
 }
 
 }  // namespace coli
