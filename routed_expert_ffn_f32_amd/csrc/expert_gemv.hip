@@ -391,7 +391,7 @@ __device__ __forceinline__ void gu_consume(const GuBuf<NCH> &b, const GuCursor &
 }
 
 // grid = kSbBlocks (XREG: 4 waves) or kSbBlocksLds (8 waves) blocks.  Dynamic
-// LDS (!XREG): the hidden rows' digit planes [T][6][h/32] uint4, then scales
+// LDS: the hidden rows' digit planes [T][6][h/32] uint4, then scales
 // [T][h/32].
 template <int NCH, bool XREG>
 __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodeProblem P) {
@@ -402,31 +402,29 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   const int h = P.h, I = P.I, T = P.T, nch = h >> 5;
   uint4 xr[XREG ? NCH : 1][kPlanes];
   float xsr[XREG ? NCH : 1];
-  // 1. the routing waves' logits first in the load queue
+  // 1. the selection inputs
   SelectInput sel;
-  if (wave < T) select_load(P.logits + (size_t)wave * P.E, P.bias, P.E, sel);
-  // 2. the hidden rows' digit planes (written by the router launch): token
-  // 0's chunks of this lane into registers, or every token's into LDS
-  if (XREG) {
-    const Rsrc rx = make_rsrc(P.xq, (uint32_t)kPlanes * (h >> 3) * 4);
-    const Rsrc rxs = make_rsrc(P.xs, (uint32_t)nch * 4);
+  route_small_load(P.logits, P.bias, T, P.E, P.k, sel);
+  // 2. the hidden rows' digit planes (written by the router launch), loaded
+  // once per block (a share per thread, no branch) and kept in LDS; with
+  // one token each wave then takes its lanes' chunks into registers
+  const int nx = T * kPlanes * nch, nxs = T * nch;  // uint4 plane chunks, scales
+  const Rsrc rx = make_rsrc(P.xq, (uint32_t)nx * 16), rxs = make_rsrc(P.xs, (uint32_t)nxs * 4);
+  constexpr int kXPer = 5, kXsPer = 2;
+  uint4 xv[kXPer];
+  float xsv[kXsPer];
 #pragma unroll
-    for (int cc = 0; cc < (XREG ? NCH : 1); ++cc) {
-      const uint32_t lc = (uint32_t)(lane + 64 * cc);
-      const bool in = (int)lc < nch;
+  for (int j = 0; j < kXPer; ++j) xv[j] = bload16(rx, (uint32_t)(threadIdx.x + j * blockDim.x) * 16, 0);
 #pragma unroll
-      for (int j = 0; j < kPlanes; ++j) xr[cc][j] = bload16(rx, in ? lc * 16 : 0x7fffffffu, (uint32_t)j * (h >> 3) * 4);
-      xsr[cc] = bloadf(rxs, lc * 4, 0);
-    }
-  } else {
-    const int n = T * kPlanes * nch;
-    const uint4 *src = reinterpret_cast<const uint4 *>(P.xq);
-    for (int i = threadIdx.x; i < n; i += blockDim.x) xl[i] = src[i];
-    float *xsl = reinterpret_cast<float *>(xl + n);
-    for (int i = threadIdx.x; i < T * nch; i += blockDim.x) xsl[i] = P.xs[i];
-  }
-  // 3. this wave's share of the shared expert's rows needs no routing: its
-  // first rows are requested before the routing is known
+  for (int j = 0; j < kXsPer; ++j) xsv[j] = bloadf(rxs, (uint32_t)(threadIdx.x + j * blockDim.x) * 4, 0);
+  // these small loads complete before any row is requested: behind the row
+  // requests in the memory queues their latency grows several-fold, and the
+  // routing, which needs them, is what the block waits for.  The selection
+  // then runs while the shared rows stream.
+  __builtin_amdgcn_s_waitcnt(0);
+  // 3. this wave's share of the shared expert's rows needs no routing; it is
+  // requested once this wave's part of the selection is done (issuing rows
+  // into full memory queues stalls a wave for microseconds)
   const int64_t W = (int64_t)gridDim.x * kWaves, gw = (int64_t)blockIdx.x * kWaves + wave;
   GuSeq q;
   q.a0 = P.has_shared ? (int)((int64_t)I * gw / W) : 0;
@@ -434,17 +432,48 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   constexpr int D = NCH > 4 ? 1 : kSbDepth;  // wide rows: one in flight (register file)
   GuBuf<NCH> buf[D];
   GuCursor pre{};
+  if (P.has_shared) {
+    pre.slot = 0;
+    gu_set_slot(P, R, pre);  // the shared expert: no routing needed
+  }
+  auto shared_prefetch = [&]() {
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    if (d < q.na) {
-      pre.slot = 0;
+    for (int d = 0; d < D; ++d) {
       pre.r = q.a0 + d;
-      gu_set_slot(P, R, pre);  // the shared expert: no routing needed
-      gu_load(buf[d], pre, true, h);
+      gu_load(buf[d], pre, d < q.na, h);
+    }
+  };
+  // the planes into LDS (more than one batch only for several long rows)
+  float *xsl = reinterpret_cast<float *>(xl + nx);
+#pragma unroll
+  for (int j = 0; j < kXPer; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    if (i < nx) xl[i] = xv[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kXsPer; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    if (i < nxs) xsl[i] = xsv[j];
+  }
+  for (int i = threadIdx.x + kXPer * blockDim.x; i < nx; i += blockDim.x) xl[i] = bload16(rx, (uint32_t)i * 16, 0);
+  for (int i = threadIdx.x + kXsPer * blockDim.x; i < nxs; i += blockDim.x) xsl[i] = bloadf(rxs, (uint32_t)i * 4, 0);
+  // 4. the routing of the batch (block barriers inside; they also publish
+  // the planes in LDS): the merging waves (one per token) request their
+  // shared rows after the merge, the others before it
+  route_small_a(sel, T, P.E, P.k, R);
+  if (wave >= T) shared_prefetch();
+  route_small_b(T, P.E, P.k, P.rsf, R);
+  if (wave < T) shared_prefetch();
+  if (XREG) {  // token 0's planes for this lane's chunks (zeros past the row)
+#pragma unroll
+    for (int cc = 0; cc < (XREG ? NCH : 1); ++cc) {
+      const int lc = lane + 64 * cc;
+      const bool in = lc < nch;
+#pragma unroll
+      for (int j = 0; j < kPlanes; ++j) xr[cc][j] = in ? xl[j * nch + lc] : make_uint4(0, 0, 0, 0);
+      xsr[cc] = in ? xsl[lc] : 0.0f;
     }
   }
-  // 4. the routing of the batch (one block barrier inside)
-  route_small(sel, T, P.E, P.k, P.rsf, R);
   if (blockIdx.x == 0) {
     const RoutingOut o{P.idx, P.wsel, P.sorted_ids, P.inv, P.offsets, P.active, P.n_active};
     publish_routing(R, T, P.k, P.E, o);
@@ -454,7 +483,7 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   q.n = q.na + (int)(Nr * (gw + 1) / W) - q.b0;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    if (d >= q.na) {
+    if (d >= q.na) {  // uniform
       const bool v = d < q.n;
       if (v) seq_seek(P, R, q, d, pre);
       gu_load(buf[d], pre, v, h);
@@ -476,37 +505,6 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
       if (ip + 1 < q.n) seq_next(P, R, q, ip, pre);
     }
   }
-}
-
-// Digit planes of 32 consecutive float32 values (a lane-owned block): scale
-// 2^(e - 22) with 2^e > max |v|, N = rint(v / scale), |N| <= 2^22, and the
-// balanced base-16 digits of N read off M = N + 0x888888 (0 <= M < 2^24):
-// digit j is ((M >> 4j) & 15) - 8, whose 4-bit code is ((M >> 4j) & 15) ^ 8.
-__device__ __forceinline__ float quantize_block32(const float (&v)[32], uint4 (&planes)[kPlanes]) {
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(v[i]));
-  int e = 0;
-  (void)__builtin_frexpf(m, &e);
-  e = m > 0.0f ? max(e, kMinExp) : kMinExp;
-  const float to_int = __int_as_float((127 + kMantBits - e) << 23);
-  const float to_real = __int_as_float((127 - kMantBits + e) << 23);
-  uint32_t M[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) M[i] = (uint32_t)((int)__builtin_rintf(v[i] * to_int) + 0x888888);
-#pragma unroll
-  for (int j = 0; j < kPlanes; ++j) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) word |= ((M[8 * q + i] >> (4 * j)) & 15u) << (4 * i);
-      w[q] = word ^ 0x88888888u;
-    }
-    planes[j] = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  return to_real;
 }
 
 template <int NCHD>
@@ -609,32 +607,54 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(Decode
   for (int r = 0; r < RM; ++r) acc[r] = 0.0f;
   DnBuf<NCHD> ba[RM], bb[RM];
   dn_table(P, tab);
-  __syncthreads();
-  // rows of the first slot in flight before the first group is quantised
+  block_barrier();
   DnSlot sa = dn_slot(P, tab, 0);
-#pragma unroll
-  for (int r = 0; r < RM; ++r) dn_load(ba[r], sa.q, sa.s, r0 + r, r < nr, I);
+  const int words = I >> 3;
   for (int g0 = 0; g0 < n_slots; g0 += gs) {
     const int gn = min(gs, n_slots - g0);
-    if (g0 > 0) __syncthreads();  // the previous group's planes are no longer read
-    for (int c = threadIdx.x; c < gn * nchd; c += blockDim.x) {
-      const int sl = c / nchd, lc = c % nchd;
-      const int p = tab.p[g0 + sl];
-      float v[32];
+    if (g0 > 0) block_barrier();  // the previous group's planes are no longer read
+    // the group's intermediate rows as digit planes in LDS, one 8-column word
+    // per thread (the four lanes of a quad share a 32-column block); their
+    // loads go ahead of the first slot's rows, so that the quantisation does
+    // not wait for those
+    uint32_t *mw = reinterpret_cast<uint32_t *>(ml);
+    const int total = gn * words;
+    constexpr int kBatch = 5;
+    for (int base = 0; base < total; base += kBatch * (int)blockDim.x) {
+      // addresses first, then every load without a branch (reads past the
+      // group give zeros), so that the waits for them are counted exactly
+      uint32_t off[kBatch];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint4 f = bload16(rmid, (uint32_t)(((size_t)p * I + 32 * lc + 4 * i) * 4), 0);
-        v[4 * i + 0] = __uint_as_float(f.x);
-        v[4 * i + 1] = __uint_as_float(f.y);
-        v[4 * i + 2] = __uint_as_float(f.z);
-        v[4 * i + 3] = __uint_as_float(f.w);
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
+        const int sl = i / words;
+        off[j] = i < total ? (uint32_t)(((size_t)tab.p[g0 + min(sl, gn - 1)] * I + 8 * (i % words)) * 4)
+                           : 0x7fff0000u;
       }
-      uint4 pl[kPlanes];
-      msc[sl * nchd + lc] = quantize_block32(v, pl);
+      uint4 va[kBatch], vc[kBatch];
 #pragma unroll
-      for (int j2 = 0; j2 < kPlanes; ++j2) ml[(sl * kPlanes + j2) * nchd + lc] = pl[j2];
+      for (int j = 0; j < kBatch; ++j) {
+        va[j] = bload16(rmid, off[j], 0);
+        vc[j] = bload16(rmid, off[j] + 16, 0);
+      }
+      if (g0 == 0 && base == 0) {  // rows of the first slot in flight, after every wave's loads above
+        block_barrier();
+#pragma unroll
+        for (int r = 0; r < RM; ++r) dn_load(ba[r], sa.q, sa.s, r0 + r, r < nr, I);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
+        const bool valid = i < total;
+        const int sl = valid ? i / words : 0, w = valid ? i % words : 0;
+        const float v[8] = {__uint_as_float(va[j].x), __uint_as_float(va[j].y), __uint_as_float(va[j].z),
+                            __uint_as_float(va[j].w), __uint_as_float(vc[j].x), __uint_as_float(vc[j].y),
+                            __uint_as_float(vc[j].z), __uint_as_float(vc[j].w)};
+        quantize_word(v, (w & 3) == 0, valid, mw + (size_t)sl * kPlanes * words + w, (size_t)words,
+                      msc + sl * nchd + (w >> 2));
+      }
     }
-    __syncthreads();
+    block_barrier();
     if (nr == 0) continue;  // uniform over the wave; the block barriers are still reached
     // slots g0 .. g0 + gn - 1, two in flight: ba holds slot qs, bb slot qs + 1
     for (int qs = g0; qs < g0 + gn; qs += 2) {
@@ -824,7 +844,7 @@ namespace {
 
 template <int NCH, bool XREG>
 hipError_t launch_gu_rows_n(const DecodeProblem &P, hipStream_t s) {
-  const uint32_t lds = XREG ? 0u : (uint32_t)(P.T * (kPlanes * 4 * (P.h >> 3) + 4 * (P.h >> 5)));
+  const uint32_t lds = (uint32_t)(P.T * (kPlanes * 4 * (P.h >> 3) + 4 * (P.h >> 5)));
   {
     static bool attr_set = false;  // LDS above 64 KB must be allowed once per kernel
     if (!attr_set) {

@@ -168,10 +168,7 @@ __device__ __forceinline__ void dma_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Barrier without the compiler's memory-model waits (which would also wait
-// for the copies still in flight): this wave's LDS accesses are complete
-// (lgkmcnt 0) and kept on their side of it by the memory clobber.
-__device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

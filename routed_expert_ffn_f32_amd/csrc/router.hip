@@ -143,23 +143,7 @@ __global__ __launch_bounds__(256) void router_logits_t1_kernel(const float *__re
   }
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= E) return;  // uniform over the wave
-  const float4 *wp = reinterpret_cast<const float4 *>(wrP) + (size_t)e * MB * 64 + lane;
-  float4 wv[MB];
-  float xv[M];
-#pragma unroll
-  for (int b = 0; b < MB; ++b) wv[b] = wp[(size_t)b * 64];
-#pragma unroll
-  for (int m = 0; m < M; ++m) xv[m] = x[lane + 64 * m];
-  float acc = 0.0f;
-#pragma unroll
-  for (int b = 0; b < MB; ++b) {
-    acc = __builtin_fmaf(xv[4 * b + 0], wv[b].x, acc);
-    acc = __builtin_fmaf(xv[4 * b + 1], wv[b].y, acc);
-    acc = __builtin_fmaf(xv[4 * b + 2], wv[b].z, acc);
-    acc = __builtin_fmaf(xv[4 * b + 3], wv[b].w, acc);
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d);
+  const float acc = logit_t1<MB>(x, wrP, e);
   if (lane == 0) logits[e] = acc;
 }
 

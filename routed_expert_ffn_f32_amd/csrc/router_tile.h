@@ -121,4 +121,33 @@ __device__ __forceinline__ float logit_chain(const float4 (&wv)[PRE], const floa
   return acc;
 }
 
+// One token, one expert per wave (lane l of the wave owning expert e): every
+// load of the chain (MB float4 blocks of the permuted router, the token's
+// h/64 values for this lane) is issued before the first fma, so the wave
+// costs one memory round trip; the arithmetic is logits_tile's, element for
+// element.  Returns the logit in every lane.
+template <int MB>
+__device__ __forceinline__ float logit_t1(const float *__restrict__ x, const float *__restrict__ wrP, int e) {
+  constexpr int M = 4 * MB;  // chain length h / 64
+  const int lane = threadIdx.x & 63;
+  const float4 *wp = reinterpret_cast<const float4 *>(wrP) + (size_t)e * MB * 64 + lane;
+  float4 wv[MB];
+  float xv[M];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) wv[b] = wp[(size_t)b * 64];
+#pragma unroll
+  for (int m = 0; m < M; ++m) xv[m] = x[lane + 64 * m];
+  float acc = 0.0f;
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    acc = __builtin_fmaf(xv[4 * b + 0], wv[b].x, acc);
+    acc = __builtin_fmaf(xv[4 * b + 1], wv[b].y, acc);
+    acc = __builtin_fmaf(xv[4 * b + 2], wv[b].z, acc);
+    acc = __builtin_fmaf(xv[4 * b + 3], wv[b].w, acc);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d);
+  return acc;
+}
+
 }  // namespace coli

@@ -165,6 +165,156 @@ __device__ __forceinline__ void select_token_regs(const SelectInput &in, int E, 
   w_out = lane < k ? (my_s / den) * rsf : 0.0f;
 }
 
+// ---------------------------------------------------------------------------
+// Selection spread over several waves (small batches, one block).
+//
+// Phase A: wave p of a token's WT waves takes experts [p c, p c + c) (c =
+// ceil(E / WT)), lane l holding expert p c + l + 64 i, finds the k-th largest
+// key by a bitwise search over ballot counts and writes the part's k best
+// under (key desc, expert asc) to LDS in ascending expert order.  The
+// token's k best overall are among these WT k candidates.  Phase B: one wave
+// holds the candidates, one per lane (ascending expert order, so the lowest
+// lane is the lowest expert), takes the k best of them the same way, ranks
+// them into slot order and sums den in slot order.
+// ---------------------------------------------------------------------------
+
+// Phase A inputs: this lane's logits and biases of experts
+// e_lo + lane + 64 i, i < kSelMaxKeys (zeros past ne); loaded early.
+__device__ __forceinline__ void select_part_load(const float *__restrict__ l, const float *__restrict__ bias,
+                                                 int e_lo, int ne, SelectInput &in) {
+  // buffer loads (reads past ne give zeros), only for the keys that exist
+  const int lane = threadIdx.x & 63, nk = (ne + 63) >> 6;
+  const Rsrc rl = make_rsrc(l + e_lo, (uint32_t)ne * 4);
+  const Rsrc rb = make_rsrc(bias ? bias + e_lo : l, bias ? (uint32_t)ne * 4 : 0u);
+#pragma unroll
+  for (int i = 0; i < kSelMaxKeys; ++i) {
+    in.l[i] = in.b[i] = 0.0f;
+    if (i < nk) {  // uniform
+      const uint32_t off = (uint32_t)(lane + 64 * i) * 4;
+      in.l[i] = bloadf(rl, off, 0);
+      in.b[i] = bloadf(rb, off, 0);
+    }
+  }
+}
+
+// The k-th largest of the keys u[] over the wave (NK per lane; absent keys
+// 0): the largest th with #{u >= th} >= k, found bit by bit from the top.
+template <int NK>
+__device__ __forceinline__ uint32_t wave_kth_key(const uint32_t (&u)[NK], int k) {
+  uint32_t th = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = th | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) cnt += __popcll(__ballot(u[i] >= cand));
+    if (cnt >= k) th = cand;
+  }
+  return th;
+}
+
+// Positions, in ascending expert order (key i of lane l is expert
+// l + 64 i), of the k keys that the order (key desc, expert asc) puts first:
+// every key above the k-th largest, then the lowest experts among the keys
+// equal to it.  pos[i] = -1 for keys not taken.
+template <int NK>
+__device__ __forceinline__ void wave_take_k(const uint32_t (&u)[NK], int k, uint32_t th, int (&pos)[NK]) {
+  int n_above = 0;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) n_above += __popcll(__ballot(u[i] > th));
+  const int need = k - n_above;
+  const int below = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));  // lanes under this one
+  const uint64_t lt_mask = below == 0 ? 0ull : (~0ull >> (64 - below));
+  int eq_before = 0, taken_before = 0;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const uint64_t eq = __ballot(u[i] == th);
+    const bool take = u[i] > th || (u[i] == th && eq_before + __popcll(eq & lt_mask) < need);
+    const uint64_t tk = __ballot(take);
+    pos[i] = take ? taken_before + __popcll(tk & lt_mask) : -1;
+    eq_before += __popcll(eq);
+    taken_before += __popcll(tk);
+  }
+}
+
+// Phase A for experts [e_lo, e_lo + ne) of one token (inputs from
+// select_part_load): the part's k best, in ascending expert order, into
+// cu/ce/cs[0..k) (key image, expert, score).
+template <int NK>
+__device__ __forceinline__ void select_part(const SelectInput &in, int e_lo, int ne, int k, uint32_t *cu, int32_t *ce,
+                                            float *cs) {
+  const int lane = threadIdx.x & 63;
+  uint32_t u[NK];
+  float s[NK];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const bool valid = lane + 64 * i < ne;
+    s[i] = valid ? sigmoid_spec(in.l[i]) : 0.0f;
+    u[i] = valid ? ordered_bits(s[i] + in.b[i]) : 0u;
+  }
+  const uint32_t th = wave_kth_key<NK>(u, k);
+  int pos[NK];
+  wave_take_k<NK>(u, k, th, pos);
+#pragma unroll
+  for (int i = 0; i < NK; ++i)
+    if (pos[i] >= 0) {
+      cu[pos[i]] = u[i];
+      ce[pos[i]] = e_lo + lane + 64 * i;
+      cs[pos[i]] = s[i];
+    }
+}
+
+// LDS writes of this wave done and ordered before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Phase B: n <= 64 candidates (cu, ce, cs in LDS, ascending expert order)
+// -> slot j (j < k) of the token in se[j], sw[j] = (s_j / den) * rsf with
+// den = ((s_0 + s_1) + s_2) + ... in slot order, and slot_of[p] = the slot
+// of the p-th selected expert in ascending expert order.  One wave: lane c
+// holds candidate c and counts the candidates the order (key desc, expert
+// asc) puts before it -- its slot when that count is below k (equal keys:
+// the lower lane is the lower expert).  `scratch` holds kMaxTopK words of
+// LDS.
+__device__ __forceinline__ void select_merge(const uint32_t *cu, const int32_t *ce, const float *cs, int n, int k,
+                                             float rsf, int32_t *se, float *sw, uint32_t *scratch,
+                                             int32_t *slot_of) {
+  const int lane = threadIdx.x & 63;
+  const bool valid = lane < n;
+  const uint32_t u = valid ? cu[lane] : 0u;
+  const int e = valid ? ce[lane] : 0;
+  const float sv = valid ? cs[lane] : 0.0f;
+  // every lane reads the candidate keys from LDS (same addresses in all
+  // lanes: broadcasts), four at a time
+  int rank = 0;
+  const uint4 *cu4 = reinterpret_cast<const uint4 *>(cu);
+  for (int j4 = 0; j4 < n; j4 += 4) {
+    const uint4 q = cu4[j4 >> 2];
+    const uint32_t uj[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j4 + i;
+      rank += j < n && (uj[i] > u || (uj[i] == u && j < lane));
+    }
+  }
+  const bool win = valid && rank < k;
+  const uint64_t wins = __ballot(win);
+  const int below = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const uint64_t lt_mask = below == 0 ? 0ull : (~0ull >> (64 - below));
+  float *ss = reinterpret_cast<float *>(scratch);  // scores in slot order
+  if (win) {
+    se[rank] = e;
+    ss[rank] = sv;
+    slot_of[__popcll(wins & lt_mask)] = rank;
+  }
+  wave_lds_sync();
+  float den = 0.0f;
+  for (int j = 0; j < k; ++j) den = den + ss[j];
+  if (win) sw[rank] = (sv / den) * rsf;
+}
+
 __device__ __forceinline__ void select_token(const float *__restrict__ l, const float *__restrict__ bias, int E,
                                              int k, float rsf, int &e_out, float &w_out) {
   SelectInput in;

@@ -21,26 +21,96 @@ struct SmallRouting {
   int32_t active[kSmallAssign];
   int32_t seg_begin[kSmallAssign + 1];
   int32_t n_active;
+  // selection candidates per token: key image, expert, score; merge scratch
+  alignas(16) uint32_t cu[kSmallT][64];
+  int32_t ce[kSmallT][64];
+  float cs[kSmallT][64];
+  uint32_t scratch[kSmallT][kMaxTopK];
+  int32_t slot_of[kSmallT][kMaxTopK];
 };
 
-// Waves 0..T-1 select one token each (their logits already loaded into
-// `in`); wave 0 then sorts the n = T*k assignments by expert, stably
-// (position = smaller keys + equal keys of lower a), and lists the segments
-// (an assignment with no equal key before it starts one).  Ends with the
-// block synchronised.
-__device__ __forceinline__ void route_small(const SelectInput &in, int T, int E, int k, float rsf,
-                                            SmallRouting &R) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave < T) {
-    int e;
-    float w;
-    select_token_regs(in, E, k, rsf, e, w);
-    if (lane < k) {
-      R.idx[wave * k + lane] = e;
-      R.w[wave * k + lane] = w;
-    }
+// How the block's waves share the selection: each token gets WT = waves / T
+// waves (WT * k <= 64), wave w working on token w / WT, part w % WT of the
+// experts (a chunk of ceil(E / WT)).
+struct SmallSelectPlan {
+  int wt, chunk, t, part, e_lo, ne;
+};
+
+__device__ __forceinline__ SmallSelectPlan small_select_plan(int T, int E, int k) {
+  const int wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  SmallSelectPlan p;
+  p.wt = waves / T;
+  if (p.wt * k > 64) p.wt = max(1, 64 / k);
+  p.chunk = (E + p.wt - 1) / p.wt;
+  p.t = wave / p.wt;
+  p.part = wave % p.wt;
+  p.e_lo = p.part * p.chunk;
+  p.ne = p.t < T ? max(0, min(p.chunk, E - p.e_lo)) : 0;
+  return p;
+}
+
+// This wave's selection inputs (issue before other loads: the routing is the
+// first thing the block waits for).
+__device__ __forceinline__ void route_small_load(const float *__restrict__ logits, const float *__restrict__ bias,
+                                                 int T, int E, int k, SelectInput &in) {
+  const SmallSelectPlan p = small_select_plan(T, E, k);
+  select_part_load(logits + (size_t)min(p.t, T - 1) * E, bias, p.e_lo, p.ne, in);
+}
+
+// Routing of the batch by the whole block (waves >= T), from the inputs of
+// route_small_load, in two calls: route_small_a (phase A over E / WT experts
+// per wave, candidates into LDS, block barrier), then route_small_b (phase B
+// by wave t for token t, select.h, then the sort).  A part's k best contain
+// every expert of the token's k best that falls in the part, so phase B sees
+// all of them.  Wave 0 then sorts the
+// n = T*k assignments by expert, stably (position = smaller keys + equal keys
+// of lower a), and lists the segments (an assignment with no equal key before
+// it starts one).  Ends with the block synchronised for LDS (global loads in
+// flight are not waited for).
+__device__ __forceinline__ void route_small_a(const SelectInput &in, int T, int E, int k, SmallRouting &R) {
+  const SmallSelectPlan p = small_select_plan(T, E, k);
+  if (p.t < T) {
+    uint32_t *cu = R.cu[p.t] + p.part * k;
+    int32_t *ce = R.ce[p.t] + p.part * k;
+    float *cs = R.cs[p.t] + p.part * k;
+    const int nk = (p.ne + 63) >> 6;
+    if (nk <= 1)
+      select_part<1>(in, p.e_lo, p.ne, k, cu, ce, cs);
+    else if (nk <= 2)
+      select_part<2>(in, p.e_lo, p.ne, k, cu, ce, cs);
+    else if (nk <= 4)
+      select_part<4>(in, p.e_lo, p.ne, k, cu, ce, cs);
+    else
+      select_part<8>(in, p.e_lo, p.ne, k, cu, ce, cs);
   }
-  __syncthreads();
+  block_barrier();
+}
+
+// Phase B and the sort (after route_small_a).
+__device__ __forceinline__ void route_small_b(int T, int E, int k, float rsf, SmallRouting &R) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wt = small_select_plan(T, E, k).wt;
+  if (wave < T)
+    select_merge(R.cu[wave], R.ce[wave], R.cs[wave], wt * k, k, rsf, R.idx + wave * k, R.w + wave * k,
+                 R.scratch[wave], R.slot_of[wave]);
+  if (T == 1) {
+    // one token: the merge gives the experts in ascending order already, and
+    // every expert has exactly one assignment
+    if (wave == 0 && lane < k) {
+      const int sl = R.slot_of[0][lane];
+      R.sorted_ids[lane] = sl;
+      R.inv[sl] = lane;
+      R.active[lane] = R.idx[sl];
+      R.seg_begin[lane] = lane;
+      if (lane == 0) {
+        R.n_active = k;
+        R.seg_begin[k] = k;
+      }
+    }
+    block_barrier();
+    return;
+  }
+  block_barrier();
   const int n = T * k;
   if (wave == 0) {
     const bool valid = lane < n;
@@ -69,7 +139,7 @@ __device__ __forceinline__ void route_small(const SelectInput &in, int T, int E,
       R.seg_begin[__popcll(starts)] = n;
     }
   }
-  __syncthreads();
+  block_barrier();
 }
 
 // Where the routing of a call goes (device arrays of the C ABI's layout).

@@ -47,6 +47,15 @@ __device__ __forceinline__ float bloadf(Rsrc r, uint32_t voff, uint32_t soff) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Block barrier for LDS data only: this wave's LDS accesses are complete
+// (lgkmcnt 0) and kept on their side of it by the memory clobber, but global
+// loads still in flight (prefetched rows) are not waited for, as
+// __syncthreads() would.  Global memory written before it is not published.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+#pragma clang diagnostic pop
+
 // Sum of v over the 64 lanes, returned uniformly (fixed combining order, so
 // the result is the same on every run).
 __device__ __forceinline__ float wave_sum(float v) {
