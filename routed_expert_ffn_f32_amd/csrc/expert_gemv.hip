@@ -243,6 +243,9 @@ __global__ __launch_bounds__(kGuWaves * 64, COLI_GU_MIN_WAVES) void gate_up_kern
 #ifndef COLI_DC_WAVES
 #define COLI_DC_WAVES 8
 #endif
+#ifndef COLI_DC_RING
+#define COLI_DC_RING 2
+#endif
 #ifndef COLI_DC_BLOCKS
 #define COLI_DC_BLOCKS 256
 #endif
@@ -255,6 +258,7 @@ constexpr int kDcLds = 64 * 1024;           // down: LDS for the digit planes of
 constexpr int kSbMaxXChunks = 4;            // T = 1 keeps the planes of h <= 64*32*4 columns in registers
 constexpr int kSbMaxXLds = 96 * 1024;       // bytes of hidden-row planes staged in LDS
 constexpr int kDcMaxChunks = 4;             // down: I <= 64*32*4
+constexpr int kDcMaxRing = COLI_DC_RING;    // down: slots in flight per wave, at most
 
 // Where the gate/up rows of a slot come from, and its assignment positions.
 struct GuCursor {
@@ -526,14 +530,17 @@ __device__ __forceinline__ void dn_load(DnBuf<NCHD> &b, const uint8_t *q, const 
   for (int cc = 0; cc < NCHD; ++cc) b.s[cc] = bloadf(rs, (uint32_t)((lane + 64 * cc) >> 1) * 4, 0);
 }
 
-// Slot q of the down sequence: tokens in order, each token's k routed
-// assignments in slot order and then its shared-expert slot.  The block
-// reads the routing once into LDS (expert, or -1 for the shared expert;
-// position of the intermediate row; combine weight).
+// Slot q of the down sequence: tokens in order; for each token its
+// shared-expert slot first (those rows need no routing, so they can be
+// requested before the routing has arrived), then its k routed assignments
+// in slot order.  The block keeps the routing of every slot in LDS: expert
+// (-1 for the shared expert), position of the intermediate row, combine
+// weight; one entry per thread of the block (entries past the last slot are
+// written and never read).
 struct DnTable {
-  int32_t e[kSmallAssign + kSmallT];
-  int32_t p[kSmallAssign + kSmallT];
-  float w[kSmallAssign + kSmallT];
+  int32_t e[kDcWaves * 64];
+  int32_t p[kDcWaves * 64];
+  float w[kDcWaves * 64];
 };
 
 struct DnSlot {
@@ -543,21 +550,32 @@ struct DnSlot {
   float w;
 };
 
-__device__ __forceinline__ void dn_table(const DecodeProblem &P, DnTable &D) {
-  const int ks = P.k + P.has_shared, n_slots = P.T * ks;
-  for (int qs = threadIdx.x; qs < n_slots; qs += blockDim.x) {
-    const int t = qs / ks, j = qs % ks;
-    if (j < P.k) {
-      const int a = t * P.k + j;
-      D.e[qs] = P.idx[a];
-      D.p[qs] = P.inv[a];
-      D.w[qs] = P.wsel[a];
-    } else {
-      D.e[qs] = -1;
-      D.p[qs] = P.T * P.k + t;
-      D.w[qs] = 1.0f;
-    }
-  }
+// Thread q reads the routing of slot q (every slot has a thread: the block
+// is larger than kSmallAssign + kSmallT); buffer loads without a branch,
+// absent entries read zeros.
+__device__ __forceinline__ void dn_table_load(const DecodeProblem &P, uint32_t (&v)[3]) {
+  const int ks = P.k + P.has_shared, n_slots = P.T * ks, n_routed = P.T * P.k;
+  const int qs = threadIdx.x, t = qs / ks, j = qs % ks - P.has_shared;
+  const uint32_t off = qs < n_slots && j >= 0 ? (uint32_t)(t * P.k + j) * 4 : 0x7fff0000u;
+  const uint32_t bytes = (uint32_t)n_routed * 4;
+  v[0] = __float_as_uint(bloadf(make_rsrc(P.idx, bytes), off, 0));
+  v[1] = __float_as_uint(bloadf(make_rsrc(P.inv, bytes), off, 0));
+  v[2] = __float_as_uint(bloadf(make_rsrc(P.wsel, bytes), off, 0));
+}
+
+// Stores without a branch: a store under a branch would let the compiler
+// sink the loads behind the rows requested after them.
+__device__ __forceinline__ void dn_table_store(const DecodeProblem &P, const uint32_t (&v)[3], DnTable &D) {
+  const int ks = P.k + P.has_shared;
+  const int qs = threadIdx.x, t = qs / ks, j = qs % ks - P.has_shared;
+  const bool routed = j >= 0;
+  D.e[qs] = routed ? (int)v[0] : -1;
+  D.p[qs] = routed ? (int)v[1] : P.T * P.k + t;
+  D.w[qs] = routed ? __uint_as_float(v[2]) : 1.0f;
+}
+
+__device__ __forceinline__ DnSlot dn_shared_slot(const DecodeProblem &P, int t) {
+  return DnSlot{P.sh_down.q, P.sh_down.s, t, 1.0f};
 }
 
 __device__ __forceinline__ DnSlot dn_slot(const DecodeProblem &P, const DnTable &D, int qs) {
@@ -577,98 +595,167 @@ __device__ __forceinline__ DnSlot dn_slot(const DecodeProblem &P, const DnTable 
 
 __device__ __forceinline__ int dn_slot_token(const DecodeProblem &P, int qs) { return qs / (P.k + P.has_shared); }
 
+// Slots in flight per wave in the down kernel: kDcMaxRing (two by default;
+// deeper rings delay the reads of the intermediate rows, which every block
+// waits for, more than they gain), fewer if the row buffers would pass about
+// 96 VGPRs (5 per row and 32-column chunk), never below two.
+template <int NCHD, int RM>
+constexpr int dc_ring() {
+  constexpr int n = 96 / (5 * NCHD * RM);
+  return n < 2 ? 2 : n > kDcMaxRing ? kDcMaxRing : n;
+}
+
 // Down projection fused with the weighted combine, small batches.
 // grid = Gd blocks of kDcWaves waves; wave w of the grid owns output rows
-// [w h / W, (w + 1) h / W) (at most RM).  The slots are taken in groups of
-// gs: the block first writes the digit planes of the group's intermediate
-// rows into LDS (one thread per 32-column block: [slot][plane][chunk] uint4,
-// then [slot][chunk] scales), then every wave streams, slot by slot, its rows
-// of the slot's down matrix (two slots in flight; gs is even unless one
-// group holds every slot, so slots pair up the same way in every group) and
-// keeps per lane
-// acc[r] += w_slot * (partial dot product of row r).  When the token changes
-// the 64 lane partials of each row are summed (one wave reduction per row
-// and token) into out -- the weighted sum over the token's slots is formed
-// before the reduction over lanes instead of after it.
-template <int NCHD, int RM>
+// [w h / W, (w + 1) h / W) (at most RM).  The intermediate rows are first
+// written into LDS as digit planes (one thread per 8-column word, the four
+// lanes of a quad sharing a 32-column block: [row][plane][chunk] uint4, then
+// [row][chunk] scales); then every wave streams, slot by slot, its rows of
+// the slot's down matrix, NS slots in flight (a ring of register buffers:
+// buffer u holds slot base + u), and keeps per lane
+// acc[r] += w_slot * (partial dot product of row r).  When the token
+// changes the 64 lane partials of each row are summed (one wave reduction
+// per row and token) into out: the weighted sum over the token's slots is
+// formed before the reduction over lanes instead of after it.
+//
+// The ring's first slots are requested before the intermediate rows have
+// arrived (their reads take microseconds: every block reads all of them),
+// so HBM streams weights during the wait.  BYPOS: every intermediate row
+// fits in LDS at once and is kept there by position (they are n_slots
+// consecutive rows, so their loads need no routing and go out with it);
+// otherwise the slots are taken in groups of gs, kept by slot, the next
+// group quantised when the ring reaches it.  No load is issued under a
+// branch that depends on the data, so the compiler's waits count exactly
+// the loads issued after the ones awaited.
+template <int NCHD, int RM, bool BYPOS>
 __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(DecodeProblem P, float *__restrict__ out,
                                                                          int gs) {
+  static_assert(kDcWaves * 64 >= kSmallAssign + kSmallT, "one thread per slot of the routing table");
+  constexpr int NS = dc_ring<NCHD, RM>();
   extern __shared__ uint4 ml[];
   __shared__ DnTable tab;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int h = P.h, I = P.I, nchd = I >> 5;
+  const int h = P.h, I = P.I, nchd = I >> 5, words = I >> 3;
   const int n_slots = P.T * (P.k + P.has_shared);
   const int64_t W = (int64_t)gridDim.x * kDcWaves, gw = (int64_t)blockIdx.x * kDcWaves + wave;
   const int r0 = (int)((int64_t)h * gw / W), nr = (int)((int64_t)h * (gw + 1) / W) - r0;
   float *msc = reinterpret_cast<float *>(ml + (size_t)gs * kPlanes * nchd);
+  uint32_t *mw = reinterpret_cast<uint32_t *>(ml);
   const Rsrc rmid = make_rsrc(P.midf, (uint32_t)n_slots * I * 4);
+  constexpr int kBatch = 5;  // 8-column words per thread and batch
+  const int batch = kBatch * (int)blockDim.x;
   float acc[RM];
 #pragma unroll
   for (int r = 0; r < RM; ++r) acc[r] = 0.0f;
-  DnBuf<NCHD> ba[RM], bb[RM];
-  dn_table(P, tab);
-  block_barrier();
-  DnSlot sa = dn_slot(P, tab, 0);
-  const int words = I >> 3;
-  for (int g0 = 0; g0 < n_slots; g0 += gs) {
-    const int gn = min(gs, n_slots - g0);
-    if (g0 > 0) block_barrier();  // the previous group's planes are no longer read
-    // the group's intermediate rows as digit planes in LDS, one 8-column word
-    // per thread (the four lanes of a quad share a 32-column block); their
-    // loads go ahead of the first slot's rows, so that the quantisation does
-    // not wait for those
-    uint32_t *mw = reinterpret_cast<uint32_t *>(ml);
+  DnBuf<NCHD> buf[NS][RM];
+  DnSlot ring[NS];
+
+  // byte offsets of the batch's words in midf (past the group: an offset
+  // that reads zeros); BYPOS: consecutive, else through the slots' positions
+  auto mid_offsets = [&](int g0, int gn, int base, uint32_t (&off)[kBatch]) {
     const int total = gn * words;
-    constexpr int kBatch = 5;
-    for (int base = 0; base < total; base += kBatch * (int)blockDim.x) {
-      // addresses first, then every load without a branch (reads past the
-      // group give zeros), so that the waits for them are counted exactly
-      uint32_t off[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
-        const int sl = i / words;
-        off[j] = i < total ? (uint32_t)(((size_t)tab.p[g0 + min(sl, gn - 1)] * I + 8 * (i % words)) * 4)
-                           : 0x7fff0000u;
-      }
-      uint4 va[kBatch], vc[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        va[j] = bload16(rmid, off[j], 0);
-        vc[j] = bload16(rmid, off[j] + 16, 0);
-      }
-      if (g0 == 0 && base == 0) {  // rows of the first slot in flight, after every wave's loads above
-        block_barrier();
-#pragma unroll
-        for (int r = 0; r < RM; ++r) dn_load(ba[r], sa.q, sa.s, r0 + r, r < nr, I);
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
-        const bool valid = i < total;
-        const int sl = valid ? i / words : 0, w = valid ? i % words : 0;
-        const float v[8] = {__uint_as_float(va[j].x), __uint_as_float(va[j].y), __uint_as_float(va[j].z),
-                            __uint_as_float(va[j].w), __uint_as_float(vc[j].x), __uint_as_float(vc[j].y),
-                            __uint_as_float(vc[j].z), __uint_as_float(vc[j].w)};
-        quantize_word(v, (w & 3) == 0, valid, mw + (size_t)sl * kPlanes * words + w, (size_t)words,
-                      msc + sl * nchd + (w >> 2));
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
+      if (BYPOS) {
+        off[j] = i < total ? (uint32_t)i * 32 : 0x7fff0000u;
+      } else {
+        const int sl = min(i / words, gn - 1);
+        off[j] = i < total ? (uint32_t)(((size_t)tab.p[g0 + sl] * I + 8 * (i % words)) * 4) : 0x7fff0000u;
       }
     }
-    block_barrier();
-    if (nr == 0) continue;  // uniform over the wave; the block barriers are still reached
-    // slots g0 .. g0 + gn - 1, two in flight: ba holds slot qs, bb slot qs + 1
-    for (int qs = g0; qs < g0 + gn; qs += 2) {
-      const bool has_b = qs + 1 < n_slots;
-      DnSlot sb{};
-      if (has_b) sb = dn_slot(P, tab, qs + 1);
+  };
+  auto mid_load = [&](const uint32_t (&off)[kBatch], uint4 (&va)[kBatch], uint4 (&vc)[kBatch]) {
 #pragma unroll
-      for (int r = 0; r < RM; ++r) dn_load(bb[r], sb.q, sb.s, r0 + r, has_b && r < nr, I);
-      // consume slot qs (rows in ba)
-      for (int half = 0; half < 2; ++half) {
-        const int qc = qs + half;
-        if (qc >= g0 + gn) break;  // uniform
-        const DnSlot sc = half == 0 ? sa : sb;
-        const int sl = qc - g0;
+    for (int j = 0; j < kBatch; ++j) {
+      va[j] = bload16(rmid, off[j], 0);
+      vc[j] = bload16(rmid, off[j] + 16, 0);
+    }
+  };
+  auto quantize = [&](int gn, int base, const uint4 (&va)[kBatch], const uint4 (&vc)[kBatch]) {
+    const int total = gn * words;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + j * (int)blockDim.x + (int)threadIdx.x;
+      const bool valid = i < total;
+      const int sl = valid ? i / words : 0, w = valid ? i % words : 0;
+      const float v[8] = {__uint_as_float(va[j].x), __uint_as_float(va[j].y), __uint_as_float(va[j].z),
+                          __uint_as_float(va[j].w), __uint_as_float(vc[j].x), __uint_as_float(vc[j].y),
+                          __uint_as_float(vc[j].z), __uint_as_float(vc[j].w)};
+      quantize_word(v, (w & 3) == 0, valid, mw + (size_t)sl * kPlanes * words + w, (size_t)words,
+                    msc + sl * nchd + (w >> 2));
+    }
+  };
+  // the rest of a group's words, one batch at a time (several batches only
+  // for long intermediate rows or several groups)
+  auto quantize_rest = [&](int g0, int gn, int base0) {
+    for (int base = base0; base < gn * words; base += batch) {
+      uint32_t off[kBatch];
+      uint4 va[kBatch], vc[kBatch];
+      mid_offsets(g0, gn, base, off);
+      mid_load(off, va, vc);
+      quantize(gn, base, va, vc);
+    }
+  };
+  // slot qs (past the last: no rows) into ring buffer u
+  auto ring_load = [&](int u, int qs) {
+    const bool v = qs < n_slots;
+    ring[u] = v ? dn_slot(P, tab, qs) : DnSlot{};
+#pragma unroll
+    for (int r = 0; r < RM; ++r) dn_load(buf[u][r], ring[u].q, ring[u].s, r0 + r, v && r < nr, I);
+  };
+
+  // prologue: the routing table and the first batch of intermediate words,
+  // then the ring's rows; the quantisation waits for the words only
+  {
+    const int gn = min(gs, n_slots);
+    uint32_t tv[3];
+    dn_table_load(P, tv);
+    uint32_t off[kBatch];
+    uint4 va[kBatch], vc[kBatch];
+    if (BYPOS) {
+      mid_offsets(0, gn, 0, off);
+      mid_load(off, va, vc);
+      // every wave's words requested before any row: a row request ahead
+      // of them in the memory pipeline would hold them for an HBM latency
+      block_barrier();
+      // a shared expert's first slot needs no routing: its rows go out now
+      ring[0] = dn_shared_slot(P, 0);
+#pragma unroll
+      for (int r = 0; r < RM; ++r) dn_load(buf[0][r], ring[0].q, ring[0].s, r0 + r, P.has_shared && r < nr, I);
+    }
+    dn_table_store(P, tv, tab);
+    block_barrier();
+    if (!BYPOS) {
+      mid_offsets(0, gn, 0, off);
+      mid_load(off, va, vc);
+    }
+    if (!BYPOS || !P.has_shared) ring_load(0, 0);
+#pragma unroll
+    for (int u = 1; u < NS; ++u) ring_load(u, u);
+    quantize(gn, 0, va, vc);
+    quantize_rest(0, gn, batch);
+    block_barrier();
+  }
+
+  for (int base = 0; base < n_slots; base += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int qc = base + u;
+      int sl = 0;
+      if (BYPOS) {
+        sl = qc < n_slots ? uniform(tab.p[qc]) : 0;
+      } else {
+        const int g0 = qc - qc % gs;
+        if (qc < n_slots && qc == g0 && qc > 0) {  // uniform over the block: the next group's planes
+          block_barrier();                          // the previous group's are no longer read
+          quantize_rest(g0, min(gs, n_slots - g0), 0);
+          block_barrier();
+        }
+        sl = qc - g0;
+      }
+      if (qc < n_slots) {
+        const DnSlot &sc = ring[u];
 #pragma unroll
         for (int cc = 0; cc < NCHD; ++cc) {
           const int lc = min(lane + 64 * cc, nchd - 1);  // lanes past the row meet zero weights
@@ -677,10 +764,8 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(Decode
           for (int j2 = 0; j2 < kPlanes; ++j2) xp[j2] = ml[(sl * kPlanes + j2) * nchd + lc];
           const float sx = msc[sl * nchd + lc] * sc.w;
 #pragma unroll
-          for (int r = 0; r < RM; ++r) {
-            const DnBuf<NCHD> &bf = half == 0 ? ba[r] : bb[r];
-            acc[r] = __builtin_fmaf((float)dot_planes(bf.w[cc], xp), bf.s[cc] * sx, acc[r]);
-          }
+          for (int r = 0; r < RM; ++r)
+            acc[r] = __builtin_fmaf((float)dot_planes(buf[u][r].w[cc], xp), buf[u][r].s[cc] * sx, acc[r]);
         }
         // the token's last slot: reduce and store
         if (qc + 1 == n_slots || dn_slot_token(P, qc + 1) != sc.t) {
@@ -693,16 +778,8 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(Decode
             acc[r] = 0.0f;
           }
         }
-        if (half == 0) {
-          // slot qs + 2 into ba
-          const bool has_n = qs + 2 < n_slots;
-          DnSlot sn{};
-          if (has_n) sn = dn_slot(P, tab, qs + 2);
-#pragma unroll
-          for (int r = 0; r < RM; ++r) dn_load(ba[r], sn.q, sn.s, r0 + r, has_n && r < nr, I);
-          sa = sn;
-        }
       }
+      ring_load(u, qc + NS);
     }
   }
 }
@@ -861,12 +938,12 @@ template <int NCHD, int RM>
 hipError_t launch_dc_rows_n(const DecodeProblem &P, float *out, int blocks, hipStream_t s) {
   const int nchd = P.I >> 5, per_slot = nchd * (kPlanes * 16 + 4);
   const int n_slots = P.T * (P.k + P.has_shared);
-  int gs = kDcLds / per_slot;  // >= 2: small batches have I <= 8192
+  const int gs = kDcLds / per_slot;  // >= 2: small batches have I <= 8192
   if (gs >= n_slots)
-    gs = n_slots;
-  else
-    gs &= ~1;
-  return launch(down_combine_rows_kernel<NCHD, RM>, blocks, kDcWaves * 64, (uint32_t)(gs * per_slot), s, P, out, gs);
+    return launch(down_combine_rows_kernel<NCHD, RM, true>, blocks, kDcWaves * 64, (uint32_t)(n_slots * per_slot), s,
+                  P, out, n_slots);
+  return launch(down_combine_rows_kernel<NCHD, RM, false>, blocks, kDcWaves * 64, (uint32_t)(gs * per_slot), s, P,
+                out, gs);
 }
 
 template <int NCHD>

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float *__restr
                                                             int k, float rsf, int32_t *__restrict__ idx,
                                                             float *__restrict__ wout) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x * 4 + uniform(threadIdx.x >> 6);  // scalar: the loads' buffer resources
   if (t >= T) return;
   int e;
   float w;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kDispatchThreads) void select_dispatch_kernel(
     int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int32_t *__restrict__ active,
     int32_t *__restrict__ n_active) {
   __shared__ int32_t sel[kFusedDispatchMax];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   for (int t = wave; t < T; t += kDispatchThreads / kWave) {
     int e;
     float w;

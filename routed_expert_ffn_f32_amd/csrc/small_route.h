@@ -37,7 +37,9 @@ struct SmallSelectPlan {
 };
 
 __device__ __forceinline__ SmallSelectPlan small_select_plan(int T, int E, int k) {
-  const int wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  // the wave index as a scalar: the buffer resources built from the plan
+  // must be wave-uniform values
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), waves = blockDim.x >> 6;
   SmallSelectPlan p;
   p.wt = waves / T;
   if (p.wt * k > 64) p.wt = max(1, 64 / k);

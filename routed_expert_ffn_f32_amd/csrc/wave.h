@@ -98,6 +98,14 @@ constexpr int kMinExp = -100;  // blocks with max |x| < 2^-101 quantise to zero
 // hold the 32 columns of one block, and every lane of the wave takes part
 // (padding lanes pass zeros and store = false).  Writes the plane words and,
 // from the block's first lane, the scale.
+//
+// The digits come without a loop over planes: M = N + 0x888888 has the
+// base-16 digits d_j + 8 (each in [0, 15], so no carries and 0 <= M < 2^24),
+// and the code of digit j is ((M >> 4j) & 15) ^ 8.  N itself is read from
+// the float y = x / s_b + 1.5 * 2^23: for |x / s_b| <= 2^22, y rounds
+// x / s_b to the nearest integer (ties to even, as rint) and its bit pattern
+// is 0x4B400000 + N.  The 8 x 6 nibbles are then transposed into the six
+// plane words with bit-field inserts and byte permutes.
 __device__ __forceinline__ void quantize_word(const float v[8], bool first_of_block, bool store,
                                               uint32_t *planes_w, size_t plane_stride, float *scale_b) {
   float m = 0.0f;
@@ -109,19 +117,36 @@ __device__ __forceinline__ void quantize_word(const float v[8], bool first_of_bl
   e = m > 0.0f ? max(e, kMinExp) : kMinExp;
   const float to_int = __int_as_float((127 + kMantBits - e) << 23);   // 2^(22 - e)
   const float to_real = __int_as_float((127 - kMantBits + e) << 23);  // 2^(e - 22)
-  int n[8];
+  constexpr uint32_t kRound = 0x4B400000u;  // 1.5 * 2^23
+  uint32_t M[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) n[i] = (int)__builtin_rintf(v[i] * to_int);
+  for (int i = 0; i < 8; ++i)
+    M[i] = __float_as_uint(__builtin_fmaf(v[i], to_int, __uint_as_float(kRound))) - (kRound - 0x888888u);
+  // pairs (2p, 2p+1): byte k of lo[p] holds nibble 2k of both values (value
+  // 2p in the low half), byte k of hi[p] nibble 2k + 1
+  uint32_t lo[4], hi[4];
 #pragma unroll
-  for (int j = 0; j < kPlanes; ++j) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      word |= (uint32_t)(n[i] & 15) << (4 * i);
-      n[i] = (n[i] + 8) >> 4;  // balanced digit: n = 16 n' + d, d = (n & 15) read as int4
-    }
-    if (store) planes_w[j * plane_stride] = word;
+  for (int p = 0; p < 4; ++p) {
+    lo[p] = (M[2 * p] & 0x0F0F0F0Fu) | ((M[2 * p + 1] << 4) & 0xF0F0F0F0u);
+    hi[p] = ((M[2 * p] >> 4) & 0x0F0F0F0Fu) | (M[2 * p + 1] & 0xF0F0F0F0u);
   }
+  // plane 2k (lo) or 2k + 1 (hi): byte p of the word is byte k of pair p
+  uint32_t w[kPlanes];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t *q = half == 0 ? lo : hi;
+    // bytes 0, 1 of pairs (0, 1) and (2, 3) interleaved; then bytes 2
+    const uint32_t a01 = __builtin_amdgcn_perm(q[1], q[0], 0x05010400u);
+    const uint32_t a23 = __builtin_amdgcn_perm(q[3], q[2], 0x05010400u);
+    const uint32_t b01 = __builtin_amdgcn_perm(q[1], q[0], 0x0C0C0602u);
+    const uint32_t b23 = __builtin_amdgcn_perm(q[3], q[2], 0x0C0C0602u);
+    w[half] = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
+    w[half + 2] = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
+    w[half + 4] = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+  }
+#pragma unroll
+  for (int j = 0; j < kPlanes; ++j)
+    if (store) planes_w[j * plane_stride] = w[j] ^ 0x88888888u;
   if (store && first_of_block) *scale_b = to_real;
 }
 
