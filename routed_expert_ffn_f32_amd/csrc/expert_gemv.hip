@@ -221,18 +221,15 @@ __global__ __launch_bounds__(kGuWaves * 64, COLI_GU_MIN_WAVES) void gate_up_kern
 // into equal contiguous runs, one per wave of the grid, so every wave streams
 // the same number of gate and up rows whatever the routing.  A row is h/32
 // chunks of 32 columns (16 bytes of codes each); lane l takes chunks
-// l, l + 64, ..., so one wave-load covers 1 KB of a row.  kSbDepth rows are
-// in flight per wave.  The hidden rows' digit planes are held in registers
-// (T = 1) or in LDS (T = 2..4).  Each row ends in two wave reductions per
-// token and one float32 store of silu(g) * u.
+// l, l + 64, ..., so one wave-load covers 1 KB of a row.  A wave's first
+// shared-expert row is requested while the block computes the routing;
+// kSbDepth rows are in flight after that.  The hidden rows' digit planes are
+// held in registers (T = 1) or in LDS (T = 2..4).  Each row ends in two wave
+// reductions per token and one float32 store of silu(g) * u.
 //
-// down + combine: block b owns output rows [b R, b R + R).  Wave w takes the
-// slots w, w + waves, ... (slot a < T*k: assignment a; T*k + t: the shared
-// expert on token t).  For its slot it first quantises the float32
-// intermediate into digit planes -- lane l owns the 32-column block l, so the
-// block scale is lane-local -- and keeps them in registers, then streams the
-// R down rows of the slot's expert, kDcDepth rows in flight, into LDS.  The
-// block then sums w_j * y_j in slot order plus the shared row into `out`.
+// down + combine: every wave owns a few output rows and streams them from
+// each slot's down matrix in turn, against the slot's intermediate row held
+// in LDS as digit planes (see the kernel's comment).
 // ---------------------------------------------------------------------------
 #ifndef COLI_SB_DEPTH
 #define COLI_SB_DEPTH 2
@@ -397,10 +394,18 @@ __device__ __forceinline__ void gu_consume(const GuBuf<NCH> &b, const GuCursor &
 // grid = kSbBlocks (XREG: 4 waves) or kSbBlocksLds (8 waves) blocks.  Dynamic
 // LDS: the hidden rows' digit planes [T][6][h/32] uint4, then scales
 // [T][h/32].
+//
+// Every load is issued at a program point that all waves pass, with invalid
+// rows reading zeros instead of being skipped, so the compiler's waits count
+// exactly the loads issued after the ones awaited.  XREG (one token): wave
+// 0 alone merges the selection and hands the routing to the other waves
+// through an LDS flag, so that it never waits for waves stalled on issuing
+// row loads; with several tokens the merging waves meet at a block barrier.
 template <int NCH, bool XREG>
 __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodeProblem P) {
   extern __shared__ uint4 xl[];
   __shared__ SmallRouting R;
+  __shared__ int routed;  // XREG: set by wave 0 once R holds the routing
   constexpr int kWaves = XREG ? 4 : 8;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int h = P.h, I = P.I, T = P.T, nch = h >> 5;
@@ -423,30 +428,24 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   for (int j = 0; j < kXsPer; ++j) xsv[j] = bloadf(rxs, (uint32_t)(threadIdx.x + j * blockDim.x) * 4, 0);
   // these small loads complete before any row is requested: behind the row
   // requests in the memory queues their latency grows several-fold, and the
-  // routing, which needs them, is what the block waits for.  The selection
-  // then runs while the shared rows stream.
+  // routing, which needs them, is what the block waits for
   __builtin_amdgcn_s_waitcnt(0);
-  // 3. this wave's share of the shared expert's rows needs no routing; it is
-  // requested once this wave's part of the selection is done (issuing rows
-  // into full memory queues stalls a wave for microseconds)
+  // 3. this wave's rows: its share of the shared expert's rows (no routing
+  // needed; the first one is requested during the routing), then its share
+  // of the routed experts' rows
   const int64_t W = (int64_t)gridDim.x * kWaves, gw = (int64_t)blockIdx.x * kWaves + wave;
   GuSeq q;
   q.a0 = P.has_shared ? (int)((int64_t)I * gw / W) : 0;
   q.na = P.has_shared ? (int)((int64_t)I * (gw + 1) / W) - q.a0 : 0;
   constexpr int D = NCH > 4 ? 1 : kSbDepth;  // wide rows: one in flight (register file)
+  GuBuf<NCH> bs;  // the first shared row
   GuBuf<NCH> buf[D];
-  GuCursor pre{};
+  GuCursor cs{};
   if (P.has_shared) {
-    pre.slot = 0;
-    gu_set_slot(P, R, pre);  // the shared expert: no routing needed
+    cs.slot = 0;
+    gu_set_slot(P, R, cs);  // the shared expert: no routing needed
+    cs.r = q.a0;
   }
-  auto shared_prefetch = [&]() {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      pre.r = q.a0 + d;
-      gu_load(buf[d], pre, d < q.na, h);
-    }
-  };
   // the planes into LDS (more than one batch only for several long rows)
   float *xsl = reinterpret_cast<float *>(xl + nx);
 #pragma unroll
@@ -461,13 +460,10 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   }
   for (int i = threadIdx.x + kXPer * blockDim.x; i < nx; i += blockDim.x) xl[i] = bload16(rx, (uint32_t)i * 16, 0);
   for (int i = threadIdx.x + kXsPer * blockDim.x; i < nxs; i += blockDim.x) xsl[i] = bloadf(rxs, (uint32_t)i * 4, 0);
-  // 4. the routing of the batch (block barriers inside; they also publish
-  // the planes in LDS): the merging waves (one per token) request their
-  // shared rows after the merge, the others before it
+  if (XREG && threadIdx.x == 0) routed = 0;
+  // 4. the routing of the batch: phase A (ends with a block barrier, which
+  // also publishes the planes and the flag), then phase B
   route_small_a(sel, T, P.E, P.k, R);
-  if (wave >= T) shared_prefetch();
-  route_small_b(T, P.E, P.k, P.rsf, R);
-  if (wave < T) shared_prefetch();
   if (XREG) {  // token 0's planes for this lane's chunks (zeros past the row)
 #pragma unroll
     for (int cc = 0; cc < (XREG ? NCH : 1); ++cc) {
@@ -478,25 +474,49 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
       xsr[cc] = in ? xsl[lc] : 0.0f;
     }
   }
-  if (blockIdx.x == 0) {
+  bool have_routing = true;
+  if (XREG) {
+    if (wave == 0) {
+      route_small_b1(P.E, P.k, P.rsf, R);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // R written before the flag
+      __hip_atomic_store(&routed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    gu_load(bs, cs, q.na > 0, h);
+    if (wave != 0) {
+      // wave 0 sets the flag without waiting for any other wave; the bound
+      // only guards against a hang (a wave that gives up streams no routed
+      // row)
+      int spins = 0;
+      while (__hip_atomic_load(&routed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0 && ++spins < (1 << 22))
+        __builtin_amdgcn_s_sleep(1);
+      asm volatile("" ::: "memory");  // R is read after the flag
+      have_routing = spins < (1 << 22);
+    }
+  } else {
+    route_small_b(T, P.E, P.k, P.rsf, R);
+    gu_load(bs, cs, q.na > 0, h);
+  }
+  const int64_t Nr = have_routing ? (int64_t)R.n_active * I : 0;
+  q.b0 = (int)(Nr * gw / W);
+  q.n = q.na + (int)(Nr * (gw + 1) / W) - q.b0;
+  // 5. the rest of the sequence (after bs's row) through a ring of D buffers
+  const int s0 = min(q.na, 1);
+  GuCursor pre{};
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const bool v = s0 + d < q.n;
+    if (v) seq_seek(P, R, q, s0 + d, pre);
+    gu_load(buf[d], pre, v, h);
+  }
+  if (s0 + D < q.n) seq_seek(P, R, q, s0 + D, pre);
+  if (blockIdx.x == 0 && have_routing) {
     const RoutingOut o{P.idx, P.wsel, P.sorted_ids, P.inv, P.offsets, P.active, P.n_active};
     publish_routing(R, T, P.k, P.E, o);
   }
-  const int64_t Nr = (int64_t)R.n_active * I;
-  q.b0 = (int)(Nr * gw / W);
-  q.n = q.na + (int)(Nr * (gw + 1) / W) - q.b0;
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    if (d >= q.na) {  // uniform
-      const bool v = d < q.n;
-      if (v) seq_seek(P, R, q, d, pre);
-      gu_load(buf[d], pre, v, h);
-    }
-  }
-  if (D < q.n) seq_seek(P, R, q, D, pre);
+  gu_consume<NCH, XREG>(bs, cs, q.na > 0, xr, xsr, xl, nch, R, P);
   GuCursor cur{};
-  seq_seek(P, R, q, 0, cur);
-  for (int i = 0; i < q.n; i += D) {
+  if (s0 < q.n) seq_seek(P, R, q, s0, cur);
+  for (int i = s0; i < q.n; i += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int ic = i + d;

@@ -144,6 +144,27 @@ __device__ __forceinline__ void route_small_b(int T, int E, int k, float rsf, Sm
   block_barrier();
 }
 
+// Phase B for one token, by the calling wave alone and without a block
+// barrier (after route_small_a): the merge, then the assignments in expert
+// order (one token: each selected expert has exactly one assignment).
+__device__ __forceinline__ void route_small_b1(int E, int k, float rsf, SmallRouting &R) {
+  const int lane = threadIdx.x & 63;
+  const int wt = small_select_plan(1, E, k).wt;
+  select_merge(R.cu[0], R.ce[0], R.cs[0], wt * k, k, rsf, R.idx, R.w, R.scratch[0], R.slot_of[0]);
+  wave_lds_sync();
+  if (lane < k) {
+    const int sl = R.slot_of[0][lane];
+    R.sorted_ids[lane] = sl;
+    R.inv[sl] = lane;
+    R.active[lane] = R.idx[sl];
+    R.seg_begin[lane] = lane;
+  }
+  if (lane == 0) {
+    R.n_active = k;
+    R.seg_begin[k] = k;
+  }
+}
+
 // Where the routing of a call goes (device arrays of the C ABI's layout).
 struct RoutingOut {
   int32_t *idx;
