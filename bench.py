@@ -218,10 +218,11 @@ def main():
     # the intermediate rows written
     gate_up_w = 2 * (I * h // 2 + 4 * I * h // 64)
     mean_experts = float(np.mean([n_active[l, c % args.pool] for l, c in calls])) + shape.n_shared
-    gu_bytes = mean_experts * gate_up_w + T * h * 4 + (T * k + T * shape.n_shared) * I * 4
-    gu_ms, gu_n = kern.get("expert_gemv_gate_up", (0.0, 0))
-    gu_avg_s = gu_ms / gu_n / 1e3 if gu_n else float("nan")
-    achieved = gu_bytes / gu_avg_s / 1e9
+    dom_name = "expert_gemv_gate_up"
+    dom_bytes = mean_experts * gate_up_w + T * h * 4 + (T * k + T * shape.n_shared) * I * 4
+    dom_ms, dom_n = kern.get(dom_name, (0.0, 0))
+    dom_avg_s = dom_ms / dom_n / 1e3 if dom_n else float("nan")
+    achieved = dom_bytes / dom_avg_s / 1e9
     traffic = read_traffic()
 
     result = {
@@ -244,10 +245,10 @@ def main():
         "expert_weight_frac_of_hbm_peak": round(expert_gbps / HBM_PEAK_GBPS, 4),
         "us_per_layer_call": round(1e3 * total_ms / (K * L), 3),
         "kernel_avg_us": kern_us,
-        "roofline": {"kernel": "expert_gemv_gate_up", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "bytes_per_launch": int(gu_bytes)},
+                     "bytes_per_launch": int(dom_bytes)},
     }
     del xs, outs
 
@@ -337,7 +338,7 @@ def cpu_baseline(args, shape, layers, dev):
     done, spent, worst = 0, 0.0, 0.0
     cache = {}
     out = torch.empty((1, shape.hidden), dtype=torch.float32, device=dev)
-    while spent < args.cpu_seconds and done < args.pool:
+    while spent < args.cpu_seconds and done < 512:
         x = synth.hidden(shape, args.seed, 1, layer=0, batch=1000 + done)
         idx, _ = oracle.route(shape, wr, b, x)
         for e in np.unique(idx):

@@ -44,6 +44,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 struct Layout {
   size_t wrP, logits, xq, xs, idx, w, offsets, sorted_ids, inv, active, n_active, mq, ms, midf, y;
   size_t xb, midb, tiles, n_tiles;  // prefill path
+  size_t queues;                    // row queues of the small-batch gate/up launch
   size_t total;
 };
 
@@ -104,6 +105,7 @@ Layout layout_of(const coli_moe_config_t &c) {
   L.midb = o;       o = align_up(o + (pre ? P * I * 2 : 0));
   L.tiles = o;      o = align_up(o + tiles * 8);
   L.n_tiles = o;    o = align_up(o + 4);
+  L.queues = o;     o = align_up(o + coli::kRowQueueWords * 4);
   L.total = o;
   return L;
 }
@@ -197,7 +199,8 @@ int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe
   m->prof_used = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (coli::launch_router_permute(w->router_w, at<float>(m, L.wrP), cfg->hidden, cfg->n_experts, s) !=
-      hipSuccess) {
+          hipSuccess ||
+      coli::launch_fill_i32(at<int32_t>(m, L.queues), coli::kRowQueueWords, 0, s) != hipSuccess) {
     delete m;
     return COLI_MOE_EDEVICE;
   }
@@ -324,6 +327,7 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
   P.offsets = offsets;
   P.active = active;
   P.n_active = n_active;
+  P.queues = at<int32_t>(m, L.queues);
 
   if (small) {
     // 2. gate/up (each block routes the batch itself), 3. down + combine

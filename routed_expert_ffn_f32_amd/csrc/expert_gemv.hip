@@ -247,6 +247,9 @@ __global__ __launch_bounds__(kGuWaves * 64, COLI_GU_MIN_WAVES) void gate_up_kern
 #define COLI_DC_BLOCKS 256
 #endif
 constexpr int kSbDepth = COLI_SB_DEPTH;     // gate/up rows in flight per wave
+constexpr int kGuQueues = 64;               // gate/up row queues (atomic counters)
+constexpr int kGuQueueStride = 64;          // int32: one counter per 256 bytes
+static_assert(kGuQueues * kGuQueueStride == kRowQueueWords, "row queue words");
 constexpr int kSbBlocks = COLI_SB_BLOCKS;   // gate/up grid, T = 1 (4 waves per block)
 constexpr int kSbBlocksLds = kSbBlocks / 2; // gate/up grid, T = 2..4 (8 waves per block)
 constexpr int kDcWaves = COLI_DC_WAVES;     // down: waves per block
@@ -285,39 +288,6 @@ __device__ __forceinline__ void gu_set_slot(const DecodeProblem &P, const SmallR
   c.su = P.up.s + e * sstride;
   c.p_begin = uniform(R.seg_begin[s]);
   c.cnt = uniform(R.seg_begin[s + 1]) - c.p_begin;
-}
-
-// A wave's rows: na rows of the shared expert starting at row a0 (known
-// before the routing), then routed rows from flat index b0 over the active
-// experts' rows (expert slot s covers flat indices s*I .. s*I + I - 1), n rows
-// in all.
-struct GuSeq {
-  int na, a0, b0, n;
-};
-
-__device__ __forceinline__ void seq_seek(const DecodeProblem &P, const SmallRouting &R, const GuSeq &q, int i,
-                                         GuCursor &c) {
-  if (i < q.na) {
-    c.slot = 0;
-    c.r = q.a0 + i;
-  } else {
-    const int f = q.b0 + (i - q.na);
-    c.slot = P.has_shared + f / P.I;
-    c.r = f % P.I;
-  }
-  gu_set_slot(P, R, c);
-}
-
-// Moves c from row i to row i + 1 of the sequence (i + 1 < q.n).
-__device__ __forceinline__ void seq_next(const DecodeProblem &P, const SmallRouting &R, const GuSeq &q, int i,
-                                         GuCursor &c) {
-  if (i + 1 == q.na) {
-    seq_seek(P, R, q, i + 1, c);
-  } else if (++c.r == P.I) {
-    c.r = 0;
-    ++c.slot;
-    gu_set_slot(P, R, c);
-  }
 }
 
 template <int NCH>
@@ -430,22 +400,40 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   // requests in the memory queues their latency grows several-fold, and the
   // routing, which needs them, is what the block waits for
   __builtin_amdgcn_s_waitcnt(0);
-  // 3. this wave's rows: its share of the shared expert's rows (no routing
-  // needed; the first one is requested during the routing), then its share
-  // of the routed experts' rows
+  // 3. the rows.  Flat row f < hs*I is row f of the shared expert (no
+  // routing needed), f = hs*I + s*I + r row r of the s-th active routed
+  // expert.  Wave gw takes row gw first if it is a shared row (requested
+  // during the routing); the rows from P0 = min(W, hs*I) on are handed out
+  // at run time: queue q = gw mod kGuQueues holds rows P0 + q + kGuQueues i,
+  // i = 0, 1, ..., and a wave takes the next i of its queue with one atomic
+  // increment, so waves that stream faster take more rows and all waves end
+  // together.
   const int64_t W = (int64_t)gridDim.x * kWaves, gw = (int64_t)blockIdx.x * kWaves + wave;
-  GuSeq q;
-  q.a0 = P.has_shared ? (int)((int64_t)I * gw / W) : 0;
-  q.na = P.has_shared ? (int)((int64_t)I * (gw + 1) / W) - q.a0 : 0;
+  const int hs = P.has_shared, P0 = (int)min<int64_t>(W, (int64_t)hs * I);
+  int32_t *const qctr = P.queues + (int)(gw % kGuQueues) * kGuQueueStride;
+  const int qoff = P0 + (int)(gw % kGuQueues);
   constexpr int D = NCH > 4 ? 1 : kSbDepth;  // wide rows: one in flight (register file)
-  GuBuf<NCH> bs;  // the first shared row
+  GuBuf<NCH> bs;  // the wave's first shared row
   GuBuf<NCH> buf[D];
   GuCursor cs{};
-  if (P.has_shared) {
+  const bool has0 = gw < P0;
+  if (has0) {
     cs.slot = 0;
     gu_set_slot(P, R, cs);  // the shared expert: no routing needed
-    cs.r = q.a0;
+    cs.r = (int)gw;
   }
+  // one atomic increment of this wave's queue: lane 0 receives the index of
+  // its next row (read with uniform() only where it is used, so that the
+  // wait for it comes as late as possible).  The first D + 1 indices are
+  // requested now: they need no routing, and arrive while it is computed.
+  auto grab = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(qctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+  };
+  int gi[D + 1];
+#pragma unroll
+  for (int d = 0; d <= D; ++d) gi[d] = grab();
   // the planes into LDS (more than one batch only for several long rows)
   float *xsl = reinterpret_cast<float *>(xl + nx);
 #pragma unroll
@@ -481,7 +469,7 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // R written before the flag
       __hip_atomic_store(&routed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    gu_load(bs, cs, q.na > 0, h);
+    gu_load(bs, cs, has0, h);
     if (wave != 0) {
       // wave 0 sets the flag without waiting for any other wave; the bound
       // only guards against a hang (a wave that gives up streams no routed
@@ -494,40 +482,56 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
     }
   } else {
     route_small_b(T, P.E, P.k, P.rsf, R);
-    gu_load(bs, cs, q.na > 0, h);
+    gu_load(bs, cs, has0, h);
   }
-  const int64_t Nr = have_routing ? (int64_t)R.n_active * I : 0;
-  q.b0 = (int)(Nr * gw / W);
-  q.n = q.na + (int)(Nr * (gw + 1) / W) - q.b0;
-  // 5. the rest of the sequence (after bs's row) through a ring of D buffers
-  const int s0 = min(q.na, 1);
-  GuCursor pre{};
+  // rows of the call (a wave without the routing stops after the shared ones)
+  const int N = hs * I + (have_routing ? R.n_active * I : 0);
+  auto cursor_of = [&](int f, GuCursor &c) {
+    const int fr = f - hs * I;
+    c.slot = fr < 0 ? 0 : hs + fr / I;
+    c.r = fr < 0 ? f : fr % I;
+    gu_set_slot(P, R, c);
+  };
+  auto row_of = [&](int i) { return qoff + kGuQueues * i < N ? qoff + kGuQueues * i : -1; };
+  // 5. the handed-out rows through a ring of D buffers.  The index of the
+  // next row is requested one step before it is used, and before that step's
+  // row loads, so that waiting for it never waits for them.
+  int fr[D];
+  GuCursor cur[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    const bool v = s0 + d < q.n;
-    if (v) seq_seek(P, R, q, s0 + d, pre);
-    gu_load(buf[d], pre, v, h);
+    fr[d] = row_of(uniform(gi[d]));
+    cur[d] = GuCursor{};
+    if (fr[d] >= 0) cursor_of(fr[d], cur[d]);
+    gu_load(buf[d], cur[d], fr[d] >= 0, h);
   }
-  if (s0 + D < q.n) seq_seek(P, R, q, s0 + D, pre);
+  int pend = gi[D];
   if (blockIdx.x == 0 && have_routing) {
     const RoutingOut o{P.idx, P.wsel, P.sorted_ids, P.inv, P.offsets, P.active, P.n_active};
     publish_routing(R, T, P.k, P.E, o);
   }
-  gu_consume<NCH, XREG>(bs, cs, q.na > 0, xr, xsr, xl, nch, R, P);
-  GuCursor cur{};
-  if (s0 < q.n) seq_seek(P, R, q, s0, cur);
-  for (int i = s0; i < q.n; i += D) {
+  gu_consume<NCH, XREG>(bs, cs, has0, xr, xsr, xl, nch, R, P);
+  // A queue hands out rows in increasing order, so once a ring entry is past
+  // the end every later one is too.  The loop body is straight-line: absent
+  // rows are summed from zeros and not stored, and every step issues its
+  // atomic and its loads (absent rows read nothing), so the compiler's waits
+  // count exactly the operations issued after the ones awaited.
+  bool more = fr[0] >= 0;
+#pragma unroll
+  for (int d = 1; d < D; ++d) more = more || fr[d] >= 0;
+  while (more) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int ic = i + d;
-      const bool v = ic < q.n;
-      gu_consume<NCH, XREG>(buf[d], cur, v, xr, xsr, xl, nch, R, P);
-      if (ic + 1 < q.n) seq_next(P, R, q, ic, cur);
-      const int ip = ic + D;
-      const bool pv = ip < q.n;
-      gu_load(buf[d], pre, pv, h);
-      if (ip + 1 < q.n) seq_next(P, R, q, ip, pre);
+      gu_consume<NCH, XREG>(buf[d], cur[d], fr[d] >= 0, xr, xsr, xl, nch, R, P);
+      const int f = row_of(uniform(pend));
+      pend = grab();
+      fr[d] = f;
+      if (f >= 0) cursor_of(f, cur[d]);
+      gu_load(buf[d], cur[d], f >= 0, h);
     }
+    more = fr[0] >= 0;
+#pragma unroll
+    for (int d = 1; d < D; ++d) more = more || fr[d] >= 0;
   }
 }
 
@@ -802,6 +806,9 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(Decode
       ring_load(u, qc + NS);
     }
   }
+  // the gate/up launch of the next call finds its row queues at zero
+  if (blockIdx.x == 0 && (int)threadIdx.x < kGuQueues)
+    __hip_atomic_store(P.queues + threadIdx.x * kGuQueueStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -1039,5 +1046,6 @@ hipError_t launch_combine(const float *y, const float *w, const int32_t *inv, in
   dim3 grid((h / 4 + 255) / 256, T);
   return launch(combine_kernel, grid, 256, 0, s, y, w, inv, T, k, h, has_shared, out);
 }
+
 
 }  // namespace coli

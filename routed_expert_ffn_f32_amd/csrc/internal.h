@@ -103,7 +103,11 @@ struct DecodeProblem {
   // read by it otherwise
   int32_t *idx, *sorted_ids, *inv, *offsets, *active, *n_active;
   float *wsel;
+  // small batches: row queues of the gate/up launch (kRowQueueWords int32,
+  // zero when it starts; the down launch clears them again)
+  int32_t *queues;
 };
+constexpr int kRowQueueWords = 64 * 64;
 
 // True when the batch takes the small-batch launch structure (router and
 // routing in one launch, gate/up, then down fused with the combine).

@@ -232,6 +232,34 @@ def test_two_runs_bitwise_identical(dev):
 
 
 # ---------------------------------------------------------------------------
+# Calls in a row on one handle: the gate/up launch hands rows out through
+# atomic queues that the down launch clears for the next call.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny_all", 1), ("olmoe", 1), ("single", 1), ("olmoe", 3),
+                                    ("tiny", 4)])
+def test_small_batch_calls_in_a_row(dev, name, T):
+    """Five calls on one handle, each with its own input: routing bit-exact
+    and outputs at the GEMV bar every time."""
+    import dataclasses
+    shapes = {"tiny": synth.TINY, "tiny_all": dataclasses.replace(synth.TINY, top_k=8), "olmoe": synth.OLMOE,
+              "single": synth.LayerShape(hidden=128, n_experts=1, top_k=1, inter=192, n_shared=1, rsf=2.5,
+                                         bias_sigma=0.0)}
+    shape = shapes[name]
+    log(f"small-batch calls in a row: {name} T={T}")
+    L = DeviceLayer(shape, 31, 0, dev, max_tokens=4, keep_host=True)
+    for b in range(5):
+        x = synth.hidden(shape, 31, T, batch=200 + b)
+        out = run(L, x, dev)
+        assert_routing_matches(L, x, T)
+        ref, _, _ = L.oracle_forward(x)
+        err = rel_err(out, ref)
+        log(f"  call {b}: rel err {err:.3e}")
+        assert err <= TOL_GEMV, (b, err)
+    L.close()
+
+
+# ---------------------------------------------------------------------------
 # The bf16 MFMA (prefill) path on small layers: full outputs.
 # ---------------------------------------------------------------------------
 
@@ -322,6 +350,21 @@ def test_glm_decode_full(dev, glm, T):
     err = rel_err(out, ref)
     log(f"  rel err {err:.3e}")
     assert err <= TOL_GEMV
+
+
+@pytest.mark.timeout(300)
+def test_glm_decode_calls_in_a_row(dev, glm):
+    """Single-token and four-token calls alternating on the GLM-like layer,
+    each against the oracle."""
+    for b, T in enumerate((1, 4, 1)):
+        log(f"GLM-like decode T={T}, call {b}")
+        x = synth.hidden(synth.GLM, 1, T, batch=300 + b)
+        out = run(glm, x, dev)
+        assert_routing_matches(glm, x, T)
+        ref, _, _ = glm.oracle_forward(x)
+        err = rel_err(out, ref)
+        log(f"  rel err {err:.3e}")
+        assert err <= TOL_GEMV
 
 
 @pytest.mark.timeout(300)
