@@ -184,11 +184,15 @@ def main():
         # distinct experts per (layer, input) from the library's own dispatch,
         # read back once outside any timed region
         na = np.zeros((L, n), np.int64)
+        ex = [[None] * n for _ in range(L)]  # the experts each call reads: active routed ones, then -1 (shared)
         for l in range(L):
             for i in range(n):
                 layers[l](xs[l][i], outs[l])
                 _, r = layers[l].last_routing()
                 na[l, i] = int(r["n_active"].item())
+                act = r["active"][:na[l, i]].cpu().tolist() + ([-1] if shape.n_shared else [])
+                ex[l][i] = torch.tensor(act, dtype=torch.int32, device=dev)
+        make_pool.experts = ex
         return xs, outs, na
 
     def run_stack(xs, outs, s0, steps):
@@ -225,6 +229,22 @@ def main():
     achieved = dom_bytes / dom_avg_s / 1e9
     traffic = read_traffic()
 
+    # read ceiling of the same access pattern: a pure-load launch of the
+    # same calls' gate and up rows (same grid, nothing computed)
+    exs = make_pool.experts
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run_probe(s0, steps):
+        for st in range(s0, s0 + steps):
+            for l in range(L):
+                e = exs[l][(st * L + l) % args.pool]
+                cm.coli_moe_probe_read(layers[l].handle, e.data_ptr(), e.numel(), stream)
+
+    run_probe(0, W)
+    probe_ms = time_calls(torch, lambda st: run_probe(W + st, 1), K)
+    probe_us = 1e3 * probe_ms / (K * L)
+    probe_bytes = mean_experts * gate_up_w
+
     result = {
         "metric": "MoE-layer tokens/s + expert-weight HBM GB/s (int4 gs64, decode T=1)",
         "value": round(tok_per_s, 1),
@@ -249,6 +269,9 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic),
                      "bytes_per_launch": int(dom_bytes)},
+        "read_ceiling": {"kernel": "read probe: the same calls' gate and up rows, loads only, same grid",
+                         "us_per_launch": round(probe_us, 3), "GBps": round(probe_bytes / probe_us / 1e3, 1),
+                         "dominant_kernel_time_over_probe": round(1e6 * dom_avg_s / probe_us, 4)},
     }
     del xs, outs
 

@@ -168,6 +168,19 @@ int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, 
                            void *stream);
 
 /*
+ * Measurement only: the HBM read ceiling of the decode gate/up kernel's
+ * access pattern.  Enqueues one launch with the small-batch gate/up launch's
+ * grid that loads, and otherwise discards, the gate and up codes and scales
+ * of every row of the n experts listed in DEVICE experts [n] (expert id, or
+ * -1 for the shared expert; ids outside [-1, n_experts) read nothing),
+ * split statically over its waves with two rows in flight per wave: the
+ * bytes the gate/up step reads for those experts, with none of its
+ * arithmetic.  Overwrites the handle's logits buffer.  1 <= n <= 64,
+ * hidden <= 8192.  Errors: -4, -3.
+ */
+int coli_moe_probe_read(const coli_moe_t *m, const int32_t *experts, int32_t n, void *stream);
+
+/*
  * Kernel timing.  coli_moe_profile_begin makes the next `max_calls` forwards
  * of the handle record a HIP event pair around each kernel they launch (host
  * allocations only; events are created here).  coli_moe_profile_end waits

@@ -75,6 +75,8 @@ def load_library():
         L.coli_moe_last_routing.restype = ctypes.c_int
         L.coli_moe_test_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.coli_moe_test_dispatch.restype = ctypes.c_int
+        L.coli_moe_probe_read.argtypes = [vp, vp, i32, vp]
+        L.coli_moe_probe_read.restype = ctypes.c_int
         L.coli_moe_profile_begin.argtypes = [vp, i32]
         L.coli_moe_profile_begin.restype = ctypes.c_int
         L.coli_moe_profile_end.argtypes = [vp, vp, vp]
@@ -132,6 +134,12 @@ def coli_moe_test_dispatch(idx: int, T: int, k: int, E: int, offsets: int, sorte
     return _check(load_library().coli_moe_test_dispatch(idx, int(T), int(k), int(E), offsets, sorted_ids,
                                                         inv, active, n_active, stream),
                   "coli_moe_test_dispatch")
+
+
+def coli_moe_probe_read(handle, experts: int, n: int, stream: int = 0) -> int:
+    """Pure-load probe of the gate/up rows of n experts (device int32 ids, -1
+    = shared): the read ceiling of the gate/up access pattern."""
+    return _check(load_library().coli_moe_probe_read(handle, experts, int(n), stream), "coli_moe_probe_read")
 
 
 def coli_moe_profile_begin(handle, max_calls: int) -> int:

@@ -414,6 +414,24 @@ int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, 
   return COLI_MOE_OK;
 }
 
+int coli_moe_probe_read(const coli_moe_t *mc, const int32_t *experts, int32_t n, void *stream) {
+  if (!mc || !experts || n < 1 || n > 64 || mc->cfg.hidden > 8192) return COLI_MOE_EARG;
+  coli_moe_t *m = const_cast<coli_moe_t *>(mc);
+  coli::DecodeProblem P{};
+  P.gate = {m->w.gate_q, m->w.gate_s};
+  P.up = {m->w.up_q, m->w.up_s};
+  P.sh_gate = {m->w.sh_gate_q, m->w.sh_gate_s};
+  P.sh_up = {m->w.sh_up_q, m->w.sh_up_s};
+  P.h = m->cfg.hidden;
+  P.I = m->cfg.inter;
+  P.E = m->cfg.n_experts;
+  P.has_shared = m->cfg.n_shared;
+  if (coli::launch_read_probe(P, experts, n, at<uint32_t>(m, m->L.logits), static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return COLI_MOE_EDEVICE;
+  return COLI_MOE_OK;
+}
+
 int coli_moe_profile_begin(coli_moe_t *m, int32_t max_calls) {
   if (!m || max_calls < 0) return COLI_MOE_EARG;
   const size_t need = (size_t)max_calls * COLI_MOE_N_KERNELS;

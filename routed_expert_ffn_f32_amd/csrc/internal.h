@@ -118,6 +118,11 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
 // gate/up: mid = silu(Wg x) * (Wu x) for every assignment position p
 // (routed: p = sorted position; shared: p = T*k + t), written as digit planes.
 hipError_t launch_gemv_gate_up(const DecodeProblem &P, hipStream_t s);
+// Read probe: the gate and up rows of n experts (device ids, -1 = shared;
+// h <= 8192) with pure loads and the small-batch gate/up launch shape; sink
+// receives at most one word.
+hipError_t launch_read_probe(const DecodeProblem &P, const int32_t *experts, int n, uint32_t *sink,
+                             hipStream_t s);
 // Small batches: out[t] = sum_j w[t,j] Wd_e mid[inv(t,j)] + Wd_sh mid[T*k + t].
 hipError_t launch_down_combine(const DecodeProblem &P, float *out, hipStream_t s);
 // Larger batches: y[p] = Wd mid[p] ...

@@ -96,6 +96,7 @@ def test_forward_and_dispatch_argument_errors():
     assert lib.coli_moe_last_routing(None, None, None, None, None, None, None, None, None) == -4
     assert lib.coli_moe_test_dispatch(0x1000, 4, 0, 8, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
     assert lib.coli_moe_test_dispatch(0x1000, 4, 2, 513, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
+    assert lib.coli_moe_probe_read(None, 0x1000, 9, None) == -4
     assert lib.coli_moe_test_dispatch(0x1000, -1, 2, 8, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
     assert lib.coli_moe_test_dispatch(None, 4, 2, 8, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
     lib.coli_moe_free(None)  # no-op
