@@ -999,7 +999,7 @@ namespace {
 template <int NCH>
 __global__ __launch_bounds__(256) void read_probe_kernel(DecodeProblem P, const int32_t *__restrict__ experts, int n,
                                                          uint32_t *__restrict__ sink) {
-  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int wave = uniform(threadIdx.x >> 6);
   const int64_t W = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wave;
   const int I = P.I, h = P.h;
   const int64_t N = (int64_t)n * I;
