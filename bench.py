@@ -22,6 +22,7 @@ the CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
     python bench.py --copy-calibration   # plain 1 GiB device copy (counter scale)
+    python bench.py --prefill-only       # the prefill layer alone (for counter runs)
 """
 from __future__ import annotations
 
@@ -57,6 +58,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="headline decode T=1 only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy 5 times and exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill layer (T=4096, Zipf load): print its JSON object and exit")
     return ap.parse_args()
 
 
@@ -153,6 +156,9 @@ def main():
         sys.exit(1)
     cm.load_library()  # fails loudly if the HIP library is not built
     dev = torch.device("cuda:0")
+    if args.prefill_only:
+        print(json.dumps(prefill(args, cm, torch, np, synth, dev)), flush=True)
+        return
     shape = synth.GLM
     L, K, W = args.layers, args.steps, args.warmup
     h, I, E, k = shape.hidden, shape.inter, shape.n_experts, shape.top_k
