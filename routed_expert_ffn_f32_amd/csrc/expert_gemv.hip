@@ -71,8 +71,6 @@ __device__ __forceinline__ void gate_up_pass(const DecodeProblem &P, const Slot 
   const uint32_t qbytes = (uint32_t)P.I * rowq, sbytes = (uint32_t)P.I * groups * 4;
   const Rsrc rqa = make_rsrc(S.qa, qbytes), rsa = make_rsrc(S.sa, sbytes);
   const Rsrc rqb = make_rsrc(S.qb, qbytes), rsb = make_rsrc(S.sb, sbytes);
-  const Rsrc rx = make_rsrc(P.xq, (uint32_t)P.T * kPlanes * words * 4);
-  const Rsrc rxs = make_rsrc(P.xs, (uint32_t)P.T * blocks * 4);
   int tok[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) tok[i] = uniform(tok_of(tc + i));
@@ -94,10 +92,14 @@ __device__ __forceinline__ void gate_up_pass(const DecodeProblem &P, const Slot 
       ws[r] = bloadf(rs, (uint32_t)(lc >> 1) * 4, (uint32_t)(r0 + r) * groups * 4);
     }
   };
+  // one token's planes and scales (a descriptor per token: the whole batch
+  // may pass 4 GiB)
   auto load_planes = [&](int t, int lc, uint4(&xt)[kPlanes]) -> float {
+    const Rsrc rx = make_rsrc(P.xq + (size_t)t * kPlanes * words, (uint32_t)kPlanes * words * 4);
+    const Rsrc rxs = make_rsrc(P.xs + (size_t)t * blocks, (uint32_t)blocks * 4);
 #pragma unroll
-    for (int j = 0; j < kPlanes; ++j) xt[j] = bload16(rx, (uint32_t)lc * 16, (uint32_t)(t * kPlanes + j) * words * 4);
-    return bloadf(rxs, (uint32_t)lc * 4, (uint32_t)t * blocks * 4);
+    for (int j = 0; j < kPlanes; ++j) xt[j] = bload16(rx, (uint32_t)lc * 16, (uint32_t)j * words * 4);
+    return bloadf(rxs, (uint32_t)lc * 4, 0);
   };
   int lc = lane;
   if (lc < nch) load_rows(rqa, rsa, lc, gw, gs);
@@ -211,6 +213,136 @@ __global__ __launch_bounds__(kGuWaves * 64, COLI_GU_MIN_WAVES) void gate_up_kern
   const Slot S = expert_slot(P, e, b, P.offsets[e + 1] - b);
   const int32_t *sid = P.sorted_ids;
   gate_up_slot<NTMAX>(P, S, row0, [&](int i) { return sid[b + i] / k; }, mid_lds);
+}
+
+// Larger batches, rows held in registers: a block is one wave, which loads
+// its kGuRows gate and up rows (all columns: chunks lc = lane + 64 cc,
+// cc < NCH) once, then runs every token of the slot through them, one token
+// at a time, the next chunk's digit planes in flight during the current
+// chunk's sums, and writes silu(g) * u of its rows to midf (float32).  Each
+// weight row is read from HBM once per call.  One-wave blocks share nothing,
+// so the waves of a SIMD drift apart: one loads its rows while another
+// computes.
+template <int NCH, class TokOf>
+__device__ __forceinline__ void gate_up_tokens(const DecodeProblem &P, const Slot &S, int r0, const TokOf &tok_of) {
+  const int lane = threadIdx.x & 63;
+  const int h = P.h, I = P.I, rowq = h >> 1, groups = h >> 6, words = h >> 3, nch = h >> 5;
+  // the rows: one descriptor per row, so lanes past the row read zeros
+  uint4 gw[NCH][kGuRows], uw[NCH][kGuRows];
+  float gs[NCH][kGuRows], us[NCH][kGuRows];
+#pragma unroll
+  for (int r = 0; r < kGuRows; ++r) {
+    const size_t row = (size_t)(r0 + r);
+    const Rsrc qa = make_rsrc(S.qa + row * rowq, (uint32_t)rowq), qb = make_rsrc(S.qb + row * rowq, (uint32_t)rowq);
+    const Rsrc sa = make_rsrc(S.sa + row * groups, (uint32_t)groups * 4);
+    const Rsrc sb = make_rsrc(S.sb + row * groups, (uint32_t)groups * 4);
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+      const uint32_t lc = (uint32_t)(lane + 64 * cc);
+      gw[cc][r] = bload16(qa, lc * 16, 0);
+      uw[cc][r] = bload16(qb, lc * 16, 0);
+      gs[cc][r] = bloadf(sa, (lc >> 1) * 4, 0);
+      us[cc][r] = bloadf(sb, (lc >> 1) * 4, 0);
+    }
+  }
+  // a token's planes: [6][h/8] words and scales [h/32], a descriptor per
+  // token (the whole batch may pass 4 GiB); lanes past the row read zeros
+  // (they meet zero weights anyway)
+  auto load_planes = [&](int tok, int cc, uint4 (&xt)[kPlanes], float &sx) {
+    const Rsrc rx = make_rsrc(P.xq + (size_t)tok * kPlanes * words, (uint32_t)kPlanes * words * 4);
+    const Rsrc rxs = make_rsrc(P.xs + (size_t)tok * nch, (uint32_t)nch * 4);
+    const uint32_t lc = (uint32_t)(lane + 64 * cc);
+#pragma unroll
+    for (int j = 0; j < kPlanes; ++j) xt[j] = bload16(rx, lc * 16, (uint32_t)j * words * 4);
+    sx = bloadf(rxs, lc * 4, 0);
+  };
+  const int cnt = S.cnt;
+  uint4 xn[kPlanes];
+  float sxn;
+  int tk = cnt > 0 ? uniform(tok_of(0)) : 0;  // the current token
+  if (cnt > 0) load_planes(tk, 0, xn, sxn);
+  for (int t = 0; t < cnt; ++t) {
+    const int tn = t + 1 < cnt ? uniform(tok_of(t + 1)) : 0;  // the next one, read a token ahead
+    float ga[kGuRows], ua[kGuRows];
+#pragma unroll
+    for (int r = 0; r < kGuRows; ++r) ga[r] = ua[r] = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < NCH; ++cc) {
+      uint4 xt[kPlanes];
+#pragma unroll
+      for (int j = 0; j < kPlanes; ++j) xt[j] = xn[j];
+      const float sx = sxn;
+      // the next (token, chunk)'s planes in flight during these sums
+      if (cc + 1 < NCH)
+        load_planes(tk, cc + 1, xn, sxn);
+      else if (t + 1 < cnt)
+        load_planes(tn, 0, xn, sxn);
+#pragma unroll
+      for (int r = 0; r < kGuRows; ++r) {
+        ga[r] = __builtin_fmaf((float)dot_planes(gw[cc][r], xt), gs[cc][r] * sx, ga[r]);
+        ua[r] = __builtin_fmaf((float)dot_planes(uw[cc][r], xt), us[cc][r] * sx, ua[r]);
+      }
+    }
+    // lane r < kGuRows takes row r's sums; four lanes write 16 bytes
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kGuRows; ++r) {
+      const float gr = wave_sum(ga[r]), ur = wave_sum(ua[r]);
+      g = lane == r ? gr : g;
+      u = lane == r ? ur : u;
+    }
+    if (lane < kGuRows) P.midf[(size_t)(S.p_begin + t) * I + r0 + lane] = g / (1.0f + expf(-g)) * u;
+    tk = tn;
+  }
+}
+
+// grid = (I / kGuRows, has_shared + n_routed_slots), one wave per block; the
+// routing and dispatch arrays come from the selection launch.
+template <int NCH>
+__global__ __launch_bounds__(64) void gate_up_tok_kernel(DecodeProblem P) {
+  const int r0 = blockIdx.x * kGuRows;
+  const int slot = (int)blockIdx.y - P.has_shared;
+  if (slot < 0) {  // shared expert: every token, weight 1
+    Slot S;
+    S.p_begin = P.T * P.k;
+    S.cnt = P.T;
+    S.qa = P.sh_gate.q;
+    S.sa = P.sh_gate.s;
+    S.qb = P.sh_up.q;
+    S.sb = P.sh_up.s;
+    gate_up_tokens<NCH>(P, S, r0, [](int i) { return i; });
+    return;
+  }
+  const int k = P.k;
+  if (slot >= *P.n_active) return;
+  const int e = P.active[slot];
+  const int b = P.offsets[e];
+  const Slot S = expert_slot(P, e, b, P.offsets[e + 1] - b);
+  const int32_t *sid = P.sorted_ids;
+  gate_up_tokens<NCH>(P, S, r0, [&](int i) { return sid[b + i] / k; });
+}
+
+// midf [n][I] (float32) as digit planes mq [n][6][I/8] words and scales
+// ms [n][I/32], one thread per 8-column word; the four words of a 32-column
+// block are a quad of lanes (I/8 is a multiple of 8, so a quad never
+// straddles two rows).
+__global__ __launch_bounds__(256) void quantize_mid_kernel(const float *__restrict__ midf, int n, int I,
+                                                           uint32_t *__restrict__ mq, float *__restrict__ ms) {
+  const int words = I >> 3;
+  const size_t wg = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const bool valid = wg < (size_t)n * words;
+  const size_t p = valid ? wg / words : 0;
+  const int w = valid ? (int)(wg % words) : 0;
+  float v[8];
+  if (valid) {
+    const float4 a = *reinterpret_cast<const float4 *>(midf + p * I + 8 * w);
+    const float4 b = *reinterpret_cast<const float4 *>(midf + p * I + 8 * w + 4);
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+  }
+  quantize_word(v, (w & 3) == 0, valid, mq + p * kPlanes * words + w, (size_t)words, ms + p * (I >> 5) + (w >> 2));
 }
 
 // ---------------------------------------------------------------------------
@@ -1075,8 +1207,22 @@ hipError_t launch_gemv_gate_up(const DecodeProblem &P, hipStream_t s) {
   }
   const int slots = P.n_routed_slots + (P.has_shared ? 1 : 0);
   if (slots == 0) return hipSuccess;
+  // rows held in registers up to h = 6144 (wider rows do not fit the
+  // register file), then the digit planes of midf for the down launch;
+  // wider: passes of at most two tokens, planes written directly
+  const int nchl = (P.h + 2047) / 2048;
+  if (nchl <= 3) {
+    const dim3 tg(P.I / kGuRows, slots);
+    hipError_t err = nchl == 1   ? launch(gate_up_tok_kernel<1>, tg, 64, 0, s, P)
+                     : nchl == 2 ? launch(gate_up_tok_kernel<2>, tg, 64, 0, s, P)
+                                 : launch(gate_up_tok_kernel<3>, tg, 64, 0, s, P);
+    if (err != hipSuccess) return err;
+    const int n = P.T * (P.k + P.has_shared);
+    const size_t nw = (size_t)n * (P.I >> 3);
+    return launch(quantize_mid_kernel, dim3((unsigned)((nw + 255) / 256)), 256, 0, s, (const float *)P.midf, n,
+                  P.I, P.mq, P.ms);
+  }
   dim3 grid(P.I / (kGuWaves * kGuRows), slots);
-  // passes of at most two tokens: wider passes do not fit the register file
   if (P.T == 1) return launch(gate_up_kernel<1>, grid, kGuWaves * 64, 0, s, P);
   return launch(gate_up_kernel<2>, grid, kGuWaves * 64, 0, s, P);
 }

@@ -97,7 +97,7 @@ struct DecodeProblem {
   const float *xs;      // and block scales [T][h/32]
   uint32_t *mq;         // expert intermediates as digit planes [P][6][I/8], P = T*k + T*has_shared
   float *ms;            // and block scales [P][I/32] (larger batches)
-  float *midf;          // expert intermediates as float32 [P][I] (small batches)
+  float *midf;          // expert intermediates as float32 [P][I]
   float *y;             // expert outputs [P][h] (larger batches)
   // routing and dispatch: written by the gate/up launch for small batches,
   // read by it otherwise
