@@ -225,6 +225,7 @@ __global__ __launch_bounds__(kGuWaves * 64, COLI_GU_MIN_WAVES) void gate_up_kern
 // computes.
 template <int NCH, class TokOf>
 __device__ __forceinline__ void gate_up_tokens(const DecodeProblem &P, const Slot &S, int r0, const TokOf &tok_of) {
+  static_assert(kGuRows == 4, "the up sums sit 4 lanes from the gate sums");
   const int lane = threadIdx.x & 63;
   const int h = P.h, I = P.I, rowq = h >> 1, groups = h >> 6, words = h >> 3, nch = h >> 5;
   // the rows: one descriptor per row, so lanes past the row read zeros
@@ -283,14 +284,14 @@ __device__ __forceinline__ void gate_up_tokens(const DecodeProblem &P, const Slo
         ua[r] = __builtin_fmaf((float)dot_planes(uw[cc][r], xt), us[cc][r] * sx, ua[r]);
       }
     }
-    // lane r < kGuRows takes row r's sums; four lanes write 16 bytes
-    float g = 0.0f, u = 0.0f;
+    // lane l: the sum of gate row l % 4 (l % 8 < 4) or up row l % 4; lane
+    // r < kGuRows brings in its up sum from a lane 4 away, and the four
+    // lanes write 16 bytes
+    float v[2 * kGuRows];
 #pragma unroll
-    for (int r = 0; r < kGuRows; ++r) {
-      const float gr = wave_sum(ga[r]), ur = wave_sum(ua[r]);
-      g = lane == r ? gr : g;
-      u = lane == r ? ur : u;
-    }
+    for (int r = 0; r < kGuRows; ++r) v[r] = ga[r], v[kGuRows + r] = ua[r];
+    const float g = rows_sum<2 * kGuRows>(v);
+    const float u = dpp_f<kDppRowRor4>(g);
     if (lane < kGuRows) P.midf[(size_t)(S.p_begin + t) * I + r0 + lane] = g / (1.0f + expf(-g)) * u;
     tk = tn;
   }
@@ -1018,6 +1019,83 @@ __global__ __launch_bounds__(kDnWaves * 64) void down_kernel(DecodeProblem P) {
   for (; tc < cnt; ++tc) down_pass<1>(P, q, s, p_begin, r0, tc);
 }
 
+// Larger batches, rows held in registers: a block is one wave, which loads
+// R down rows (all columns: chunks lc = lane + 64 cc, cc < NCHD) once and
+// runs every intermediate row of the slot through them, the next chunk's
+// digit planes in flight during the current chunk's sums.
+template <int NCHD, int R>
+__global__ __launch_bounds__(64) void down_tok_kernel(DecodeProblem P) {
+  const int lane = threadIdx.x & 63;
+  const int slot = (int)blockIdx.y - P.has_shared;
+  const uint8_t *q;
+  const float *s;
+  int p_begin, cnt;
+  if (slot < 0) {
+    q = P.sh_down.q;
+    s = P.sh_down.s;
+    p_begin = P.T * P.k;
+    cnt = P.T;
+  } else {
+    if (slot >= *P.n_active) return;
+    const int e = P.active[slot];
+    const size_t qstride = (size_t)P.h * (P.I >> 1), sstride = (size_t)P.h * (P.I >> 6);
+    q = P.down.q + e * qstride;
+    s = P.down.s + e * sstride;
+    p_begin = P.offsets[e];
+    cnt = P.offsets[e + 1] - p_begin;
+  }
+  const int h = P.h, I = P.I, rowq = I >> 1, groups = I >> 6, words = I >> 3, nch = I >> 5;
+  const int r0 = blockIdx.x * R;
+  uint4 dw[NCHD][R];
+  float ds[NCHD][R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const size_t row = (size_t)(r0 + r);
+    const Rsrc rq = make_rsrc(q + row * rowq, (uint32_t)rowq), rs = make_rsrc(s + row * groups, (uint32_t)groups * 4);
+#pragma unroll
+    for (int cc = 0; cc < NCHD; ++cc) {
+      const uint32_t lc = (uint32_t)(lane + 64 * cc);
+      dw[cc][r] = bload16(rq, lc * 16, 0);
+      ds[cc][r] = bloadf(rs, (lc >> 1) * 4, 0);
+    }
+  }
+  // an intermediate row's planes [6][I/8] words and scales [I/32], a
+  // descriptor per row; lanes past the row read zeros
+  auto load_planes = [&](int p, int cc, uint4 (&xt)[kPlanes], float &sx) {
+    const Rsrc rx = make_rsrc(P.mq + (size_t)p * kPlanes * words, (uint32_t)kPlanes * words * 4);
+    const Rsrc rxs = make_rsrc(P.ms + (size_t)p * nch, (uint32_t)nch * 4);
+    const uint32_t lc = (uint32_t)(lane + 64 * cc);
+#pragma unroll
+    for (int j = 0; j < kPlanes; ++j) xt[j] = bload16(rx, lc * 16, (uint32_t)j * words * 4);
+    sx = bloadf(rxs, lc * 4, 0);
+  };
+  uint4 xn[kPlanes];
+  float sxn;
+  if (cnt > 0) load_planes(p_begin, 0, xn, sxn);
+  for (int t = 0; t < cnt; ++t) {
+    const int p = p_begin + t;
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int cc = 0; cc < NCHD; ++cc) {
+      uint4 xt[kPlanes];
+#pragma unroll
+      for (int j = 0; j < kPlanes; ++j) xt[j] = xn[j];
+      const float sx = sxn;
+      if (cc + 1 < NCHD)
+        load_planes(p, cc + 1, xn, sxn);
+      else if (t + 1 < cnt)
+        load_planes(p + 1, 0, xn, sxn);
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = __builtin_fmaf((float)dot_planes(dw[cc][r], xt), ds[cc][r] * sx, acc[r]);
+    }
+    // lane r < R holds row r's sum; R lanes write 4R contiguous bytes
+    const float y = rows_sum<R>(acc);
+    if (lane < R) P.y[(size_t)p * h + r0 + lane] = y;
+  }
+}
+
 // out[t][c..c+3]; the k slot weights and positions are loaded first (up to
 // kMaxTopK, uniform per block), then all expert rows, then summed in slot
 // order and the shared row added last.
@@ -1240,6 +1318,15 @@ hipError_t launch_down_combine(const DecodeProblem &P, float *out, hipStream_t s
 hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s) {
   const int slots = P.n_routed_slots + (P.has_shared ? 1 : 0);
   if (slots == 0 || P.T == 0) return hipSuccess;
+  // rows held in registers up to I = 8192 (16, 8 or 4 rows a wave; h is a
+  // multiple of 64); wider: passes of up to four intermediate rows
+  switch ((P.I + 2047) / 2048) {
+    case 1: return launch(down_tok_kernel<1, 16>, dim3(P.h / 16, slots), 64, 0, s, P);
+    case 2: return launch(down_tok_kernel<2, 8>, dim3(P.h / 8, slots), 64, 0, s, P);
+    case 3: return launch(down_tok_kernel<3, 4>, dim3(P.h / 4, slots), 64, 0, s, P);
+    case 4: return launch(down_tok_kernel<4, 4>, dim3(P.h / 4, slots), 64, 0, s, P);
+    default: break;
+  }
   dim3 grid(P.h / (kDnWaves * kDnRows), slots);
   if (P.T == 1)
     return launch(down_kernel<1>, grid, kDnWaves * 64, 0, s, P);

@@ -68,6 +68,46 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// One halving step of rows_sum: the first N values become N/2, lane l
+// keeping value 2i + hi of each pair and adding the other one from the lane
+// CTRL brings in, which differs from l in the bit that hi is taken from.
+template <int CTRL, int N, int R>
+__device__ __forceinline__ void rows_halve(float (&v)[R], bool hi) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = hi ? v[2 * i + 1] : v[2 * i];
+    const float send = hi ? v[2 * i] : v[2 * i + 1];
+    v[i] = keep + dpp_f<CTRL>(send);
+  }
+}
+
+// Sums over the 64 lanes of R values at once (R a power of two, <= 16):
+// lane l receives the sum of v[l % R].  Bits 0 .. log2(R) - 1 of the lane
+// number each halve the values (a quad swap for bits 0 and 1, a rotation by
+// 4 or 8 within the 16-lane row for bits 2 and 3: the lane rotated in
+// differs in that bit and agrees in the lower ones), so that each lane is
+// left with one partial sum, of value l % R; the other lane bits are summed
+// plainly, across rows with the 16- and 32-lane swaps.  Fixed order: the
+// same result on every run.  Leaves v clobbered.
+template <int R>
+__device__ __forceinline__ float rows_sum(float (&v)[R]) {
+  static_assert(R == 1 || R == 2 || R == 4 || R == 8 || R == 16, "R: a power of two up to 16");
+  const int lane = threadIdx.x & 63;
+  if constexpr (R >= 2) rows_halve<kDppQuadXor1, R>(v, lane & 1);
+  if constexpr (R >= 4) rows_halve<kDppQuadXor2, R / 2>(v, lane & 2);
+  if constexpr (R >= 8) rows_halve<kDppRowRor4, R / 4>(v, lane & 4);
+  if constexpr (R >= 16) rows_halve<kDppRowRor8, R / 8>(v, lane & 8);
+  float s = v[0];
+  if constexpr (R < 2) s += dpp_f<kDppQuadXor1>(s);
+  if constexpr (R < 4) s += dpp_f<kDppQuadXor2>(s);
+  if constexpr (R < 8) s += dpp_f<kDppRowRor4>(s);
+  if constexpr (R < 16) s += dpp_f<kDppRowRor8>(s);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Max of v over the lanes 4a..4a+3 of a quad, in every lane of the quad.
 __device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, dpp_f<kDppQuadXor1>(v));

@@ -167,6 +167,18 @@ def test_skewed_routing_many_tokens_per_expert(dev):
     assert rel_err(out, ref) <= TOL_GEMV
 
 
+@pytest.mark.parametrize("h,I", [(3072, 4096), (1024, 6144), (2048, 8192), (8192, 512), (512, 10240)])
+def test_larger_batch_row_widths(dev, h, I):
+    """T = 12 (above the small-batch path) at the widths that pick each
+    register-resident row width of the larger-batch kernels: gate/up rows of
+    2 and 1 chunks of 2048 columns per lane, down rows of 2, 3 and 4 chunks
+    (8, 4 and 4 rows a wave); and the streaming kernels past them (h = 8192
+    for gate/up, I = 10240 for down)."""
+    log(f"larger batch h={h} I={I} T=12")
+    shape = synth.LayerShape(hidden=h, n_experts=6, top_k=2, inter=I, n_shared=1, rsf=1.5, bias_sigma=0.02)
+    check_full(shape, 11, 12, dev)
+
+
 def test_all_codes_including_minus_eight(dev):
     """Codes drawn uniformly over all 256 byte values (so -8 appears) with
     random positive scales: the unpacking of every code is exercised."""
