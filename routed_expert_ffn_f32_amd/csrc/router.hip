@@ -113,6 +113,17 @@ __global__ __launch_bounds__(kDispatchThreads) void select_dispatch_kernel(
   dispatch_block(sel, T * k, E, offsets, sorted_ids, inv, active, n_active);
 }
 
+// Large batches: grid = ceil(T / 32) x ceil(E / 16) blocks (token groups
+// major) of 8 waves, logits only.
+__global__ __launch_bounds__(512) void router_logits_wide_kernel(const float *__restrict__ x,
+                                                                 const float *__restrict__ wrP, int T, int h, int E,
+                                                                 float *__restrict__ logits) {
+  __shared__ float4 xs[2][kWideT][64];
+  __shared__ float4 ws[2][kWideE][64];
+  const int egroups = (E + kWideE - 1) / kWideE;
+  logits_wide_tile(x, wrP, T, h, E, (blockIdx.x / egroups) * kWideT, (blockIdx.x % egroups) * kWideE, logits, xs, ws);
+}
+
 // One token: grid = ceil(E / 4) blocks of 4 waves, wave w of block b owns
 // expert 4b + w.  Every load of its chain (MB float4 blocks of the permuted
 // router, the token's h/64 values for this lane) is issued before the first
@@ -159,6 +170,9 @@ hipError_t launch_router_permute(const float *wr, float *wrP, int h, int E, hipS
 
 size_t router_permuted_floats(int h, int E) { return (size_t)E * ((((h >> 6) + 3) >> 2)) * 256; }
 
+// Batches from this size on take the wide tiles (enough blocks to fill the chip).
+constexpr int kWideMinT = 256;
+
 hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits, uint32_t *xq,
                                 float *xs, hipStream_t s) {
   if (T <= 0) return hipSuccess;
@@ -175,10 +189,15 @@ hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, 
   } else if (T < 64) {
     const int nlb = ((T + 3) / 4) * ((E + 7) / 8);
     return launch(router_logits_kernel<2, 4>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
-  } else {
+  } else if (T < kWideMinT) {
     const int nlb = ((T + 3) / 4) * ((E + 15) / 16);
     return launch(router_logits_kernel<4, 4>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
   }
+  // large batches: the wide tiles, then (GEMV path only) the digit planes
+  const unsigned nwb = (unsigned)(((T + kWideT - 1) / kWideT) * ((E + kWideE - 1) / kWideE));
+  hipError_t err = launch(router_logits_wide_kernel, nwb, 512, 0, s, x, wrP, T, h, E, logits);
+  if (err != hipSuccess || qblocks == 0) return err;
+  return launch(router_logits_kernel<4, 4>, qblocks, 256, 0, s, x, wrP, T, h, E, logits, 0, xq, xs);
 }
 
 hipError_t launch_router_select(const float *logits, const float *bias, int T, int E, int k, float rsf,

@@ -12,6 +12,7 @@
 #pragma once
 
 #include "internal.h"
+#include "wave.h"
 
 namespace coli {
 
@@ -148,6 +149,142 @@ __device__ __forceinline__ float logit_t1(const float *__restrict__ x, const flo
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) acc = acc + __shfl_xor(acc, d);
   return acc;
+}
+
+// The xor butterfly (32, 16, 8, 4, 2, 1) of 64 values at once, transposed:
+// each step pairs value i with value i + N/2 (N values left) and every lane
+// keeps the one its lane bit selects, adding the partner lane's partial of
+// it -- the same two partials the butterfly adds, so every sum is the
+// butterfly's, bit for bit.  Lane l ends with the full sum of value l.
+// Partners: the 32- and 16-lane swaps (each pairs two registers at once),
+// row_ror:8 (= xor 8 within a 16-lane row), the xor-4 swizzle, quad
+// permutations for xor 2 and 1.
+template <int CTRL>
+__device__ __forceinline__ float dpp_xf(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float butterfly64_transposed(float (&v)[64]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 32]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 16]), false, false);
+    v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float keep = b3 ? v[i + 8] : v[i], send = b3 ? v[i] : v[i + 8];
+    v[i] = keep + dpp_xf<0x128>(send);  // row_ror:8
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float keep = b2 ? v[i + 4] : v[i], send = b2 ? v[i] : v[i + 4];
+    v[i] = keep + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, send), 0x101F));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float keep = b1 ? v[i + 2] : v[i], send = b1 ? v[i] : v[i + 2];
+    v[i] = keep + dpp_xf<0x4E>(send);  // quad_perm [2,3,0,1]
+  }
+  const float keep = b0 ? v[1] : v[0], send = b0 ? v[0] : v[1];
+  return keep + dpp_xf<0xB1>(send);  // quad_perm [1,0,3,2]
+}
+
+// Large batches: a block of 8 waves computes kWideT tokens x kWideE experts
+// (kWideT * kWideE = 512), wave w the 8 x 8 pairs of token group
+// w / (kWideE / 8) and expert group w % (kWideE / 8); every lane holds its
+// chain partial of all 64 pairs.  Per block of 4 chain steps
+// the block stages the 32 token rows and the 16 router columns in LDS in
+// the lane-permuted order (a lane's 4 consecutive chain elements are one
+// 16-byte read), double-buffered, the next block's global loads in flight
+// during the current block's fmas.  Each fma is logits_tile's, element for
+// element, and the final butterfly runs transposed.
+constexpr int kWideT = 32, kWideE = 16;
+static_assert(kWideT * kWideE == 8 * 64 && kWideT % 8 == 0 && kWideE % 8 == 0, "8 waves of 8 x 8 pairs");
+
+__device__ __forceinline__ void logits_wide_tile(const float *__restrict__ x, const float *__restrict__ wrP, int T,
+                                                 int h, int E, int t0, int e0, float *__restrict__ logits,
+                                                 float4 (*xs)[kWideT][64], float4 (*ws)[kWideE][64]) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int XK = kWideT / 8, WK = kWideE / 8;  // staged rows per thread
+  const int tw = wave / WK, ew = wave % WK;
+  const int M = h >> 6, MB = (M + 3) >> 2;
+  // staging: this thread copies lane `lane` of tokens wave + 8 k (k < XK)
+  // and of experts wave + 8 k (k < WK); a token row's descriptor ends at its
+  // h columns, so chain steps past M read zeros without a branch
+  Rsrc xr[XK];
+  const float4 *wr[WK];
+#pragma unroll
+  for (int k = 0; k < XK; ++k) xr[k] = make_rsrc(x + (size_t)min(t0 + wave + 8 * k, T - 1) * h, (uint32_t)h * 4);
+#pragma unroll
+  for (int k = 0; k < WK; ++k)
+    wr[k] = reinterpret_cast<const float4 *>(wrP) + (size_t)min(e0 + wave + 8 * k, E - 1) * MB * 64 + lane;
+  // two register sets: block b + 2's loads are issued while block b is
+  // computed (one block of fmas is shorter than a load's latency here);
+  // past the last block they re-read it (unused)
+  float4 xv[2][XK], wv[2][WK];
+  auto load = [&](int b, int set) {
+    b = min(b, MB - 1);
+#pragma unroll
+    for (int k = 0; k < XK; ++k) {
+      float f[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = bloadf(xr[k], (uint32_t)(lane + 64 * (4 * b + i)) * 4, 0);
+      xv[set][k] = make_float4(f[0], f[1], f[2], f[3]);
+    }
+#pragma unroll
+    for (int k = 0; k < WK; ++k) wv[set][k] = wr[k][(size_t)b * 64];
+  };
+  float acc[64];
+#pragma unroll
+  for (int j = 0; j < 64; ++j) acc[j] = 0.0f;
+  auto step = [&](int b, int set) {
+#pragma unroll
+    for (int k = 0; k < XK; ++k) xs[set][wave + 8 * k][lane] = xv[set][k];
+#pragma unroll
+    for (int k = 0; k < WK; ++k) ws[set][wave + 8 * k][lane] = wv[set][k];
+    __syncthreads();  // block b staged; every wave past block b - 1's reads of the other buffer
+    load(b + 2, set);
+    float4 a[8], c[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) a[t] = xs[set][8 * tw + t][lane];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = ws[set][8 * ew + e][lane];
+    auto fmas = [&](int i) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float xa = i == 0 ? a[t].x : i == 1 ? a[t].y : i == 2 ? a[t].z : a[t].w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float wc = i == 0 ? c[e].x : i == 1 ? c[e].y : i == 2 ? c[e].z : c[e].w;
+          acc[8 * t + e] = __builtin_fmaf(xa, wc, acc[8 * t + e]);
+        }
+      }
+    };
+    if (4 * b + 4 <= M) {  // a full block: no per-step guard, so the reads are hoisted
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fmas(i);
+    } else {  // the chain's last, partial block: its steps past M are skipped
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (4 * b + i < M) fmas(i);
+    }
+  };
+  load(0, 0);
+  load(1, 1);
+  for (int b = 0; b < MB; b += 2) {
+    step(b, 0);
+    if (b + 1 < MB) step(b + 1, 1);
+  }
+  const float sum = butterfly64_transposed(acc);
+  const int t = t0 + 8 * tw + (lane >> 3), e = e0 + 8 * ew + (lane & 7);
+  if (t < T && e < E) logits[(size_t)t * E + e] = sum;
 }
 
 }  // namespace coli

@@ -179,6 +179,18 @@ def test_larger_batch_row_widths(dev, h, I):
     check_full(shape, 11, 12, dev)
 
 
+def test_router_wide_tiles_ragged(dev):
+    """T = 300 takes the router's wide tiles (32 tokens x 16 experts per
+    block) with every edge ragged: T not a multiple of 32, E = 20 not a
+    multiple of 16, h = 320 (5 chain steps per lane, a partial 4-step
+    block).  Routing weights must match the oracle bit for bit, which needs
+    each logit's fma chain and butterfly unchanged; h = 320 keeps the call
+    on the GEMV path, so the digit-plane launch that follows runs too."""
+    log("router wide tiles T=300 E=20 h=320")
+    shape = synth.LayerShape(hidden=320, n_experts=20, top_k=3, inter=128, n_shared=1, rsf=2.5, bias_sigma=0.05)
+    check_full(shape, 31, 300, dev)
+
+
 def test_all_codes_including_minus_eight(dev):
     """Codes drawn uniformly over all 256 byte values (so -8 appears) with
     random positive scales: the unpacking of every code is exercised."""
