@@ -183,21 +183,27 @@ hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, 
     if (h == 4096) return launch(router_logits_t1_kernel<16>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs);
     return launch(router_logits_t1_kernel<24>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs);
   }
-  if (T < 4) {
+  // tiles per wave (experts x tokens) by batch size, measured on the GLM-like
+  // layer (h = 6144, E = 256): the smallest tiles while they give the chip
+  // enough waves, larger ones as the batch grows
+  if (T < 12) {
     const int nlb = T * ((E + 3) / 4);
     return launch(router_logits_kernel<1, 1>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
-  } else if (T < 64) {
+  } else if (T < 24) {
+    const int nlb = ((T + 1) / 2) * ((E + 3) / 4);
+    return launch(router_logits_kernel<1, 2>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
+  } else if (T < 48) {
+    const int nlb = ((T + 1) / 2) * ((E + 7) / 8);
+    return launch(router_logits_kernel<2, 2>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
+  } else if (T < kWideMinT) {
     const int nlb = ((T + 3) / 4) * ((E + 7) / 8);
     return launch(router_logits_kernel<2, 4>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
-  } else if (T < kWideMinT) {
-    const int nlb = ((T + 3) / 4) * ((E + 15) / 16);
-    return launch(router_logits_kernel<4, 4>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
   }
   // large batches: the wide tiles, then (GEMV path only) the digit planes
   const unsigned nwb = (unsigned)(((T + kWideT - 1) / kWideT) * ((E + kWideE - 1) / kWideE));
   hipError_t err = launch(router_logits_wide_kernel, nwb, 512, 0, s, x, wrP, T, h, E, logits);
   if (err != hipSuccess || qblocks == 0) return err;
-  return launch(router_logits_kernel<4, 4>, qblocks, 256, 0, s, x, wrP, T, h, E, logits, 0, xq, xs);
+  return launch(router_logits_kernel<2, 4>, qblocks, 256, 0, s, x, wrP, T, h, E, logits, 0, xq, xs);
 }
 
 hipError_t launch_router_select(const float *logits, const float *bias, int T, int E, int k, float rsf,
