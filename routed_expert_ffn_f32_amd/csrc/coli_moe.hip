@@ -238,24 +238,30 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
     return coli::launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill ? nullptr : xq, xs, s);
   });
   if (e != hipSuccess) return COLI_MOE_EDEVICE;
-  if (prefill) {
-    // 2. selection and dispatch, 3. bf16 activations and the tile list,
-    // 4. grouped GEMMs on MFMA, 5. weighted combine
-    if ((int64_t)T * k <= coli::kFusedDispatchMax) {
-      e = timed(m, K_ROUTER_SELECT, s, [&] {
+  // Selection and dispatch: one workgroup does both while each of its waves
+  // selects at most one token (its counting sort then reads the choices from
+  // LDS); larger batches select one token per wave over many workgroups,
+  // then sort in a launch of their own.
+  auto select_and_dispatch = [&]() -> hipError_t {
+    if (T <= coli::kDispatchThreads / coli::kWave) {
+      static_assert(coli::kDispatchThreads / coli::kWave * coli::kMaxTopK <= coli::kFusedDispatchMax,
+                    "the fused launch's LDS holds every choice");
+      return timed(m, K_ROUTER_SELECT, s, [&] {
         return coli::launch_select_dispatch(logits, bias, T, E, k, rsf, idx, wsel, offsets, sorted_ids, inv,
                                             active, n_active, s);
       });
-      if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    } else {
-      e = timed(m, K_ROUTER_SELECT, s,
-                [&] { return coli::launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
-      if (e != hipSuccess) return COLI_MOE_EDEVICE;
-      e = timed(m, K_DISPATCH, s, [&] {
-        return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
-      });
-      if (e != hipSuccess) return COLI_MOE_EDEVICE;
     }
+    hipError_t err = timed(m, K_ROUTER_SELECT, s,
+                           [&] { return coli::launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
+    if (err != hipSuccess) return err;
+    return timed(m, K_DISPATCH, s, [&] {
+      return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
+    });
+  };
+  if (prefill) {
+    // 2. selection and dispatch, 3. bf16 activations and the tile list,
+    // 4. grouped GEMMs on MFMA, 5. weighted combine
+    if (select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
     coli::PrefillProblem Q{};
     Q.gate = {m->w.gate_q, m->w.gate_s};
     Q.up = {m->w.up_q, m->w.up_s};
@@ -336,22 +342,8 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
     e = timed(m, K_DOWN, s, [&] { return coli::launch_down_combine(P, out, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
   } else {
-    // 2. selection and dispatch (one workgroup up to kFusedDispatchMax assignments)
-    if ((int64_t)T * k <= coli::kFusedDispatchMax) {
-      e = timed(m, K_ROUTER_SELECT, s, [&] {
-        return coli::launch_select_dispatch(logits, bias, T, E, k, rsf, idx, wsel, offsets, sorted_ids, inv,
-                                            active, n_active, s);
-      });
-      if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    } else {
-      e = timed(m, K_ROUTER_SELECT, s,
-                [&] { return coli::launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
-      if (e != hipSuccess) return COLI_MOE_EDEVICE;
-      e = timed(m, K_DISPATCH, s, [&] {
-        return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
-      });
-      if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    }
+    // 2. selection and dispatch
+    if (select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
     // 3. gate/up, down, weighted combine
     e = timed(m, K_GATE_UP, s, [&] { return coli::launch_gemv_gate_up(P, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
