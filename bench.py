@@ -134,6 +134,44 @@ def kernel_profile(cm, handles, run, n_calls):
     return {n: (ms, c) for n, (ms, c) in kern.items() if c}
 
 
+def measured_peaks(cm, torch, dev):
+    """This GPU's own rates, measured in the same run with the library's
+    probes, beside the published peaks: the HBM read rate over an 8 GiB
+    buffer (every byte read once) and the back-to-back bf16 MFMA rate (one
+    wave per SIMD on every CU); each the best of five launches timed with
+    HIP events, each probe's result checked."""
+    stream = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def best_ms(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return min(out)
+
+    nbytes = 8 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    hbm_ms = best_ms(lambda: cm.coli_moe_probe_stream(buf.data_ptr(), nbytes, sink.data_ptr(), stream))
+    del buf
+    blocks, iters = 256, 40000
+    sink.zero_()
+    mfma_ms = best_ms(lambda: cm.coli_moe_probe_mfma(iters, blocks, sink.data_ptr(), stream))
+    torch.cuda.synchronize()
+    waves_ok = int(sink.item())
+    flops = blocks * 4 * iters * cm.MFMA_PROBE_MFMAS_PER_ROUND * 32768
+    return {"hbm_read_GBps": round(nbytes / (hbm_ms / 1e3) / 1e9, 1), "hbm_buffer_bytes": nbytes,
+            "mfma_bf16_TFLOPs": round(flops / (mfma_ms / 1e3) / 1e12, 1),
+            "mfma_probe_waves_checked": f"{waves_ok} of {6 * blocks * 4}",
+            "published": {"hbm_GBps": HBM_PEAK_GBPS, "bf16_dense_TFLOPs": BF16_PEAK_TFLOPS}}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -279,7 +317,22 @@ def main():
                          "us_per_launch": round(probe_us, 3), "GBps": round(probe_bytes / probe_us / 1e3, 1),
                          "dominant_kernel_time_over_probe": round(1e6 * dom_avg_s / probe_us, 4)},
     }
+    # per-step times of the same stack (a separate loop, one event per step)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    evs[0].record()
+    for s in range(K):
+        run_stack(xs, outs, W + s, 1)
+        evs[s + 1].record()
+    torch.cuda.synchronize()
+    st = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(K))
+    result["step_ms_percentiles"] = {"p10": round(st[K // 10], 5), "p50": round(st[K // 2], 5),
+                                     "p90": round(st[min(K - 1, (9 * K) // 10)], 5)}
     del xs, outs
+
+    # ---- this GPU's own peak rates --------------------------------------------
+    peaks = measured_peaks(cm, torch, dev)
+    peaks["dominant_kernel_frac_of_measured_hbm"] = round(achieved / peaks["hbm_read_GBps"], 4)
+    result["measured_peaks"] = peaks
 
     # ---- decode batches on the same stack ----------------------------------
     if batches:
@@ -303,6 +356,8 @@ def main():
     # ---- prefill on its own layer ------------------------------------------
     if not args.no_extra:
         result["prefill"] = prefill(args, cm, torch, np, synth, dev)
+        result["prefill"]["mfma_gemm_frac_of_measured_mfma"] = round(
+            result["prefill"]["mfma_gemm_tflops"] / peaks["mfma_bf16_TFLOPs"], 4)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, shape, layers, dev)
@@ -384,8 +439,14 @@ def cpu_baseline(args, shape, layers, dev):
         rms = np.sqrt((r ** 2).mean(axis=-1, keepdims=True))
         worst = max(worst, float((np.abs(got - r) / np.maximum(np.abs(r), rms)).max()))
         done += 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(done / spent, 4), "unit": "tokens/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{done} decode calls of T=1 on layer 0 (routing + 8 routed + shared expert "
                       f"FFNs in float64), {spent:.1f} s",
             "gpu_max_rel_err_on_sample": worst}

@@ -181,6 +181,26 @@ int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, 
 int coli_moe_probe_read(const coli_moe_t *m, const int32_t *experts, int32_t n, void *stream);
 
 /*
+ * Measurement only: the rates this GPU reaches, for setting the layer's
+ * figures against them (no handle needed).
+ *
+ * coli_moe_probe_stream reads every byte of the DEVICE buffer buf [bytes]
+ * once (16-byte loads, bytes a multiple of 16, buf 16-byte aligned) and
+ * XORs all its 32-bit words into the DEVICE word *sink (the caller clears
+ * it first; the result does not depend on the order of reads).
+ *
+ * coli_moe_probe_mfma runs `blocks` blocks of 4 waves, each wave `iters`
+ * rounds of 8 back-to-back v_mfma_f32_32x32x16_bf16 (32768 flops each) on
+ * all-ones operands; each wave whose results all equal 16 * iters adds 1 to
+ * the DEVICE word *sink.  1 <= iters < 2^20, 1 <= blocks <= 2^20.
+ *
+ * Both only enqueue on `stream`.  Errors: -4 NULL/misaligned pointer or a
+ * size out of range, -3 HIP launch error.
+ */
+int coli_moe_probe_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+int coli_moe_probe_mfma(int32_t iters, int32_t blocks, uint32_t *sink, void *stream);
+
+/*
  * Kernel timing.  coli_moe_profile_begin makes the next `max_calls` forwards
  * of the handle record a HIP event pair around each kernel they launch (host
  * allocations only; events are created here).  coli_moe_profile_end waits

@@ -77,6 +77,10 @@ def load_library():
         L.coli_moe_test_dispatch.restype = ctypes.c_int
         L.coli_moe_probe_read.argtypes = [vp, vp, i32, vp]
         L.coli_moe_probe_read.restype = ctypes.c_int
+        L.coli_moe_probe_stream.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.coli_moe_probe_stream.restype = ctypes.c_int
+        L.coli_moe_probe_mfma.argtypes = [i32, i32, vp, vp]
+        L.coli_moe_probe_mfma.restype = ctypes.c_int
         L.coli_moe_profile_begin.argtypes = [vp, i32]
         L.coli_moe_profile_begin.restype = ctypes.c_int
         L.coli_moe_profile_end.argtypes = [vp, vp, vp]
@@ -140,6 +144,21 @@ def coli_moe_probe_read(handle, experts: int, n: int, stream: int = 0) -> int:
     """Pure-load probe of the gate/up rows of n experts (device int32 ids, -1
     = shared): the read ceiling of the gate/up access pattern."""
     return _check(load_library().coli_moe_probe_read(handle, experts, int(n), stream), "coli_moe_probe_read")
+
+
+def coli_moe_probe_stream(buf: int, nbytes: int, sink: int, stream: int = 0) -> int:
+    """XOR of every 32-bit word of a device buffer into the device word at
+    sink, each byte read once (the HBM read rate of this GPU)."""
+    return _check(load_library().coli_moe_probe_stream(buf, int(nbytes), sink, stream), "coli_moe_probe_stream")
+
+
+MFMA_PROBE_MFMAS_PER_ROUND = 8
+
+
+def coli_moe_probe_mfma(iters: int, blocks: int, sink: int, stream: int = 0) -> int:
+    """blocks x 4 waves of iters x 8 back-to-back bf16 MFMAs (32768 flops
+    each); each wave whose results check adds 1 to the device word at sink."""
+    return _check(load_library().coli_moe_probe_mfma(int(iters), int(blocks), sink, stream), "coli_moe_probe_mfma")
 
 
 def coli_moe_profile_begin(handle, max_calls: int) -> int:

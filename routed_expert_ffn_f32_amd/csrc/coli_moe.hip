@@ -424,6 +424,21 @@ int coli_moe_probe_read(const coli_moe_t *mc, const int32_t *experts, int32_t n,
   return COLI_MOE_OK;
 }
 
+int coli_moe_probe_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4)) return COLI_MOE_EARG;
+  return coli::launch_stream_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? COLI_MOE_OK
+             : COLI_MOE_EDEVICE;
+}
+
+int coli_moe_probe_mfma(int32_t iters, int32_t blocks, uint32_t *sink, void *stream) {
+  if (!sink || !aligned(sink, 4) || iters < 1 || iters >= (1 << 20) || blocks < 1 || blocks > (1 << 20))
+    return COLI_MOE_EARG;
+  return coli::launch_mfma_probe(iters, blocks, sink, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? COLI_MOE_OK
+             : COLI_MOE_EDEVICE;
+}
+
 int coli_moe_profile_begin(coli_moe_t *m, int32_t max_calls) {
   if (!m || max_calls < 0) return COLI_MOE_EARG;
   const size_t need = (size_t)max_calls * COLI_MOE_N_KERNELS;

@@ -121,6 +121,13 @@ hipError_t launch_gemv_gate_up(const DecodeProblem &P, hipStream_t s);
 // Read probe: the gate and up rows of n experts (device ids, -1 = shared;
 // h <= 8192) with pure loads and the small-batch gate/up launch shape; sink
 // receives at most one word.
+// Measurement probes (probes.hip): XOR of every word of a device buffer
+// (bytes a multiple of 16) into *sink; back-to-back bf16 MFMAs, `blocks`
+// blocks of 4 waves, each wave adding 1 to *sink when its results check.
+constexpr int kProbeStreamBlocks = 256 * 8;
+constexpr int kMfmaChains = 8;  // MFMAs per round of the MFMA probe
+hipError_t launch_stream_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_mfma_probe(int iters, int blocks, uint32_t *sink, hipStream_t s);
 hipError_t launch_read_probe(const DecodeProblem &P, const int32_t *experts, int n, uint32_t *sink,
                              hipStream_t s);
 // Small batches: out[t] = sum_j w[t,j] Wd_e mid[inv(t,j)] + Wd_sh mid[T*k + t].

@@ -97,6 +97,16 @@ def test_forward_and_dispatch_argument_errors():
     assert lib.coli_moe_test_dispatch(0x1000, 4, 0, 8, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
     assert lib.coli_moe_test_dispatch(0x1000, 4, 2, 513, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
     assert lib.coli_moe_probe_read(None, 0x1000, 9, None) == -4
+    # measurement probes: every bad argument is refused before any launch
+    assert lib.coli_moe_probe_stream(None, 1024, 0x2000, None) == -4
+    assert lib.coli_moe_probe_stream(0x1000, 1000, 0x2000, None) == -4   # not a multiple of 16
+    assert lib.coli_moe_probe_stream(0x1008, 1024, 0x2000, None) == -4   # buffer not 16-byte aligned
+    assert lib.coli_moe_probe_stream(0x1000, 0, 0x2000, None) == -4
+    assert lib.coli_moe_probe_stream(0x1000, 1024, None, None) == -4
+    assert lib.coli_moe_probe_mfma(0, 4, 0x2000, None) == -4
+    assert lib.coli_moe_probe_mfma(1 << 20, 4, 0x2000, None) == -4
+    assert lib.coli_moe_probe_mfma(10, 0, 0x2000, None) == -4
+    assert lib.coli_moe_probe_mfma(10, 4, None, None) == -4
     assert lib.coli_moe_test_dispatch(0x1000, -1, 2, 8, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
     assert lib.coli_moe_test_dispatch(None, 4, 2, 8, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
     lib.coli_moe_free(None)  # no-op

@@ -191,6 +191,28 @@ def test_router_wide_tiles_ragged(dev):
     check_full(shape, 31, 300, dev)
 
 
+def test_measurement_probes(dev):
+    """The probes bench.py measures the GPU's own rates with do their work:
+    the stream probe's XOR of a 64 MiB + 48 B buffer (not a multiple of
+    its grid stride) equals numpy's, so every word was read exactly once;
+    every wave of the MFMA probe finds all its accumulators at 16 x iters."""
+    import routed_expert_ffn_f32_amd as cm
+    log("measurement probes")
+    stream = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(5)
+    words = (64 << 20) // 4 + 12
+    host = rng.integers(0, 2**32, size=words, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to(dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cm.coli_moe_probe_stream(buf.data_ptr(), words * 4, sink.data_ptr(), stream)
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(host))
+    sink.zero_()
+    cm.coli_moe_probe_mfma(1000, 96, sink.data_ptr(), stream)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 96 * 4
+
+
 def test_all_codes_including_minus_eight(dev):
     """Codes drawn uniformly over all 256 byte values (so -8 appears) with
     random positive scales: the unpacking of every code is exercised."""
