@@ -262,6 +262,23 @@ def test_token_counts_on_one_handle(dev):
     assert ei.value.code == -1
 
 
+def test_kernel_choice_boundaries_on_one_handle(dev):
+    """One GEMV-path handle (h = 320 is not a multiple of 256, so no MFMA
+    path at any T) at the batch sizes on both sides of every switch between
+    kernels: the small-batch kernels (T <= 4), the router's tile sizes (12,
+    24, 48, 256), selection and sort in one workgroup (T <= 16).  Routing
+    bit-exact and outputs against the oracle at each."""
+    log("kernel choice boundaries")
+    shape = synth.LayerShape(hidden=320, n_experts=24, top_k=4, inter=192, n_shared=1, rsf=2.5, bias_sigma=0.05)
+    L = DeviceLayer(shape, 41, 0, dev, max_tokens=300, keep_host=True)
+    for T in (4, 5, 11, 12, 16, 17, 23, 24, 47, 48, 255, 256, 300):
+        x = synth.hidden(shape, 41, T, batch=T)
+        out = run(L, x, dev)
+        assert_routing_matches(L, x, T)
+        ref, _, _ = L.oracle_forward(x)
+        assert rel_err(out, ref) <= TOL_GEMV, T
+
+
 def test_two_runs_bitwise_identical(dev):
     log("determinism")
     shape = synth.OLMOE
