@@ -279,6 +279,39 @@ def test_kernel_choice_boundaries_on_one_handle(dev):
         assert rel_err(out, ref) <= TOL_GEMV, T
 
 
+@pytest.mark.parametrize("path", ["small_batch", "token_rows", "mfma"])
+def test_outlier_channels_and_zero_rows(dev, path):
+    """Hidden rows of three kinds in one batch: N(0,1); all zeros (every
+    logit 0, so the selection falls to the bias, and the output must be
+    exactly 0); N(0,1) with four massive-activation channels at +-300 (one
+    32-column block of the digit-plane format then spans five orders of
+    magnitude).  Routing bit-exact for every row, zero rows exactly zero,
+    the rest against the oracle at the path's bound."""
+    log(f"outlier channels and zero rows, {path}")
+    if path == "mfma":
+        shape, T, thr = MID, 300, 64
+    else:
+        shape = synth.LayerShape(hidden=320, n_experts=24, top_k=4, inter=192, n_shared=1, rsf=2.5, bias_sigma=0.05)
+        T, thr = (3, 0) if path == "small_batch" else (20, 0)
+    L = DeviceLayer(shape, 51, 0, dev, max_tokens=T, prefill_threshold=thr, keep_host=True)
+    x = synth.hidden(shape, 51, T, batch=77)
+    x[1::3] = 0.0
+    ch = [3, 77, 150, shape.hidden - 1]
+    x[2::3, ch] = np.where(x[2::3, ch] < 0, -300.0, 300.0).astype(np.float32)
+    out = run(L, x, dev)
+    assert_routing_matches(L, x, T)
+    zero = np.all(x == 0.0, axis=1)
+    assert zero.sum() == len(range(1, T, 3))
+    assert np.all(out[zero] == 0.0)
+    ref, _, _ = L.oracle_forward(x[~zero])
+    if path == "mfma":
+        assert_mfma_close(out[~zero], ref, "outliers: ")
+    else:
+        err = rel_err(out[~zero], ref)
+        log(f"  rel err {err:.3e}")
+        assert err <= TOL_GEMV, err
+
+
 def test_two_runs_bitwise_identical(dev):
     log("determinism")
     shape = synth.OLMOE
