@@ -113,9 +113,9 @@ __global__ __launch_bounds__(kDispatchThreads) void select_dispatch_kernel(
   dispatch_block(sel, T * k, E, offsets, sorted_ids, inv, active, n_active);
 }
 
-// Large batches: grid = ceil(T / 32) x ceil(E / 16) blocks (token groups
-// major) of 8 waves, logits only.
-__global__ __launch_bounds__(512) void router_logits_wide_kernel(const float *__restrict__ x,
+// Large batches: grid = ceil(T / kWideT) x ceil(E / kWideE) blocks (token
+// groups major) of kWideWaves waves, logits only.
+__global__ __launch_bounds__(kWideWaves * 64) void router_logits_wide_kernel(const float *__restrict__ x,
                                                                  const float *__restrict__ wrP, int T, int h, int E,
                                                                  float *__restrict__ logits) {
   __shared__ float4 xs[2][kWideT][64];
@@ -201,7 +201,7 @@ hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, 
   }
   // large batches: the wide tiles, then (GEMV path only) the digit planes
   const unsigned nwb = (unsigned)(((T + kWideT - 1) / kWideT) * ((E + kWideE - 1) / kWideE));
-  hipError_t err = launch(router_logits_wide_kernel, nwb, 512, 0, s, x, wrP, T, h, E, logits);
+  hipError_t err = launch(router_logits_wide_kernel, nwb, kWideWaves * 64, 0, s, x, wrP, T, h, E, logits);
   if (err != hipSuccess || qblocks == 0) return err;
   return launch(router_logits_kernel<2, 4>, qblocks, 256, 0, s, x, wrP, T, h, E, logits, 0, xq, xs);
 }

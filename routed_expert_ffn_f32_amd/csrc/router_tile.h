@@ -196,9 +196,9 @@ __device__ __forceinline__ float butterfly64_transposed(float (&v)[64]) {
   return keep + dpp_xf<0xB1>(send);  // quad_perm [1,0,3,2]
 }
 
-// Large batches: a block of 8 waves computes kWideT tokens x kWideE experts
-// (kWideT * kWideE = 512), wave w the 8 x 8 pairs of token group
-// w / (kWideE / 8) and expert group w % (kWideE / 8); every lane holds its
+// Large batches: a block of kWideWaves waves computes kWideT tokens x kWideE
+// experts (kWideT * kWideE = 64 kWideWaves), wave w the 8 x 8 pairs of token
+// group w / (kWideE / 8) and expert group w % (kWideE / 8); every lane holds its
 // chain partial of all 64 pairs.  Per block of 4 chain steps
 // the block stages the 32 token rows and the 16 router columns in LDS in
 // the lane-permuted order (a lane's 4 consecutive chain elements are one
@@ -206,25 +206,27 @@ __device__ __forceinline__ float butterfly64_transposed(float (&v)[64]) {
 // during the current block's fmas.  Each fma is logits_tile's, element for
 // element, and the final butterfly runs transposed.
 constexpr int kWideT = 32, kWideE = 16;
-static_assert(kWideT * kWideE == 8 * 64 && kWideT % 8 == 0 && kWideE % 8 == 0, "8 waves of 8 x 8 pairs");
+constexpr int kWideWaves = kWideT * kWideE / 64;
+static_assert(kWideT % 8 == 0 && kWideE % 8 == 0 && kWideT % kWideWaves == 0 && kWideE % kWideWaves == 0,
+              "waves of 8 x 8 pairs; every thread stages the same number of rows");
 
 __device__ __forceinline__ void logits_wide_tile(const float *__restrict__ x, const float *__restrict__ wrP, int T,
                                                  int h, int E, int t0, int e0, float *__restrict__ logits,
                                                  float4 (*xs)[kWideT][64], float4 (*ws)[kWideE][64]) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr int XK = kWideT / 8, WK = kWideE / 8;  // staged rows per thread
+  constexpr int NW = kWideWaves, XK = kWideT / NW, WK = kWideE / NW;  // staged rows per thread
   const int tw = wave / WK, ew = wave % WK;
   const int M = h >> 6, MB = (M + 3) >> 2;
-  // staging: this thread copies lane `lane` of tokens wave + 8 k (k < XK)
-  // and of experts wave + 8 k (k < WK); a token row's descriptor ends at its
+  // staging: this thread copies lane `lane` of tokens wave + NW k (k < XK)
+  // and of experts wave + NW k (k < WK); a token row's descriptor ends at its
   // h columns, so chain steps past M read zeros without a branch
   Rsrc xr[XK];
   const float4 *wr[WK];
 #pragma unroll
-  for (int k = 0; k < XK; ++k) xr[k] = make_rsrc(x + (size_t)min(t0 + wave + 8 * k, T - 1) * h, (uint32_t)h * 4);
+  for (int k = 0; k < XK; ++k) xr[k] = make_rsrc(x + (size_t)min(t0 + wave + NW * k, T - 1) * h, (uint32_t)h * 4);
 #pragma unroll
   for (int k = 0; k < WK; ++k)
-    wr[k] = reinterpret_cast<const float4 *>(wrP) + (size_t)min(e0 + wave + 8 * k, E - 1) * MB * 64 + lane;
+    wr[k] = reinterpret_cast<const float4 *>(wrP) + (size_t)min(e0 + wave + NW * k, E - 1) * MB * 64 + lane;
   // two register sets: block b + 2's loads are issued while block b is
   // computed (one block of fmas is shorter than a load's latency here);
   // past the last block they re-read it (unused)
@@ -246,9 +248,9 @@ __device__ __forceinline__ void logits_wide_tile(const float *__restrict__ x, co
   for (int j = 0; j < 64; ++j) acc[j] = 0.0f;
   auto step = [&](int b, int set) {
 #pragma unroll
-    for (int k = 0; k < XK; ++k) xs[set][wave + 8 * k][lane] = xv[set][k];
+    for (int k = 0; k < XK; ++k) xs[set][wave + NW * k][lane] = xv[set][k];
 #pragma unroll
-    for (int k = 0; k < WK; ++k) ws[set][wave + 8 * k][lane] = wv[set][k];
+    for (int k = 0; k < WK; ++k) ws[set][wave + NW * k][lane] = wv[set][k];
     __syncthreads();  // block b staged; every wave past block b - 1's reads of the other buffer
     load(b + 2, set);
     float4 a[8], c[8];
