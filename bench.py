@@ -40,7 +40,7 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_gemv_gate_up.txt")
 # sources of the dominant kernel: a counter summary taken on other sources
-# does not describe this build
+# describes other code
 TRAFFIC_SOURCES = ["routed_expert_ffn_f32_amd/csrc/expert_gemv.hip", "routed_expert_ffn_f32_amd/csrc/wave.h",
                    "routed_expert_ffn_f32_amd/csrc/select.h", "routed_expert_ffn_f32_amd/csrc/internal.h"]
 
@@ -176,7 +176,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one MI355X: this build has no multi-GPU path "
+        print("bench.py measures one MI355X: the library has no multi-GPU path "
               "(--gpus must be 1; see the sharding notes of the design).", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:

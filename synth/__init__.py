@@ -10,7 +10,7 @@ Every tensor is its own stream, named by (seed, tag) with
 tag = layer << 40 | kind << 32 | index, so any tensor (say one expert of one
 layer) can be regenerated alone, in any order, on any host.
 
-The workloads follow the five synthetic layer configurations of the task:
+The workloads are five synthetic layer configurations:
 weights N(0, 0.02) before int4 gs64 quantisation, router N(0, 0.02), hidden
 states N(0, 1); selection bias N(0, sigma_b) (0.01 tiny, 0 for the OLMoE-like
 layer with uniform selection, 0.05 GLM-like), plus for the prefill workload a
