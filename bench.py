@@ -289,6 +289,23 @@ def main():
     probe_us = 1e3 * probe_ms / (K * L)
     probe_bytes = mean_experts * gate_up_w
 
+    # every decode kernel's algorithmic bytes and rate: the router (f32 table
+    # and the token row, the digit planes written), gate/up (above), down with
+    # the combine (the experts' down codes and scales, the intermediate rows,
+    # the output row)
+    down_w = h * (I // 2 + 4 * I // 64)
+    per_kernel_bytes = {
+        "router_logits": E * h * 4 + T * h * 4 + T * (6 * h // 8 + h // 32) * 4,
+        dom_name: dom_bytes,
+        "expert_gemv_down": mean_experts * down_w + (T * k + T * shape.n_shared) * I * 4 + T * h * 4,
+    }
+    kernel_rates = {}
+    for name, nbytes in per_kernel_bytes.items():
+        ms, n = kern.get(name, (0.0, 0))
+        if n:
+            us = 1e3 * ms / n
+            kernel_rates[name] = {"bytes": int(nbytes), "us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1)}
+
     result = {
         "metric": "MoE-layer tokens/s + expert-weight HBM GB/s (int4 gs64, decode T=1)",
         "value": round(tok_per_s, 1),
@@ -309,6 +326,7 @@ def main():
         "expert_weight_frac_of_hbm_peak": round(expert_gbps / HBM_PEAK_GBPS, 4),
         "us_per_layer_call": round(1e3 * total_ms / (K * L), 3),
         "kernel_avg_us": kern_us,
+        "kernel_rates": kernel_rates,
         "roofline": {"kernel": dom_name, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic),
