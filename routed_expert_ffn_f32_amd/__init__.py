@@ -19,9 +19,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# COLI_MOE_LIB may name another build of the same library (e.g. a tuning
-# variant); by default the in-tree build is loaded.
-LIB_PATH = os.environ.get("COLI_MOE_LIB") or os.path.join(_HERE, "_lib", "libcoli_moe.so")
+# The in-tree build (routed_expert_ffn_f32_amd/build.py), and only that.
+LIB_PATH = os.path.join(_HERE, "_lib", "libcoli_moe.so")
 
 COLI_MOE_OK = 0
 COLI_MOE_ECAPACITY = -1

@@ -35,8 +35,8 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, obj: str, extra=()) -> None:
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, obj: str) -> None:
+    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -46,16 +46,15 @@ def _compile(src: str, obj: str, extra=()) -> None:
         sys.stderr.write("\n".join(noise) + "\n")
 
 
-def build(verbose: bool = False, out: str = LIB, defines=(), objdir: str = "") -> str:
-    """Compile every source for gfx950 and link the shared library (`defines`
-    are extra -D options, for tuning builds written elsewhere)."""
-    objdir = objdir or os.path.join(HERE, "_build")
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link the shared library in-tree."""
+    out = LIB
+    objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     os.makedirs(os.path.dirname(out), exist_ok=True)
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    extra = [f"-D{d}" for d in defines]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], extra), zip(SOURCES, objs)))
+        list(ex.map(lambda so: _compile(so[0], so[1]), zip(SOURCES, objs)))
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -34,7 +34,7 @@ enum Kernel {
 const char *const kKernelNames[COLI_MOE_N_KERNELS] = {
     "router_logits",    "router_select_dispatch", "dispatch",            "expert_gemv_gate_up",
     "expert_gemv_down", "combine",                "expert_mfma_gate_up", "expert_mfma_down",
-    "prefill_to_bf16",  "build_tiles"};
+    "prefill_to_half",  "build_tiles"};
 // (small batches: "expert_gemv_down" is the down projection fused with the combine)
 
 constexpr size_t kAlign = 256;
@@ -43,12 +43,12 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // Byte offsets of the workspace regions.
 struct Layout {
   size_t wrP, logits, xq, xs, idx, w, offsets, sorted_ids, inv, active, n_active, mq, ms, midf, y;
-  size_t xb, midb, tiles, n_tiles;  // prefill path
+  size_t xb, xexp, xn2, midb, pstats, tiles, n_tiles;  // prefill path
   size_t queues;                    // row queues of the small-batch gate/up launch
   size_t total;
 };
 
-// The prefill (MFMA) path takes h and I multiples of 256, and bf16
+// The prefill (MFMA) path takes h and I multiples of 256, and half
 // activation buffers ([max_tokens][h] and [P][I]) under 4 GiB, since its
 // copies address them with 32-bit offsets; T below the threshold, or other
 // shapes, take the GEMV path.
@@ -56,6 +56,11 @@ bool prefill_shape(const coli_moe_config_t &c) {
   const uint64_t T = (uint64_t)c.max_tokens, P = T * (uint64_t)(c.top_k + (c.n_shared ? 1 : 0));
   return coli::prefill_shape_ok(c.hidden, c.inter) && T * (uint64_t)c.hidden * 2 < (1ull << 32) &&
          P * (uint64_t)c.inter * 2 < (1ull << 32);
+}
+
+// True when the handle's workspace holds the prefill buffers.
+bool prefill_enabled(const coli_moe_config_t &c) {
+  return prefill_shape(c) && (c.prefill_threshold == 0 ? 256 : c.prefill_threshold) <= c.max_tokens;
 }
 
 bool config_ok(const coli_moe_config_t &c, int *code) {
@@ -99,10 +104,13 @@ Layout layout_of(const coli_moe_config_t &c) {
   L.ms = o;         o = align_up(o + P * (I / 32) * 4);
   L.midf = o;       o = align_up(o + P * I * 4);
   L.y = o;          o = align_up(o + P * h * 4);
-  const bool pre = prefill_shape(c) && (c.prefill_threshold == 0 ? 256 : c.prefill_threshold) <= c.max_tokens;
+  const bool pre = prefill_enabled(c);
   const size_t tiles = pre ? (size_t)coli::prefill_max_tiles(c.max_tokens, c.top_k, c.n_experts, c.n_shared) : 0;
   L.xb = o;         o = align_up(o + (pre ? T * h * 2 : 0));
+  L.xexp = o;       o = align_up(o + (pre ? T * 4 : 0));
+  L.xn2 = o;        o = align_up(o + (pre ? T * 4 : 0));
   L.midb = o;       o = align_up(o + (pre ? P * I * 2 : 0));
+  L.pstats = o;     o = align_up(o + (pre ? (E + 1) * sizeof(coli::PrefillStats) : 0));
   L.tiles = o;      o = align_up(o + tiles * 8);
   L.n_tiles = o;    o = align_up(o + 4);
   L.queues = o;     o = align_up(o + coli::kRowQueueWords * 4);
@@ -156,6 +164,37 @@ T *at(coli_moe_t *m, size_t off) {
   return reinterpret_cast<T *>(m->ws + off);
 }
 
+coli::PrefillProblem prefill_problem(coli_moe_t *m, int T) {
+  const coli_moe_config_t &c = m->cfg;
+  const Layout &L = m->L;
+  coli::PrefillProblem Q{};
+  Q.gate = {m->w.gate_q, m->w.gate_s};
+  Q.up = {m->w.up_q, m->w.up_s};
+  Q.down = {m->w.down_q, m->w.down_s};
+  Q.sh_gate = {m->w.sh_gate_q, m->w.sh_gate_s};
+  Q.sh_up = {m->w.sh_up_q, m->w.sh_up_s};
+  Q.sh_down = {m->w.sh_down_q, m->w.sh_down_s};
+  Q.h = c.hidden;
+  Q.I = c.inter;
+  Q.T = T;
+  Q.k = c.top_k;
+  Q.E = c.n_experts;
+  Q.has_shared = c.n_shared;
+  Q.xb = at<_Float16>(m, L.xb);
+  Q.xexp = at<int32_t>(m, L.xexp);
+  Q.xn2 = at<float>(m, L.xn2);
+  Q.mid = at<_Float16>(m, L.midb);
+  Q.y = at<float>(m, L.y);
+  Q.stats = at<coli::PrefillStats>(m, L.pstats);
+  Q.offsets = at<int32_t>(m, L.offsets);
+  Q.sorted_ids = at<int32_t>(m, L.sorted_ids);
+  Q.active = at<int32_t>(m, L.active);
+  Q.n_active = at<int32_t>(m, L.n_active);
+  Q.tiles = at<int2>(m, L.tiles);
+  Q.n_tiles = at<int32_t>(m, L.n_tiles);
+  return Q;
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,7 +239,8 @@ int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (coli::launch_router_permute(w->router_w, at<float>(m, L.wrP), cfg->hidden, cfg->n_experts, s) !=
           hipSuccess ||
-      coli::launch_fill_i32(at<int32_t>(m, L.queues), coli::kRowQueueWords, 0, s) != hipSuccess) {
+      coli::launch_fill_i32(at<int32_t>(m, L.queues), coli::kRowQueueWords, 0, s) != hipSuccess ||
+      (prefill_enabled(m->cfg) && coli::launch_prefill_stats(prefill_problem(m, 0), s) != hipSuccess)) {
     delete m;
     return COLI_MOE_EDEVICE;
   }
@@ -259,33 +299,11 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
     });
   };
   if (prefill) {
-    // 2. selection and dispatch, 3. bf16 activations and the tile list,
+    // 2. selection and dispatch, 3. half activations and the tile list,
     // 4. grouped GEMMs on MFMA, 5. weighted combine
     if (select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
-    coli::PrefillProblem Q{};
-    Q.gate = {m->w.gate_q, m->w.gate_s};
-    Q.up = {m->w.up_q, m->w.up_s};
-    Q.down = {m->w.down_q, m->w.down_s};
-    Q.sh_gate = {m->w.sh_gate_q, m->w.sh_gate_s};
-    Q.sh_up = {m->w.sh_up_q, m->w.sh_up_s};
-    Q.sh_down = {m->w.sh_down_q, m->w.sh_down_s};
-    Q.h = h;
-    Q.I = I;
-    Q.T = T;
-    Q.k = k;
-    Q.E = E;
-    Q.has_shared = c.n_shared;
-    Q.xb = at<__bf16>(m, L.xb);
-    Q.mid = at<__bf16>(m, L.midb);
-    Q.y = y;
-    Q.offsets = offsets;
-    Q.sorted_ids = sorted_ids;
-    Q.active = active;
-    Q.n_active = n_active;
-    Q.tiles = at<int2>(m, L.tiles);
-    Q.n_tiles = at<int32_t>(m, L.n_tiles);
-    e = timed(m, K_PREFILL_PREP, s,
-              [&] { return coli::launch_prefill_prep(hidden, T, h, at<__bf16>(m, L.xb), s); });
+    coli::PrefillProblem Q = prefill_problem(m, T);
+    e = timed(m, K_PREFILL_PREP, s, [&] { return coli::launch_prefill_prep(hidden, T, h, Q, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     e = timed(m, K_BUILD_TILES, s, [&] { return coli::launch_build_tiles(Q, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;

@@ -36,13 +36,7 @@
 namespace coli {
 namespace {
 
-#ifndef COLI_GU_ROWS
-#define COLI_GU_ROWS 4
-#endif
-#ifndef COLI_GU_MIN_WAVES
-#define COLI_GU_MIN_WAVES 1
-#endif
-constexpr int kGuRows = COLI_GU_ROWS;      // gate/up rows per wave
+constexpr int kGuRows = 4;                 // gate/up rows per wave
 constexpr int kGuWaves = 32 / kGuRows;     // a block owns 32 rows of I
 constexpr int kDnWaves = 4;  // down block (larger batches): 4 waves x 8 rows
 constexpr int kDnRows = 8;
@@ -191,7 +185,7 @@ __device__ __forceinline__ Slot expert_slot(const DecodeProblem &P, int e, int p
 // grid = (I / 32, has_shared + n_routed_slots), 256 threads; the routing
 // and dispatch arrays come from the selection launch.
 template <int NTMAX>
-__global__ __launch_bounds__(kGuWaves * 64, COLI_GU_MIN_WAVES) void gate_up_kernel(DecodeProblem P) {
+__global__ __launch_bounds__(kGuWaves * 64, 1) void gate_up_kernel(DecodeProblem P) {
   __shared__ float mid_lds[kGuWaves * kGuRows][4];
   const int row0 = blockIdx.x * (kGuWaves * kGuRows);
   const int slot = (int)blockIdx.y - P.has_shared;
@@ -364,34 +358,19 @@ __global__ __launch_bounds__(256) void quantize_mid_kernel(const float *__restri
 // each slot's down matrix in turn, against the slot's intermediate row held
 // in LDS as digit planes (see the kernel's comment).
 // ---------------------------------------------------------------------------
-#ifndef COLI_SB_DEPTH
-#define COLI_SB_DEPTH 2
-#endif
-#ifndef COLI_SB_BLOCKS
-#define COLI_SB_BLOCKS 512
-#endif
-#ifndef COLI_DC_WAVES
-#define COLI_DC_WAVES 8
-#endif
-#ifndef COLI_DC_RING
-#define COLI_DC_RING 2
-#endif
-#ifndef COLI_DC_BLOCKS
-#define COLI_DC_BLOCKS 256
-#endif
-constexpr int kSbDepth = COLI_SB_DEPTH;     // gate/up rows in flight per wave
+constexpr int kSbDepth = 2;     // gate/up rows in flight per wave
 constexpr int kGuQueues = 64;               // gate/up row queues (atomic counters)
 constexpr int kGuQueueStride = 64;          // int32: one counter per 256 bytes
 static_assert(kGuQueues * kGuQueueStride == kRowQueueWords, "row queue words");
-constexpr int kSbBlocks = COLI_SB_BLOCKS;   // gate/up grid, T = 1 (4 waves per block)
+constexpr int kSbBlocks = 512;   // gate/up grid, T = 1 (4 waves per block)
 constexpr int kSbBlocksLds = kSbBlocks / 2; // gate/up grid, T = 2..4 (8 waves per block)
-constexpr int kDcWaves = COLI_DC_WAVES;     // down: waves per block
-constexpr int kDcBlocks = COLI_DC_BLOCKS;   // down: blocks (at most; fewer when h is small)
+constexpr int kDcWaves = 8;     // down: waves per block
+constexpr int kDcBlocks = 256;   // down: blocks (at most; fewer when h is small)
 constexpr int kDcLds = 64 * 1024;           // down: LDS for the digit planes of a slot group
 constexpr int kSbMaxXChunks = 4;            // T = 1 keeps the planes of h <= 64*32*4 columns in registers
 constexpr int kSbMaxXLds = 96 * 1024;       // bytes of hidden-row planes staged in LDS
 constexpr int kDcMaxChunks = 4;             // down: I <= 64*32*4
-constexpr int kDcMaxRing = COLI_DC_RING;    // down: slots in flight per wave, at most
+constexpr int kDcMaxRing = 2;    // down: slots in flight per wave, at most
 
 // Where the gate/up rows of a slot come from, and its assignment positions.
 struct GuCursor {

@@ -1,4 +1,4 @@
-// Prefill-sized expert FFN: grouped GEMMs on the bf16 matrix cores (MFMA)
+// Prefill-sized expert FFN: grouped GEMMs on the fp16 matrix cores (MFMA)
 // with float32 accumulation.
 //
 // Source: "colibri engine teardown" page, "Three key engineering decisions",
@@ -7,46 +7,66 @@
 // GEMM on its token group, fed by the expert offsets of step 3.  With
 // thousands of tokens the expert FFN is a dense contraction per expert
 // (M = tokens of the expert, N = weight rows, K = columns), so it runs on
-// v_mfma_f32_32x32x16_bf16.
+// v_mfma_f32_32x32x16_f16.
 //
-// Operands:
-//  A  activations in bf16 ([T][h] hidden rows for gate/up, the intermediate
-//     [P][I] for down), gathered per tile into LDS;
-//  B  the weights dequantised in registers straight into bf16: code q of a
-//     64-column group with scale s becomes bf16(q * s), computed as
-//     fma(u, s, -8 s) with u = q + 8 taken as an unsigned byte (exact before
-//     the one rounding to bf16).  Each weight is dequantised once per tile
-//     and feeds the 8 MFMA blocks of the tile's 256 tokens.
+// Number format.  The 16-bit operands are IEEE half precision (11-bit
+// significand): the matrix cores run it at the bf16 rate, the int4 codes
+// become halves with two packed instructions per pair, and every operand
+// rounding is 8 times smaller than bf16's.  Half precision has a narrow
+// exponent range, which power-of-two factors recover exactly:
+//  - hidden rows: x' = x * 2^-ex(t), ex(t) chosen per token so that
+//    max |x'| lies in [2^14, 2^15) (prep kernel, which also records
+//    ||x'||^2);
+//  - weights: w' = half(q * half(s * 2^ew)), ew per expert matrix chosen so
+//    that the largest scale times 2^ew lies in [2^11, 2^12), so |w'| < 2^15
+//    (scale_stats_kernel, at init);
+//  - intermediate: mid' = mid * 2^(14 - eb), with eb = floor(log2 B) for a
+//    bound B >= |mid| of the (token, expert): |silu(g)| <= |g| and
+//    |g_i| <= ||x|| ||G_i||, ||G_i|| <= 64 ||s_i|| (|q| <= 8, 64 codes per
+//    scale), so B = 4096 ||x||^2 max_i ||sG_i|| max_i ||sU_i||, and
+//    |mid'| < 2^15.
+// The float32 epilogues undo each factor exactly (ldexp).
+//
+// Weight conversion: a 32-bit word holds 8 codes (nibble c = column c, two's
+// complement).  Flipping a nibble's top bit turns it into u = q + 8; the
+// halves 0x6400 | u and 0x6400 | (u << 4) are 1024 + u and 1024 + 16 u, so a
+// packed add of -1032 (or -1152) leaves q (or 16 q) exactly, and a packed
+// multiply by the group's half scale (or a sixteenth of it) rounds q * s
+// once to half.  The 8 halves come out in the column order
+// 0 4 1 5 2 6 3 7; K is a sum index, so the activations are stored in the
+// same order within every 8 columns (prep kernel and the gate/up epilogue),
+// and A and B agree.
 //
 // Tiles: 256 rows of A (tokens of one expert) x 256 weight rows (gate/up:
 // 128 intermediate rows of gate and the same 128 of up; down: 256 output
-// rows); 8 waves, two per SIMD so that one wave's dequantisation overlaps the
-// other's MFMAs.  Wave w owns one 32-row MFMA block of B (gate/up: pair
-// w / 2, gate for even w, up for odd w) and all 256 tokens (8 blocks of 32
-// tokens, those wholly past the expert's last token skipped).  K runs in
-// steps of 64 columns (one scale group); each lane owns 32 of the 64
-// columns, so the 4 MFMAs of a step cover columns {8j..8j+7} and
-// {32+8j..32+8j+7} -- K is a sum index, any order common to A and B gives
-// the same products.  A rows and weights are copied into LDS rings ahead of
-// use.  For SwiGLU the up waves hand their accumulators to the gate waves
-// through LDS.
+// rows); 8 waves, two per SIMD.  Wave w owns one 32-row MFMA block of B
+// (gate/up: pair w / 2, gate for even w, up for odd w) and all 256 tokens
+// (8 blocks of 32 tokens, those wholly past the expert's last token
+// skipped), so each converted weight feeds up to 8 MFMAs.  K runs in steps
+// of 64 columns (one scale group); each lane owns 32 of the 64 columns, so
+// the 4 MFMAs of a step cover columns {8j..8j+7} and {32+8j..32+8j+7}.  A
+// rows and weights are copied into LDS rings ahead of use, the copies spread
+// between MFMA groups.  For SwiGLU the up waves hand their accumulators to
+// the gate waves through LDS.  Tiles are long in M and short in N because a
+// token row per step is one whole cache line while a weight row per step is
+// a 32-byte piece of one: the copies cost least per MFMA that way.
 //
 // The tile list (expert slot, first token) is built on the device from the
-// dispatch offsets.  The grid is launched for the largest possible list; each
-// block maps its hardware index to a (tile, column block) pair so that the
-// column blocks of one tile run on one XCD (hardware block i runs on XCD
-// i mod 8), where they share the tile's activation rows in that XCD's L2, and
-// blocks past the real list leave at once.
+// dispatch offsets, largest tiles first.  The grid is launched for the
+// largest possible list; each block maps its hardware index to a (tile,
+// column block) pair so that the column blocks of one tile run on one XCD
+// (hardware block i runs on XCD i mod 8), where they share the tile's
+// activation rows in that XCD's L2, and blocks past the real list leave at
+// once.
 #include "internal.h"
 #include "wave.h"
 
 namespace coli {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 256;          // tokens per tile
 constexpr int BK = 64;           // columns per K step = one scale group
@@ -54,37 +74,45 @@ constexpr int kWaves = 8;        // waves per block
 constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  const f32x2 f = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
-}
+// Exponent range kept for the intermediate's bound.
+constexpr int kMidExpMin = -100, kMidExpMax = 100;
+// LDS after the K loop: the up waves' accumulators (up to 128 KB), then the
+// tile rows' exponents.
+constexpr int kRowExpOff = 128 * 1024;
 
-__device__ __forceinline__ float ubyte(uint32_t v, int j) {
-  float f;
-  switch (j) {
-    case 0: asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v)); break;
-    case 1: asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v)); break;
-    case 2: asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v)); break;
-    default: asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v)); break;
-  }
-  return f;
-}
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// 8 int4 codes (nibble c = column c, two's complement) -> bf16(q * s) in
-// column order.  m8s = -8 s.
-__device__ __forceinline__ bf16x8 dequant_word(uint32_t w, float s, float m8s) {
-  const uint32_t v = w ^ 0x88888888u;  // u = q + 8 in every nibble
-  const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
-  uint32_t p[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    p[j] = pack_bf16(__builtin_fmaf(ubyte(lo, j), s, m8s), __builtin_fmaf(ubyte(hi, j), s, m8s));
-  return __builtin_bit_cast(bf16x8, p);
+// Storage position of column c within its group of 8 (column order
+// 0 4 1 5 2 6 3 7 of the converted weights).
+__device__ __forceinline__ int perm8(int c) { return (c & ~7) | ((c & 3) << 1) | ((c >> 2) & 1); }
+
+// floor(log2 |v|) for v != 0 (denormals included).
+__device__ __forceinline__ int ilog2f(float v) { return __builtin_amdgcn_frexp_expf(v) - 1; }
+
+// Bits of k where m is clear, bits of a ^ k where m is set (one v_bitop3).
+__device__ __forceinline__ uint32_t merge_xor(uint32_t a, uint32_t m, uint32_t k) { return ((a ^ k) & m) | (k & ~m); }
+
+// 8 int4 codes -> half(q * s) in the order 0 4 1 5 2 6 3 7; s1 = (s, s),
+// s16 = (s / 16, s / 16) as halves.  Each pair: the two nibbles with their
+// sign bit flipped (u = q + 8) dropped into the low mantissa bits of 1024
+// (bits 0-3) or, for the odd nibbles, bits 4-7 (1024 + 16 u).
+__device__ __forceinline__ f16x8 convert8(uint32_t w, f16x2 s1, f16x2 s16) {
+  const uint32_t w8 = w >> 8;
+  constexpr uint32_t kLo = 0x000F000Fu, kHi = 0x00F000F0u;
+  constexpr uint32_t kLoMagic = 0x64086408u, kHiMagic = 0x64806480u;  // 1024, 1024 with the sign bits to flip
+  const f16x2 c0 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const f16x2 c1 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const f16x2 d0 = (__builtin_bit_cast(f16x2, merge_xor(w, kLo, kLoMagic)) + c0) * s1;
+  const f16x2 d1 = (__builtin_bit_cast(f16x2, merge_xor(w, kHi, kHiMagic)) + c1) * s16;
+  const f16x2 d2 = (__builtin_bit_cast(f16x2, merge_xor(w8, kLo, kLoMagic)) + c0) * s1;
+  const f16x2 d3 = (__builtin_bit_cast(f16x2, merge_xor(w8, kHi, kHiMagic)) + c1) * s16;
+  return f16x8{d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
 }
 
 struct Tile {
   int p_begin, rows;  // first sorted position of the tile, valid rows (1..BM)
   int e;              // expert, -1 = shared
+  int stat;           // index into the per-expert statistics (E for the shared expert)
 };
 
 // Maps the hardware block index to (tile, column block); false for surplus
@@ -103,10 +131,12 @@ __device__ __forceinline__ bool tile_of_block(const PrefillProblem &P, int nb, T
   int cnt;
   if (d.x < 0) {
     t.e = -1;
+    t.stat = P.E;
     t.p_begin = P.T * P.k + d.y;
     cnt = P.T;
   } else {
     t.e = P.active[d.x];
+    t.stat = t.e;
     const int o = P.offsets[t.e];
     t.p_begin = o + d.y;
     cnt = P.offsets[t.e + 1] - o;
@@ -115,10 +145,10 @@ __device__ __forceinline__ bool tile_of_block(const PrefillProblem &P, int nb, T
   return true;
 }
 
-// LDS rings, filled by LDS-DMA loads (global_load_lds, 16 or 4 bytes per
-// lane, lane-linear in LDS):
+// LDS rings, filled by LDS-DMA loads (global_load_lds, 16 bytes per lane,
+// lane-linear in LDS):
 //  A ring, 4 slots = two pairs of K steps (the pair being computed and the
-//    next pair in flight): the tile's rows of 64 bf16 (128 bytes = 8 chunks
+//    next pair in flight): the tile's rows of 64 halves (128 bytes = 8 chunks
 //    of 16 bytes); chunk c of row r sits in slot c ^ ((r >> 1) & 7), so that
 //    the 16 rows read by 16 neighbouring lanes fall in 16 different bank
 //    groups (64 banks).  One block barrier per pair of steps publishes a
@@ -162,15 +192,11 @@ __device__ __forceinline__ void dma16v(uint32_t lds, const void *addr) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr)
                : "memory", "m0");
 }
-#pragma clang diagnostic pop
 template <int N>
 __device__ __forceinline__ void dma_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-
-
-
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+#pragma clang diagnostic pop
 
 // Where this lane's copies come from.
 struct Sources {
@@ -179,6 +205,7 @@ struct Sources {
   const uint8_t *q_base; // codes of this wave's 32 rows
   uint32_t q_off;        // row lane / 2 of the 32, this lane's 16 bytes
   const float *s_row;    // scales of row 32 w + lane (lanes 0..31)
+  float wm;              // 2^ew of this wave's weight table
 };
 
 template <int NMB>
@@ -256,11 +283,11 @@ struct WaveGemm {
 
   // One 64-column step.  Software-pipelined by MFMA group: while the NMB
   // MFMAs of group j run, the A fragments of group j + 1 are read from LDS
-  // and its weights dequantised (the compiler interleaves them; a fixed
+  // and its weights converted (the compiler interleaves them; a fixed
   // one MFMA : one LDS read : three VALU pattern measured 3% slower).
   // Step g from A slot g & 3, Q slot sq.
   template <class C>
-  __device__ __forceinline__ void compute(const char *lds, int g, int sq, const C &copies) {
+  __device__ __forceinline__ void compute(const char *lds, int g, int sq, float wm, const C &copies) {
     const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
     const char *A = lds + (g & 3) * kASlotBytes;
     const char *Q = lds + kQRingOff + sq * kQSlotBytes;
@@ -268,26 +295,28 @@ struct WaveGemm {
     const float c = *reinterpret_cast<const float *>(lds + kSRingOff + ((g >> 2) & 1) * kSSlotBytes +
                                                      (32 * wave + nl) * 16 + (g & 3) * 4);
     const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-    const float m8c = -8.0f * c;
+    const float sc = c * wm;
+    const _Float16 h1 = (_Float16)sc, h16 = (_Float16)(sc * 0.0625f);
+    const f16x2 s1 = {h1, h1}, s16 = {h16, h16};
     // row r = 32 mb + nl of group j: chunk slot (4 half + j) ^ ((r >> 1) & 7), (r >> 1) & 7 = (nl >> 1) & 7
     const char *arow = A + nl * 128;
     const int sw_ = (nl >> 1) & 7;
-    bf16x8 af[2][NMB], bf[2];
+    f16x8 af[2][NMB], bf[2];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
-      af[0][mb] = *reinterpret_cast<const bf16x8 *>(arow + mb * 4096 + (((4 * half) ^ sw_) * 16));
-    bf[0] = dequant_word(qw[0], c, m8c);
+      af[0][mb] = *reinterpret_cast<const f16x8 *>(arow + mb * 4096 + (((4 * half) ^ sw_) * 16));
+    bf[0] = convert8(qw[0], s1, s16);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cur = j & 1, nxt = cur ^ 1;
       if (j < 3) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
-          af[nxt][mb] = *reinterpret_cast<const bf16x8 *>(arow + mb * 4096 + (((4 * half + j + 1) ^ sw_) * 16));
-        bf[nxt] = dequant_word(qw[j + 1], c, m8c);
+          af[nxt][mb] = *reinterpret_cast<const f16x8 *>(arow + mb * 4096 + (((4 * half + j + 1) ^ sw_) * 16));
+        bf[nxt] = convert8(qw[j + 1], s1, s16);
       }
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][mb], bf[cur], acc[mb], 0, 0, 0);
+      for (int mb = 0; mb < NMB; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][mb], bf[cur], acc[mb], 0, 0, 0);
       copies.after(j);
     }
   }
@@ -323,12 +352,12 @@ struct WaveGemm {
       const bool chunk = g % 4 == 0;
       const PairCopies<NMB> pc{S,  lds, min(g + 2, G - 2), (g + 2) & 3, min(g + 2, G - 1), sq2,
                                chunk ? min(g / 4 + 1, last_chunk) : -1, (g / 4 + 1) & 1};
-      compute(lds, g, sq, pc);
+      compute(lds, g, sq, S.wm, pc);
       if (chunk)
         dma_wait<2 * kA + 2>();
       else
         dma_wait<2 * kA + 1>();
-      compute(lds, g + 1, sq1, QCopies{S, lds, min(g + 3, G - 1), sq});  // Q(g+3) into step g's slot
+      compute(lds, g + 1, sq1, S.wm, QCopies{S, lds, min(g + 3, G - 1), sq});  // Q(g+3) into step g's slot
       sq = sq2;
     }
     dma_wait<0>();    // no copy may land in LDS after this point
@@ -339,10 +368,24 @@ struct WaveGemm {
 // Row m of the tile held by register i of an MFMA block (token-block mb).
 __device__ __forceinline__ int acc_row(int mb, int half, int i) { return 32 * mb + 4 * half + 8 * (i >> 2) + (i & 3); }
 
-// ---------------------------------------------------------------------------
-// gate/up: mid[p][n] = silu(x_t . Wg[n]) * (x_t . Wu[n]), bf16.
-// Column blocks of 128 intermediate rows.
-// ---------------------------------------------------------------------------
+// Token of sorted position p (routed: its assignment's token; shared: p - T k).
+__device__ __forceinline__ int token_of(const PrefillProblem &P, const Tile &t, int p) {
+  return t.e < 0 ? p - P.T * P.k : P.sorted_ids[p] / P.k;
+}
+
+// Exponent eb of the intermediate's bound for token tok and the tile's expert.
+__device__ __forceinline__ int mid_exp(const PrefillProblem &P, const PrefillStats &st, float cmid, int tok) {
+  const float f = P.xn2[tok] * cmid;
+  if (!(f > 0.0f)) return kMidExpMin;
+  const int eb = ilog2f(f) + 2 * P.xexp[tok] - st.ew[0] - st.ew[1];
+  return min(max(eb, kMidExpMin), kMidExpMax);
+}
+
+// 4096 max ||sG_i|| max ||sU_i|| over the prescaled scales.
+__device__ __forceinline__ float mid_coef(const PrefillStats &st) { return 4096.0f * sqrtf(st.n2[0] * st.n2[1]); }
+
+__device__ __forceinline__ float pow2f(int e) { return __builtin_amdgcn_ldexpf(1.0f, e); }
+
 template <int NMB>
 __device__ __forceinline__ void a_sources(Sources &S, const PrefillProblem &P, const Tile &t, bool gather, int row_bytes) {
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -351,16 +394,36 @@ __device__ __forceinline__ void a_sources(Sources &S, const PrefillProblem &P, c
     // tile row of this lane in copy i (padding rows repeat the last valid row)
     const int r = 8 * ACopies<NMB>::index(i, wave) + (lane >> 3);
     const int p = t.p_begin + min(r, t.rows - 1);
-    const int row = !gather ? p : (t.e < 0 ? p - P.T * P.k : P.sorted_ids[p] / P.k);
+    const int row = !gather ? p : token_of(P, t, p);
     S.a_off[i] = (uint32_t)row * (uint32_t)row_bytes + a_chunk(r, lane);
   }
 }
 
+// Exponents of tile row m (0 for rows past the tile): the token's ex and the
+// intermediate's eb.  Each thread of the block takes one row.
+struct RowExp {
+  int ex, eb;
+};
+__device__ __forceinline__ RowExp row_exp(const PrefillProblem &P, const Tile &t, const PrefillStats &st, int m) {
+  RowExp r{0, 0};
+  if (m < t.rows) {
+    const int tok = token_of(P, t, t.p_begin + m);
+    r.ex = P.xexp[tok];
+    r.eb = mid_exp(P, st, mid_coef(st), tok);
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// gate/up: mid'[p][c] = half(silu(g) * u * 2^(14 - eb)), g = x . Wg[c],
+// u = x . Wu[c].  Column blocks of 128 intermediate rows.
+// ---------------------------------------------------------------------------
 template <int NMB>
 __device__ __forceinline__ void gate_up_tile(const PrefillProblem &P, const Tile &t, int n_blk, char *lds) {
   const int h = P.h, I = P.I;
   const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
   const int pair = wave >> 1, up = wave & 1;
+  const PrefillStats st = P.stats[t.stat];
   Sources S;
   S.a_base = reinterpret_cast<const char *>(P.xb);
   a_sources<NMB>(S, P, t, true, h * 2);
@@ -371,9 +434,15 @@ __device__ __forceinline__ void gate_up_tile(const PrefillProblem &P, const Tile
   S.q_base = M.q + eq + (size_t)row0 * (h >> 1);
   S.q_off = (uint32_t)((lane >> 1) * (h >> 1) + ((lane & 1) ^ ((lane >> 4) & 1)) * 16);
   S.s_row = M.s + es + (size_t)(row0 + nl) * (h >> 6);
+  S.wm = pow2f(st.ew[up]);
+  // this thread's tile row: its token's exponent and the intermediate's
+  // (loads issued now, used after the K loop)
+  const RowExp rx = row_exp(P, t, st, threadIdx.x);
 
   WaveGemm<NMB> W;
   W.run(S, h / BK, lds);
+  int2 *rowx = reinterpret_cast<int2 *>(lds + kRowExpOff);
+  if (threadIdx.x < BM) rowx[threadIdx.x] = make_int2(rx.ex, rx.eb);
 
   // up waves hand their accumulators to the gate wave of their pair, lane by
   // lane (the same lane holds the same (token, row) in both waves)
@@ -386,18 +455,20 @@ __device__ __forceinline__ void gate_up_tile(const PrefillProblem &P, const Tile
   }
   block_barrier();
   if (!up) {
-    const int n = row0 + nl;
+    const int cs = perm8(row0 + nl);
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = acc_row(mb, half, i);
         if (m < t.rows) {
-          const float gv = W.acc[mb][i], uv = xchg[(mb * 16 + i) * 64 + lane];
-          // silu in float32 with the hardware exp and reciprocal (the result is
-          // rounded to bf16)
-          const float sg = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
-          P.mid[(size_t)(t.p_begin + m) * I + n] = (__bf16)(sg * uv);
+          const int2 e = rowx[m];
+          const float g = __builtin_amdgcn_ldexpf(W.acc[mb][i], e.x - st.ew[0]);
+          const float u = __builtin_amdgcn_ldexpf(xchg[(mb * 16 + i) * 64 + lane], e.x - st.ew[1]);
+          // silu in float32 with the hardware exp and reciprocal
+          const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+          const float mid = __builtin_amdgcn_ldexpf(sg * u, 14 - e.y);
+          P.mid[(size_t)(t.p_begin + m) * I + cs] = (_Float16)mid;
         }
       }
   }
@@ -410,6 +481,7 @@ template <int NMB>
 __device__ __forceinline__ void down_tile(const PrefillProblem &P, const Tile &t, int n_blk, char *lds) {
   const int h = P.h, I = P.I;
   const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
+  const PrefillStats st = P.stats[t.stat];
   Sources S;
   S.a_base = reinterpret_cast<const char *>(P.mid);
   a_sources<NMB>(S, P, t, false, I * 2);
@@ -419,9 +491,14 @@ __device__ __forceinline__ void down_tile(const PrefillProblem &P, const Tile &t
   S.q_base = D.q + (t.e < 0 ? 0 : (size_t)t.e * qstride) + (size_t)row0 * (I >> 1);
   S.q_off = (uint32_t)((lane >> 1) * (I >> 1) + ((lane & 1) ^ ((lane >> 4) & 1)) * 16);
   S.s_row = D.s + (t.e < 0 ? 0 : (size_t)t.e * sstride) + (size_t)(row0 + nl) * (I >> 6);
+  S.wm = pow2f(st.ew[2]);
+  const RowExp rx = row_exp(P, t, st, threadIdx.x);
 
   WaveGemm<NMB> W;
   W.run(S, I / BK, lds);
+  int *rowe = reinterpret_cast<int *>(lds + kRowExpOff);
+  if (threadIdx.x < BM) rowe[threadIdx.x] = rx.eb - st.ew[2] - 14;
+  block_barrier();
 
   const int r = row0 + nl;
 #pragma unroll
@@ -429,12 +506,12 @@ __device__ __forceinline__ void down_tile(const PrefillProblem &P, const Tile &t
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = acc_row(mb, half, i);
-      if (m < t.rows) P.y[(size_t)(t.p_begin + m) * h + r] = W.acc[mb][i];
+      if (m < t.rows) P.y[(size_t)(t.p_begin + m) * h + r] = __builtin_amdgcn_ldexpf(W.acc[mb][i], rowe[m]);
     }
 }
 
-#define COLI_NMB_SWITCH(FN)                \
-  switch ((t.rows + 31) / 32) {            \
+#define COLI_NMB_SWITCH(FN)                 \
+  switch ((t.rows + 31) / 32) {             \
     case 1: FN<1>(P, t, n_blk, lds); break; \
     case 2: FN<2>(P, t, n_blk, lds); break; \
     case 3: FN<3>(P, t, n_blk, lds); break; \
@@ -465,9 +542,9 @@ __global__ __launch_bounds__(kThreads, 1) void down_mfma_kernel(PrefillProblem P
 
 // ---------------------------------------------------------------------------
 // Tile list: (slot, first token) for every BM tokens of every active expert,
-// then of the shared expert (slot -1), ordered by the tile's count of 32-token
-// blocks, largest first, and by slot within a count.  One workgroup of 1024 threads, one slot per thread
-// (n_active <= 512).
+// then of the shared expert (slot -1), ordered by the tile's count of
+// 32-token blocks, largest first, and by slot within a count.  One workgroup
+// of 1024 threads, one slot per thread (n_active <= 512).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__restrict__ offsets,
                                                            const int32_t *__restrict__ active,
@@ -489,26 +566,26 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__rest
   const int full = cnt / BM, rest = cnt - full * BM;
   const int part_nb = (rest + 31) / 32;  // 0 = no partial tile
   // per bucket: full tiles go to bucket kB, the partial one to bucket part_nb;
-  // exclusive scans over threads for each bucket (bucket kB counts full tiles)
+  // exclusive scans over threads for each bucket
   int mine[kB + 1], before[kB + 1];
 #pragma unroll
-  for (int k = 0; k <= kB; ++k) {
-    mine[k] = (k == kB ? full : 0) + (k == part_nb && k > 0 ? 1 : 0);
-    int incl = mine[k];
+  for (int b = 0; b <= kB; ++b) {
+    mine[b] = (b == kB ? full : 0) + (b == part_nb && b > 0 ? 1 : 0);
+    int incl = mine[b];
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int v = __shfl_up(incl, d);
       if (lane >= d) incl += v;
     }
-    before[k] = incl - mine[k];
-    if (lane == 63) wave_sum[wave][k] = incl;
+    before[b] = incl - mine[b];
+    if (lane == 63) wave_sum[wave][b] = incl;
   }
   __syncthreads();
   if (tid == 0) {
     int o = 0;
-    for (int k = kB; k >= 1; --k) {  // largest first
-      bucket_start[k] = o;
-      for (int w = 0; w < 16; ++w) o += wave_sum[w][k];
+    for (int b = kB; b >= 1; --b) {  // largest first
+      bucket_start[b] = o;
+      for (int w = 0; w < 16; ++w) o += wave_sum[w][b];
     }
     bucket_start[0] = o;
     *n_tiles = o;
@@ -516,11 +593,11 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__rest
   __syncthreads();
   const int slot = tid < na ? tid : -1;
 #pragma unroll
-  for (int k = 1; k <= kB; ++k) {
-    if (!mine[k]) continue;
-    int o = bucket_start[k] + before[k];
-    for (int w = 0; w < wave; ++w) o += wave_sum[w][k];
-    if (k == kB) {
+  for (int b = 1; b <= kB; ++b) {
+    if (!mine[b]) continue;
+    int o = bucket_start[b] + before[b];
+    for (int w = 0; w < wave; ++w) o += wave_sum[w][b];
+    if (b == kB) {
       for (int i = 0; i < full; ++i) tiles[o + i] = make_int2(slot, i * BM);
       if (part_nb == kB) tiles[o + full] = make_int2(slot, full * BM);
     } else {
@@ -529,15 +606,94 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t *__rest
   }
 }
 
-// x [T][h] float -> bf16 (round to nearest even), 8 values per thread.
-__global__ __launch_bounds__(256) void to_bf16_kernel(const float *__restrict__ x, size_t n_words,
-                                                      __bf16 *__restrict__ xb) {
-  const size_t w = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (w >= n_words) return;
-  const float4 a = reinterpret_cast<const float4 *>(x)[2 * w];
-  const float4 b = reinterpret_cast<const float4 *>(x)[2 * w + 1];
-  const uint4 o = make_uint4(pack_bf16(a.x, a.y), pack_bf16(a.z, a.w), pack_bf16(b.x, b.y), pack_bf16(b.z, b.w));
-  reinterpret_cast<uint4 *>(xb)[w] = o;
+// ---------------------------------------------------------------------------
+// Hidden rows to half: one block per token.  x' = x * 2^-ex with ex =
+// floor(log2 max |x|) - 14 (0 for an all-zero row), rounded once to half and
+// stored in the column order of the converted weights; xexp[t] = ex,
+// xn2[t] = sum of x'^2 (float32, fixed order).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_reduce(float v, float *red, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float o = __shfl_xor(v, d);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0];
+  for (int i = 1; i < 4; ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+  return v;
+}
+
+__global__ __launch_bounds__(256) void prep_x_kernel(const float *__restrict__ x, int h, _Float16 *__restrict__ xb,
+                                                     int32_t *__restrict__ xexp, float *__restrict__ xn2) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const float4 *row = reinterpret_cast<const float4 *>(x + (size_t)t * h);
+  const int n8 = h >> 3;
+  float mx = 0.0f;
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    const float4 a = row[2 * i], b = row[2 * i + 1];
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+  }
+  mx = block_reduce(mx, red, true);
+  const int ex = mx > 0.0f ? ilog2f(mx) - 14 : 0;
+  float ss = 0.0f;
+  uint4 *out = reinterpret_cast<uint4 *>(xb + (size_t)t * h);
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    const float4 a = row[2 * i], b = row[2 * i + 1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    _Float16 o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float s = __builtin_amdgcn_ldexpf(v[c], -ex);
+      ss = __builtin_fmaf(s, s, ss);
+      o[(c & 3) * 2 + (c >> 2)] = (_Float16)s;
+    }
+    out[i] = __builtin_bit_cast(uint4, o);
+  }
+  ss = block_reduce(ss, red, false);
+  if (threadIdx.x == 0) {
+    xexp[t] = ex;
+    xn2[t] = ss;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-expert statistics of the prescaling, one block per (matrix, expert):
+// ew = 11 - floor(log2 max s) (0 for an all-zero table), and for gate and up
+// the largest squared row norm of the scales times 2^ew.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void scale_stats_kernel(PrefillProblem P, int n_stats) {
+  __shared__ float red[4];
+  const int mat = blockIdx.x, e = blockIdx.y;  // mat 0 gate, 1 up, 2 down
+  const bool sh = e == P.E;
+  const ExpertTables &tab = mat == 0 ? (sh ? P.sh_gate : P.gate) : mat == 1 ? (sh ? P.sh_up : P.up)
+                                                                            : (sh ? P.sh_down : P.down);
+  const int rows = mat < 2 ? P.I : P.h, groups = (mat < 2 ? P.h : P.I) >> 6;
+  const float *s = tab.s + (sh ? 0 : (size_t)e * rows * groups);
+  const size_t n = (size_t)rows * groups;
+  float mx = 0.0f;
+  for (size_t i = threadIdx.x; i < n; i += 256) mx = fmaxf(mx, fabsf(s[i]));
+  mx = block_reduce(mx, red, true);
+  const int ew = mx > 0.0f ? 11 - ilog2f(mx) : 0;
+  if (threadIdx.x == 0) P.stats[e].ew[mat] = ew;
+  if (mat == 2) return;
+  float best = 0.0f;
+  for (int r = threadIdx.x; r < rows; r += 256) {
+    float acc = 0.0f;
+    for (int g = 0; g < groups; ++g) {
+      const float v = __builtin_amdgcn_ldexpf(s[(size_t)r * groups + g], ew);
+      acc = __builtin_fmaf(v, v, acc);
+    }
+    best = fmaxf(best, acc);
+  }
+  best = block_reduce(best, red, true);
+  if (threadIdx.x == 0) P.stats[e].n2[mat] = best;
+  (void)n_stats;
 }
 
 int grid_blocks(int nb, int max_tiles) { return kXcds * nb * ((max_tiles + kXcds - 1) / kXcds); }
@@ -551,9 +707,13 @@ int prefill_max_tiles(int T, int k, int E, int has_shared) {
   return n / BM + routed_slots + (has_shared ? (T + BM - 1) / BM : 0);
 }
 
-hipError_t launch_prefill_prep(const float *x, int T, int h, __bf16 *xb, hipStream_t s) {
-  const size_t n_words = (size_t)T * h / 8;
-  return launch(to_bf16_kernel, (unsigned)((n_words + 255) / 256), 256, 0, s, x, n_words, xb);
+hipError_t launch_prefill_prep(const float *x, int T, int h, PrefillProblem &P, hipStream_t s) {
+  return launch(prep_x_kernel, T, 256, 0, s, x, h, const_cast<_Float16 *>(P.xb), P.xexp, P.xn2);
+}
+
+hipError_t launch_prefill_stats(const PrefillProblem &P, hipStream_t s) {
+  const int n = P.E + (P.has_shared ? 1 : 0);
+  return launch(scale_stats_kernel, dim3(3, n), 256, 0, s, P, n);
 }
 
 hipError_t launch_build_tiles(const PrefillProblem &P, hipStream_t s) {

@@ -139,17 +139,29 @@ hipError_t launch_combine(const float *y, const float *w, const int32_t *inv, in
                           int has_shared, float *out, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Prefill path (expert_mfma.hip): grouped GEMMs on bf16 MFMA.
+// Prefill path (expert_mfma.hip): grouped GEMMs on fp16 MFMA.
 // ---------------------------------------------------------------------------
+// Power-of-two prescaling of one expert's tables (index E: the shared expert):
+// weights w' = w * 2^ew[m] (m: 0 gate, 1 up, 2 down), and the largest squared
+// row norm of the prescaled gate and up scales.
+struct PrefillStats {
+  int32_t ew[3];
+  float n2[2];
+  int32_t pad[3];
+};
+
 struct PrefillProblem {
   ExpertTables gate, up, down;
   ExpertTables sh_gate, sh_up, sh_down;
   int h, I, T, k, E, has_shared;
-  const __bf16 *xb;  // [T][h] hidden rows in bf16
-  __bf16 *mid;       // [P][I] intermediate in bf16
-  float *y;          // [P][h] expert outputs
+  const _Float16 *xb;    // [T][h] hidden rows x * 2^-xexp[t] in half, columns permuted in 8s
+  int32_t *xexp;         // [T] per-token exponents
+  float *xn2;            // [T] squared norms of the scaled rows
+  _Float16 *mid;         // [P][I] intermediate (scaled), half, columns permuted in 8s
+  float *y;              // [P][h] expert outputs
+  PrefillStats *stats;   // [E + has_shared]
   const int32_t *offsets, *sorted_ids, *active, *n_active;
-  int2 *tiles;       // (slot or -1 for the shared expert, first token)
+  int2 *tiles;           // (slot or -1 for the shared expert, first token)
   int32_t *n_tiles;
 };
 
@@ -157,10 +169,12 @@ struct PrefillProblem {
 bool prefill_shape_ok(int h, int I);
 // Largest tile count of a call (grid size of the GEMM launches).
 int prefill_max_tiles(int T, int k, int E, int has_shared);
-// x [T][h] float -> bf16.
-hipError_t launch_prefill_prep(const float *x, int T, int h, __bf16 *xb, hipStream_t s);
+// x [T][h] float -> scaled half rows (P.xb), P.xexp, P.xn2.
+hipError_t launch_prefill_prep(const float *x, int T, int h, PrefillProblem &P, hipStream_t s);
+// P.stats from the scale tables (once per set of tables).
+hipError_t launch_prefill_stats(const PrefillProblem &P, hipStream_t s);
 hipError_t launch_build_tiles(const PrefillProblem &P, hipStream_t s);
-// mid = silu(x Wg^T) * (x Wu^T) per expert tile, bf16.
+// mid = silu(x Wg^T) * (x Wu^T) per expert tile, half (scaled).
 hipError_t launch_gate_up_mfma(const PrefillProblem &P, hipStream_t s);
 // y = mid Wd^T per expert tile, float32.
 hipError_t launch_down_mfma(const PrefillProblem &P, hipStream_t s);

@@ -2,18 +2,14 @@
 the same seeded inputs.
 
 Bar: expert indices, routing weights and every dispatch array bit-exact;
-layer outputs:
- - float32-accumulate GEMV path: max relative error 2e-3, element-wise
-   (floored at the row RMS);
- - bf16 MFMA path: max over tokens of the per-token relative error
-   ||out_t - ref_t|| / ||ref_t|| at most 2e-2, and element-wise (floored at
-   the row RMS) at most 6e-2.  Dequantising to bf16 rounds four operands
-   (hidden rows, gate/up weights, the intermediate, down weights) to 8
-   significant bits, which gives about 4e-3 RMS error relative to the row
-   RMS; the element-wise maximum over a 4096 x 6144 output is then about
-   2.3e-2, so the element-wise bound is set at 6e-2 (about 15 sigma), which
-   any wrong element (error of the order of the row RMS or more) still
-   exceeds by far.
+layer outputs, max relative error element-wise (floored at the row RMS,
+tests/gpu_util.rel_err):
+ - float32-accumulate GEMV path: 2e-3;
+ - fp16 MFMA (prefill) path: 2e-2.  The per-token relative error
+   ||out_t - ref_t|| / ||ref_t|| is logged beside it.  Half precision rounds
+   the hidden rows, the weights (q * s) and the intermediate to 11
+   significant bits, about 6e-4 RMS error relative to the row RMS, so the
+   element-wise maximum over a 4096 x 6144 output is near 3.5e-3.
 """
 import json
 import os
@@ -29,8 +25,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL_GEMV = 2e-3
-TOL_MFMA = 2e-2        # per-token relative error
-TOL_MFMA_ELEM = 6e-2   # element-wise, floored at the row RMS
+TOL_MFMA_ELEM = 2e-2   # element-wise, floored at the row RMS
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -43,8 +38,8 @@ def dev():
 
 def assert_mfma_close(out, ref, what=""):
     nw, ew = row_rel_err(out, ref), rel_err(out, ref)
-    log(f"  {what}per-token rel err {nw:.3e}, element-wise {ew:.3e}")
-    assert nw <= TOL_MFMA, (what, nw)
+    log(f"  {what}element-wise rel err {ew:.3e} (bar {TOL_MFMA_ELEM:.0e}), per-token {nw:.3e}, "
+        f"rows {len(out)}")
     assert ew <= TOL_MFMA_ELEM, (what, ew)
 
 
@@ -398,11 +393,66 @@ def test_mfma_path_few_tokens(dev):
     check_mfma(MID, 23, 5, dev, threshold=1)
 
 
+def random_tables(rng, n, h, I, lo, hi):
+    """n experts of uniform random code bytes (every code, -8 included) and
+    scales log-uniform in [lo, hi) (each group its own)."""
+    def sc(shape):
+        return np.exp(rng.uniform(np.log(lo), np.log(hi), shape)).astype(np.float32)
+    return dict(gate_q=rng.integers(0, 256, (n, I, h // 2), dtype=np.uint8), gate_s=sc((n, I, h // 64)),
+                up_q=rng.integers(0, 256, (n, I, h // 2), dtype=np.uint8), up_s=sc((n, I, h // 64)),
+                down_q=rng.integers(0, 256, (n, h, I // 2), dtype=np.uint8), down_s=sc((n, h, I // 64)))
+
+
+def test_mfma_path_all_codes_wide_scales(dev):
+    """MFMA path on uniform random code bytes (all 16 codes, -8 included)
+    with group scales log-uniform over five decades, 1e-6 .. 1e-1: the
+    per-matrix power-of-two prescale keeps every weight a normal half."""
+    log("MFMA path, all codes, scales 1e-6 .. 1e-1")
+    rng = np.random.default_rng(123)
+    h, I, E = MID.hidden, MID.inter, MID.n_experts
+    routed = random_tables(rng, E, h, I, 1e-6, 1e-1)
+    shared = {k: v[0] for k, v in random_tables(rng, 1, h, I, 1e-6, 1e-1).items()}
+    L = DeviceLayer(MID, 61, 0, dev, max_tokens=200, prefill_threshold=64, keep_host=True, routed=routed,
+                    shared=shared)
+    x = synth.hidden(MID, 61, 200)
+    out = run(L, x, dev)
+    assert_routing_matches(L, x, 200)
+    ref, _, _ = L.oracle_forward(x)
+    assert_mfma_close(out, ref, "all codes: ")
+
+
+def test_mfma_path_hidden_and_weight_ranges(dev):
+    """MFMA path with hidden rows scaled by 10^-4 .. 10^4 (row by row) and
+    experts whose scales sit near 1e-7 or near 10: every per-token,
+    per-matrix and intermediate power-of-two factor is exercised, far outside
+    half precision's own range."""
+    log("MFMA path, hidden rows 1e-4 .. 1e4, scales near 1e-7 and 10")
+    rng = np.random.default_rng(321)
+    h, I, E = MID.hidden, MID.inter, MID.n_experts
+    routed = synth.routed_tables(MID, 62)
+    for name in ("gate_s", "up_s", "down_s"):
+        routed[name] = routed[name].copy()
+        routed[name][: E // 2] *= np.float32(1e-5)
+        routed[name][E // 2:] *= np.float32(1e3)
+    shared = synth.shared_tables(MID, 62)
+    L = DeviceLayer(MID, 62, 0, dev, max_tokens=160, prefill_threshold=64, keep_host=True, routed=routed,
+                    shared=shared)
+    x = synth.hidden(MID, 62, 160)
+    x = (x * (10.0 ** rng.integers(-4, 5, size=(160, 1)))).astype(np.float32)
+    out = run(L, x, dev)
+    assert_routing_matches(L, x, 160)
+    ref, _, _ = L.oracle_forward(x)
+    assert np.all(np.isfinite(out))
+    assert_mfma_close(out, ref, "ranges: ")
+
+
 def test_mfma_path_no_shared_expert_olmoe(dev):
     """OLMoE-like layer (h 2048, E 64, k 8, I 1024, no shared expert) at
-    T = 512 on the MFMA path, outputs of sampled tokens."""
+    T = 512 on the MFMA path, outputs of 96 tokens (every 8th, plus the
+    last)."""
     log("MFMA path OLMoE-like T=512")
-    check_mfma(synth.OLMOE, 24, 512, dev, threshold=256, rows=[0, 1, 255, 300, 511])
+    rows = list(range(0, 512, 8))[:95] + [511]
+    check_mfma(synth.OLMOE, 24, 512, dev, threshold=256, rows=rows)
 
 
 def test_threshold_switch_on_one_handle(dev):
@@ -463,24 +513,69 @@ def test_glm_decode_calls_in_a_row(dev, glm):
         assert err <= TOL_GEMV
 
 
-@pytest.mark.timeout(300)
-def test_glm_decode_T64_sampled(dev, glm):
+@pytest.mark.timeout(600)
+def test_glm_decode_T64_all_rows(dev, glm):
     T = 64
-    log("GLM-like decode T=64")
+    log("GLM-like decode T=64, every row against the oracle")
     x = synth.hidden(synth.GLM, 1, T, batch=164)
     out = run(glm, x, dev)
     assert_routing_matches(glm, x, T)
-    rows = [0, 13, 37, 63]
-    ref, _, _ = glm.oracle_forward(x[rows])
-    err = rel_err(out[rows], ref)
-    log(f"  rel err {err:.3e}")
+    ref, _, _ = glm.oracle_forward(x)
+    err = rel_err(out, ref)
+    log(f"  rel err {err:.3e} over {T} rows")
     assert err <= TOL_GEMV
 
 
-@pytest.mark.timeout(300)
+@pytest.mark.timeout(600)
+def test_two_resident_glm_layers_on_separate_handles(dev, glm):
+    """Layers 0 and 1 of the stack resident at once, each on its own handle:
+    single-token and four-token calls alternate between them, each against
+    the oracle of its own layer (the benchmark cycles 8 such layers)."""
+    log("building GLM-like layer 1 beside layer 0")
+    L1 = DeviceLayer(synth.GLM, 1, 1, dev, max_tokens=64)
+    try:
+        for b, (lay, T) in enumerate(((glm, 1), (L1, 1), (glm, 4), (L1, 4), (L1, 1))):
+            log(f"  layer {lay.layer} T={T}")
+            x = synth.hidden(synth.GLM, 1, T, layer=lay.layer, batch=500 + b)
+            out = run(lay, x, dev)
+            assert_routing_matches(lay, x, T)
+            ref, _, _ = lay.oracle_forward(x)
+            err = rel_err(out, ref)
+            log(f"  rel err {err:.3e}")
+            assert err <= TOL_GEMV, (lay.layer, T, err)
+    finally:
+        L1.close()
+
+
+def prefill_sample_rows(idx: np.ndarray, E: int, n_rows: int, seed: int) -> list:
+    """Tokens whose outputs cover every kind of GEMM tile of a prefill call:
+    the first and last token of every 128-token tile of the most loaded
+    expert, one token of each expert holding at most 32 tokens (one-block
+    tiles), the shared expert's last tile (the last tokens), then random
+    tokens up to n_rows."""
+    T = idx.shape[0]
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    head = int(np.argmax(counts))
+    on_head = np.nonzero((idx == head).any(axis=1))[0]
+    rows = set(int(on_head[i]) for i in range(0, len(on_head), 128))
+    rows |= set(int(on_head[min(i + 127, len(on_head) - 1)]) for i in range(0, len(on_head), 128))
+    for e in np.nonzero((counts > 0) & (counts <= 32))[0]:
+        rows.add(int(np.nonzero((idx == e).any(axis=1))[0][0]))
+    rows |= set(range(max(0, T - 8), T)) | {0, 1, T // 2}
+    rest = np.random.default_rng(seed).permutation(T)
+    for r in rest:
+        if len(rows) >= n_rows:
+            break
+        rows.add(int(r))
+    return sorted(rows)
+
+
+@pytest.mark.timeout(900)
 def test_glm_prefill_routing_and_sampled_outputs(dev):
     """T = 4096 on the prefill workload (Zipf-biased selection): routing and
-    dispatch bit-exact for every token, outputs on sampled tokens."""
+    dispatch bit-exact for every token, outputs of 256 tokens covering every
+    tile of the head expert, the one-block tail tiles and the shared
+    expert's last tile, element-wise at the MFMA bar."""
     T = 4096
     log("GLM-like prefill T=4096 (Zipf selection bias)")
     L = DeviceLayer(synth.GLM_PREFILL, 1, 0, dev, max_tokens=T)
@@ -488,11 +583,10 @@ def test_glm_prefill_routing_and_sampled_outputs(dev):
     out = run(L, x, dev)
     idx, _ = assert_routing_matches(L, x, T)
     counts = np.bincount(idx.reshape(-1), minlength=256)
-    log(f"  distinct experts {int((counts > 0).sum())}, head load {int(counts.max())}")
-    head = int(np.argmax(counts))
-    on_head = np.nonzero((idx == head).any(axis=1))[0]
-    extra = np.random.default_rng(4096).choice(T, 26, replace=False)
-    rows = sorted(set([0, 1, 2047, 4095, int(on_head[0]), int(on_head[-1])] + [int(r) for r in extra]))
+    log(f"  distinct experts {int((counts > 0).sum())}, head load {int(counts.max())}, "
+        f"experts with <= 32 tokens {int(((counts > 0) & (counts <= 32)).sum())}")
+    rows = prefill_sample_rows(idx, 256, 256, 4096)
+    log(f"  oracle on {len(rows)} rows")
     ref, _, _ = L.oracle_forward(x[rows])
     assert_mfma_close(out[rows], ref)
     L.close()
