@@ -67,7 +67,7 @@ typedef struct {
   int32_t group_size;        /* weights per scale: must be 64 */
   int32_t n_group;           /* expert groups of noaux_tc: must be 1 */
   int32_t max_tokens;        /* most tokens one forward may take, >= 1 */
-  int32_t prefill_threshold; /* T >= this takes the bf16 MFMA path; 0 = 256 */
+  int32_t prefill_threshold; /* T >= this takes the MFMA (fp16) path; 0 = 256 */
   float routed_scaling_factor;
 } coli_moe_config_t;
 
@@ -129,14 +129,36 @@ int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe
  * DEVICE float32 [T][hidden] (16-byte aligned, may not alias `hidden`).
  * Asynchronous on `stream`; the host never reads device data.  T == 0 checks
  * the arguments and enqueues nothing (dry run).  T >= prefill_threshold runs
- * the bf16 MFMA grouped-GEMM path when hidden and inter are multiples of 256
- * and the bf16 copies of the activations ([max_tokens][hidden] and
- * [max_tokens*(top_k+n_shared)][inter]) stay under 4 GiB; every other call
- * runs the float32-accumulate GEMV path.
+ * the MFMA grouped-GEMM path (fp16 operands, float32 accumulation) when
+ * hidden and inter are multiples of 256 and the 16-bit copies of the
+ * activations ([max_tokens][hidden] and [max_tokens*(top_k+n_shared)][inter])
+ * stay under 4 GiB; every other call runs the float32-accumulate GEMV path.
  * Errors: -4 bad handle/pointer, -1 T > max_tokens (or T < 0 gives -4),
  * -3 HIP launch error.
  */
 int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, void *stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, serving
+ * loops, harnesses that forbid hipMalloc): the same layer forward as
+ * coli_moe_forward, with no handle and no workspace argument.  Its workspace
+ * is a device array inside the library of COLI_MOE_STATIC_SCRATCH_BYTES
+ * (64 MiB) per device, held from the first call on a device until the
+ * process ends; the call allocates nothing, host or device.  Each call
+ * re-stages the per-layer state in it (router copy, cleared counters,
+ * prefill statistics) on `stream` and then runs the forward, so calls whose
+ * work overlaps on one device race on that array: serialise them (one
+ * stream, or events).  Arguments as for coli_moe_init (cfg, w: DEVICE weight
+ * tables, borrowed for the call) and coli_moe_forward (hidden, out, T).
+ * Errors: -1 T > max_tokens, or the configuration's workspace
+ * (coli_moe_workspace_bytes) exceeds COLI_MOE_STATIC_SCRATCH_BYTES -- e.g.
+ * a layer with h 6144, 256 experts, top-8, I 2048 and a shared expert fits
+ * up to max_tokens 163; -2 routing configuration; -4 bad argument;
+ * -3 HIP error.  T == 0 checks the arguments and enqueues nothing.
+ */
+#define COLI_MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int coli_moe_forward_noalloc(const coli_moe_config_t *cfg, const coli_moe_weights_t *w, const float *hidden,
+                             float *out, int32_t T, void *stream);
 
 /* Release the handle (host memory only).  NULL is a no-op.  The caller must
  * make sure no enqueued forward of the handle is still running. */

@@ -28,6 +28,7 @@ COLI_MOE_EROUTING = -2
 COLI_MOE_EDEVICE = -3
 COLI_MOE_EARG = -4
 COLI_MOE_N_KERNELS = 10
+COLI_MOE_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class ColiMoeError(RuntimeError):
@@ -68,6 +69,8 @@ def load_library():
         L.coli_moe_init.restype = ctypes.c_int
         L.coli_moe_forward.argtypes = [vp, vp, vp, i32, vp]
         L.coli_moe_forward.restype = ctypes.c_int
+        L.coli_moe_forward_noalloc.argtypes = [cfgp, wp, vp, vp, i32, vp]
+        L.coli_moe_forward_noalloc.restype = ctypes.c_int
         L.coli_moe_free.argtypes = [vp]
         L.coli_moe_free.restype = None
         L.coli_moe_last_routing.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -120,6 +123,14 @@ def coli_moe_init(cfg: coli_moe_config_t, weights: coli_moe_weights_t, workspace
 
 def coli_moe_forward(handle, hidden: int, out: int, T: int, stream: int = 0) -> int:
     return _check(load_library().coli_moe_forward(handle, hidden, out, int(T), stream), "coli_moe_forward")
+
+
+def coli_moe_forward_noalloc(cfg: coli_moe_config_t, weights: coli_moe_weights_t, hidden: int, out: int, T: int,
+                             stream: int = 0) -> int:
+    """The forward without handle or workspace: the library's own device
+    array (COLI_MOE_STATIC_SCRATCH_BYTES per device) is the workspace."""
+    return _check(load_library().coli_moe_forward_noalloc(ctypes.byref(cfg), ctypes.byref(weights), hidden, out,
+                                                          int(T), stream), "coli_moe_forward_noalloc")
 
 
 def coli_moe_free(handle) -> None:

@@ -10,6 +10,7 @@
 // copy, expert offsets) follows the opaque context of the cf-1.com Colibri
 // article, section 3.2.
 #include <algorithm>
+#include <atomic>
 #include <new>
 #include <vector>
 
@@ -195,7 +196,73 @@ coli::PrefillProblem prefill_problem(coli_moe_t *m, int T) {
   return Q;
 }
 
+
+int weights_ok(const coli_moe_config_t &cfg, const coli_moe_weights_t &w) {
+  const void *tabs[] = {w.gate_q, w.gate_s, w.up_q, w.up_s, w.down_q, w.down_s};
+  for (const void *p : tabs)
+    if (!p || !aligned(p, 16)) return COLI_MOE_EARG;
+  if (!w.router_w || !aligned(w.router_w, 4) || (w.sel_bias && !aligned(w.sel_bias, 4))) return COLI_MOE_EARG;
+  if (cfg.n_shared) {
+    const void *sh[] = {w.sh_gate_q, w.sh_gate_s, w.sh_up_q, w.sh_up_s, w.sh_down_q, w.sh_down_s};
+    for (const void *p : sh)
+      if (!p || !aligned(p, 16)) return COLI_MOE_EARG;
+  }
+  return COLI_MOE_OK;
+}
+
+// Host fields of a handle over the workspace ws (no allocation).
+void set_up(coli_moe_t *m, const coli_moe_config_t &cfg, const coli_moe_weights_t &w, char *ws, const Layout &L) {
+  m->cfg = cfg;
+  if (m->cfg.prefill_threshold == 0) m->cfg.prefill_threshold = 256;
+  m->w = w;
+  m->ws = ws;
+  m->L = L;
+  m->last_T = 0;
+  m->prof_calls_left = 0;
+  m->prof_calls_done = 0;
+  m->prof_used = 0;
+}
+
+// The workspace state every forward starts from: the lane-permuted router,
+// cleared row queues, and the prefill prescale statistics.
+hipError_t stage(coli_moe_t *m, hipStream_t s) {
+  hipError_t e = coli::launch_router_permute(m->w.router_w, at<float>(m, m->L.wrP), m->cfg.hidden,
+                                             m->cfg.n_experts, s);
+  if (e == hipSuccess) e = coli::launch_fill_i32(at<int32_t>(m, m->L.queues), coli::kRowQueueWords, 0, s);
+  if (e == hipSuccess && prefill_enabled(m->cfg)) e = coli::launch_prefill_stats(prefill_problem(m, 0), s);
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace of coli_moe_forward_noalloc: one file-scope device array (each
+// device the library runs on holds its own copy until the process ends).
+// Host code never passes the array's name to a kernel: it is a host-side
+// stand-in, not a device address.  The device address is taken once per
+// device with hipGetSymbolAddress and used everywhere instead.
+// ---------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) char scratch[COLI_MOE_STATIC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::atomic<char *> scratch_ptr[kMaxDevices];
+
+hipError_t scratch_of_current_device(char **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  char *p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void *addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    p = static_cast<char *>(addr);
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
+
 
 extern "C" {
 
@@ -211,36 +278,15 @@ int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe
   *out = nullptr;
   int code = COLI_MOE_OK;
   if (!config_ok(*cfg, &code)) return code;
-  const void *tabs[] = {w->gate_q, w->gate_s, w->up_q, w->up_s, w->down_q, w->down_s};
-  for (const void *p : tabs)
-    if (!p || !aligned(p, 16)) return COLI_MOE_EARG;
-  if (!w->router_w || !aligned(w->router_w, 4) || (w->sel_bias && !aligned(w->sel_bias, 4)))
-    return COLI_MOE_EARG;
-  if (cfg->n_shared) {
-    const void *sh[] = {w->sh_gate_q, w->sh_gate_s, w->sh_up_q, w->sh_up_s, w->sh_down_q, w->sh_down_s};
-    for (const void *p : sh)
-      if (!p || !aligned(p, 16)) return COLI_MOE_EARG;
-  }
+  if ((code = weights_ok(*cfg, *w)) != COLI_MOE_OK) return code;
   if (!aligned(workspace, kAlign)) return COLI_MOE_EARG;
   const Layout L = layout_of(*cfg);
   if (workspace_bytes < L.total) return COLI_MOE_ECAPACITY;
 
   coli_moe_t *m = new (std::nothrow) coli_moe_t();
   if (!m) return COLI_MOE_EARG;
-  m->cfg = *cfg;
-  if (m->cfg.prefill_threshold == 0) m->cfg.prefill_threshold = 256;
-  m->w = *w;
-  m->ws = static_cast<char *>(workspace);
-  m->L = L;
-  m->last_T = 0;
-  m->prof_calls_left = 0;
-  m->prof_calls_done = 0;
-  m->prof_used = 0;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (coli::launch_router_permute(w->router_w, at<float>(m, L.wrP), cfg->hidden, cfg->n_experts, s) !=
-          hipSuccess ||
-      coli::launch_fill_i32(at<int32_t>(m, L.queues), coli::kRowQueueWords, 0, s) != hipSuccess ||
-      (prefill_enabled(m->cfg) && coli::launch_prefill_stats(prefill_problem(m, 0), s) != hipSuccess)) {
+  set_up(m, *cfg, *w, static_cast<char *>(workspace), L);
+  if (stage(m, static_cast<hipStream_t>(stream)) != hipSuccess) {
     delete m;
     return COLI_MOE_EDEVICE;
   }
@@ -378,6 +424,26 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
     ++m->prof_calls_done;
   }
   return COLI_MOE_OK;
+}
+
+int coli_moe_forward_noalloc(const coli_moe_config_t *cfg, const coli_moe_weights_t *w, const float *hidden,
+                             float *out, int32_t T, void *stream) {
+  if (!cfg || !w || T < 0) return COLI_MOE_EARG;
+  int code = COLI_MOE_OK;
+  if (!config_ok(*cfg, &code)) return code;
+  if ((code = weights_ok(*cfg, *w)) != COLI_MOE_OK) return code;
+  if (T > cfg->max_tokens) return COLI_MOE_ECAPACITY;
+  const Layout L = layout_of(*cfg);
+  if (L.total > (size_t)COLI_MOE_STATIC_SCRATCH_BYTES) return COLI_MOE_ECAPACITY;
+  if (T == 0) return COLI_MOE_OK;
+  if (!hidden || !out || !aligned(hidden, 16) || !aligned(out, 16)) return COLI_MOE_EARG;
+  char *ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) return COLI_MOE_EDEVICE;
+  coli_moe_t m;  // on the stack: no host allocation either
+  set_up(&m, *cfg, *w, ws, L);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (stage(&m, s) != hipSuccess) return COLI_MOE_EDEVICE;
+  return coli_moe_forward(&m, hidden, out, T, stream);
 }
 
 void coli_moe_free(coli_moe_t *m) {

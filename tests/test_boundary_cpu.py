@@ -128,3 +128,26 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(cm, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="build it"):
         cm.load_library()
+
+
+def test_forward_noalloc_host_checks():
+    """The allocation-free forward rejects bad arguments, over-capacity
+    calls and configurations whose workspace exceeds the library's static
+    device array before any HIP call; a zero-token call is a dry run."""
+    lib = cm.load_library()
+    w = _weights()
+    limit = cm.COLI_MOE_STATIC_SCRATCH_BYTES
+    assert 0 < cm.coli_moe_workspace_bytes(_cfg(max_tokens=64)) <= limit
+    assert cm.coli_moe_workspace_bytes(_cfg(max_tokens=163)) <= limit < cm.coli_moe_workspace_bytes(_cfg(max_tokens=164))
+    f = lib.coli_moe_forward_noalloc
+    assert f(None, ctypes.byref(w), 0x1000, 0x2000, 1, None) == -4
+    assert f(ctypes.byref(_cfg()), None, 0x1000, 0x2000, 1, None) == -4
+    assert f(ctypes.byref(_cfg(n_group=2)), ctypes.byref(w), 0x1000, 0x2000, 1, None) == -2
+    assert f(ctypes.byref(_cfg(max_tokens=64)), ctypes.byref(w), 0x1000, 0x2000, 65, None) == -1
+    assert f(ctypes.byref(_cfg(max_tokens=164)), ctypes.byref(w), 0x1000, 0x2000, 1, None) == -1
+    assert f(ctypes.byref(_cfg(max_tokens=64)), ctypes.byref(w), 0x1000, 0x2000, -1, None) == -4
+    assert f(ctypes.byref(_cfg(max_tokens=64)), ctypes.byref(w), 0x1000, 0x2000, 0, None) == 0
+    assert f(ctypes.byref(_cfg(max_tokens=64)), ctypes.byref(w), 0x1001, 0x2000, 1, None) == -4
+    with pytest.raises(cm.ColiMoeError) as ei:
+        cm.coli_moe_forward_noalloc(_cfg(max_tokens=164), w, 0x1000, 0x2000, 1)
+    assert ei.value.code == -1
