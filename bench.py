@@ -60,6 +60,9 @@ def parse():
                     help="run a plain 1 GiB device-to-device copy 5 times and exit")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill layer (T=4096, Zipf load): print its JSON object and exit")
+    ap.add_argument("--no-cache", action="store_true", help="skip the expert-cache rows")
+    ap.add_argument("--cache-only", action="store_true",
+                    help="only the expert-cache rows (host-backed GLM-like layer): print their JSON object and exit")
     return ap.parse_args()
 
 
@@ -196,6 +199,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.prefill_only:
         print(json.dumps(prefill(args, cm, torch, np, synth, dev)), flush=True)
+        return
+    if args.cache_only:
+        print(json.dumps(cache_rows(args, cm, torch, np, synth, dev)), flush=True)
         return
     shape = synth.GLM
     L, K, W = args.layers, args.steps, args.warmup
@@ -377,6 +383,9 @@ def main():
         result["prefill"]["mfma_gemm_frac_of_measured_mfma"] = round(
             result["prefill"]["mfma_gemm_tflops"] / peaks["mfma_bf16_TFLOPs"], 4)
 
+    if not args.no_extra and not args.no_cache:
+        result["expert_cache"] = cache_rows(args, cm, torch, np, synth, dev)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, shape, layers, dev)
 
@@ -424,6 +433,146 @@ def prefill(args, cm, torch, np, synth, dev):
     return res
 
 
+def cache_rows(args, cm, torch, np, synth, dev):
+    """The GLM-like layer with its 256 routed experts in pinned host memory
+    and an HBM expert cache of n slots, decode T = 1 on fresh N(0,1) inputs
+    (uniform routing, the hardest case for a cache): tokens/s against the
+    hit rate, and the host -> HBM copy rate.  Then router look-ahead prefetch
+    on two such layers whose inputs are correlated like consecutive layers of
+    a residual stream (x1 = x0 + 0.2 N(0,1)): the pair's tokens/s with and
+    without it, and its recall."""
+    shape = synth.GLM
+    h, E, k, I = shape.hidden, shape.n_experts, shape.top_k, shape.inter
+    eb = shape.expert_bytes
+
+    def host_layer(layer):
+        routed = synth.routed_tables(shape, args.seed, layer)
+        host = {n: torch.from_numpy(v).pin_memory() for n, v in routed.items()}
+        del routed
+        wr, b = synth.router(shape, args.seed, layer)
+        res = {"router_w": torch.from_numpy(wr).to(dev), "sel_bias": torch.from_numpy(b).to(dev)}
+        res.update({"sh_" + n: torch.from_numpy(v).to(dev) for n, v in synth.shared_tables(shape, args.seed, layer).items()})
+        return res, host
+
+    cfg = cm.make_config(hidden=h, n_experts=E, top_k=k, inter=I, n_shared=shape.n_shared,
+                         routed_scaling_factor=shape.rsf, max_tokens=1)
+    t0 = time.time()
+    res0, host0 = host_layer(0)
+    log(f"cache bench: layer 0 in pinned host memory ({time.time() - t0:.1f} s)")
+    xs = [torch.from_numpy(synth.hidden(shape, args.seed, 1, layer=0, batch=5000 + i)).to(dev) for i in range(64)]
+    out = torch.empty((1, h), dtype=torch.float32, device=dev)
+    rows = []
+    for n_slots in (256, 128, 64, 32):
+        C = cm.ExpertCache(cfg, res0, host0, n_slots)
+        warm = 256 if n_slots == E else 32
+        for i in range(warm):
+            C(xs[i % 64], out)
+        torch.cuda.synchronize()
+        s0 = C.stats()
+        n = 64
+        t = time.perf_counter()
+        for i in range(n):
+            C(xs[(warm + i) % 64], out)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+        s1 = C.stats()
+        need = s1["needed"] - s0["needed"]
+        hits = s1["hits"] - s0["hits"]
+        copied = s1["bytes_copied"] - s0["bytes_copied"]
+        rows.append({"n_slots": n_slots, "hbm_GB": round(n_slots * eb / 1e9, 2), "tokens_per_s": round(n / dt, 1),
+                     "us_per_call": round(1e6 * dt / n, 1), "hit_rate": round(hits / need, 4),
+                     "host_to_hbm_GBps": round(copied / dt / 1e9, 2)})
+        log(f"cache {rows[-1]}")
+        C.close()
+        del C
+    # PILOT on two correlated layers, 32 slots each
+    res1, host1 = host_layer(1)
+    rng = np.random.default_rng(args.seed)
+    pairs = []
+    for i in range(64):
+        x0 = synth.hidden(shape, args.seed, 1, layer=0, batch=6000 + i)
+        x1 = (x0 + 0.2 * rng.standard_normal(x0.shape)).astype(np.float32)
+        pairs.append((torch.from_numpy(x0).to(dev), torch.from_numpy(x1).to(dev)))
+    pilot = {}
+    for use in (False, True):
+        C0, C1 = cm.ExpertCache(cfg, res0, host0, 32), cm.ExpertCache(cfg, res1, host1, 32)
+
+        def step(i):
+            x0, x1 = pairs[i % 64]
+            if use:
+                C1.prefetch(x0, k)
+            C0(x0, out)
+            C1(x1, out)
+
+        for i in range(16):
+            step(i)
+        torch.cuda.synchronize()
+        a0, b0 = C1.stats(), C0.stats()
+        n = 48
+        t = time.perf_counter()
+        for i in range(n):
+            step(16 + i)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+        a1 = C1.stats()
+        key = "with_prefetch" if use else "without_prefetch"
+        pilot[key] = {"tokens_per_s_two_layers": round(n / dt, 1), "us_per_token_two_layers": round(1e6 * dt / n, 1),
+                      "layer1_hit_rate": round((a1["hits"] - a0["hits"]) / (a1["needed"] - a0["needed"]), 4)}
+        if use:
+            pilot[key]["layer1_prefetch_recall"] = round(
+                (a1["prefetch_hits"] - a0["prefetch_hits"]) / (a1["needed"] - a0["needed"]), 4)
+        log(f"pilot {key}: {pilot[key]}")
+        C0.close()
+        C1.close()
+    del host0, host1
+    return {"workload": "GLM-5.2-like layer, 256 routed experts (21.2 MB each) in pinned host memory, "
+                        "decode T=1 on fresh N(0,1) inputs (uniform routing)",
+            "expert_bytes": eb, "slots": rows,
+            "router_lookahead_prefetch": dict(pilot, slots_per_layer=32,
+                                              inputs="x1 = x0 + 0.2 N(0,1) (consecutive-layer correlation)")}
+
+
+def host_cpu():
+    """The host's CPU as lscpu and /proc/cpuinfo describe it: model string,
+    sockets, physical cores, logical CPUs."""
+    import subprocess
+    info = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        kv = dict(ln.split(":", 1) for ln in out.splitlines() if ":" in ln)
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        info["model_name"] = kv.get("Model name", "")
+        for key, name in (("Socket(s)", "sockets"), ("Core(s) per socket", "cores_per_socket"),
+                          ("Thread(s) per core", "threads_per_core"), ("CPU(s)", "logical_cpus")):
+            if kv.get(key, "").isdigit():
+                info[name] = int(kv[key])
+        if "sockets" in info and "cores_per_socket" in info:
+            info["physical_cores"] = info["sockets"] * info["cores_per_socket"]
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    try:
+        cores, fields = set(), {}
+        phys = None
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ":" not in ln:
+                    continue
+                k, v = (x.strip() for x in ln.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v
+                if k == "physical id":
+                    phys = v
+                if k == "core id":
+                    cores.add((phys, v))
+        info["cpuinfo"] = fields
+        if cores and "physical_cores" not in info:
+            info["physical_cores"] = len(cores)
+    except OSError:
+        pass
+    info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    return info
+
+
 def cpu_baseline(args, shape, layers, dev):
     """The oracle, as it stands, on a bounded sample of the same workload:
     single decode tokens of layer 0, until the time budget is spent.  The
@@ -457,14 +606,10 @@ def cpu_baseline(args, shape, layers, dev):
         rms = np.sqrt((r ** 2).mean(axis=-1, keepdims=True))
         worst = max(worst, float((np.abs(got - r) / np.maximum(np.abs(r), rms)).max()))
         done += 1
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
-    return {"value": round(done / spent, 4), "unit": "tokens/s", "cores": oracle.threads(),
-            "cpu_model": model, "kind": "oracle",
+    cpu = host_cpu()
+    return {"value": round(done / spent, 4), "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "cores_meaning": "OpenMP threads the oracle ran on (one per logical CPU it may use)",
+            "host_cpu": cpu,
             "sample": f"{done} decode calls of T=1 on layer 0 (routing + 8 routed + shared expert "
                       f"FFNs in float64), {spent:.1f} s",
             "gpu_max_rel_err_on_sample": worst}

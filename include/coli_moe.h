@@ -236,6 +236,141 @@ int coli_moe_profile_end(coli_moe_t *m, float *kernel_ms, int32_t *kernel_launch
 /* Name of kernel i (0 <= i < COLI_MOE_N_KERNELS), a static string. */
 const char *coli_moe_kernel_name(int32_t i);
 
+/*
+ * ---------------------------------------------------------------------------
+ * HBM expert cache with host-RAM backing (three tiers: HBM slots, pinned host
+ * memory, and -- outside this library -- disk).  Source: "Colibri 调优与运行时
+ * 旋钮实战指南" (tuning and runtime knobs guide), sections on the resource
+ * plan (hot / warm / cold tiers, a per-layer expert LRU), online re-pinning
+ * (LFRU score of decayed frequency and recency, at most four swaps, 25%
+ * hysteresis) and the learning cache (.coli_usage routing counts, hottest
+ * experts pinned); "colibrì 引擎拆解" (engine teardown), "System map".
+ *
+ * A cache handle is one layer whose routed experts live in host memory and
+ * are copied on demand into n_slots HBM slots.  Each forward runs the router,
+ * selection and dispatch on the device, reads the call's expert list back
+ * (the host waits for `stream` once per call), copies the misses from the
+ * host tables into slots on the cache's own copy stream, and then runs the
+ * expert kernels on the slots: outputs are bit for bit those of
+ * coli_moe_forward on fully resident tables.  Every call runs the
+ * float32-accumulate GEMV path (prefill_threshold is ignored).  A cache's
+ * calls must be issued on one stream (or serialised by the caller).
+ * ---------------------------------------------------------------------------
+ */
+typedef struct coli_moe_cache coli_moe_cache_t; /* opaque */
+
+/* The routed experts of one layer in HOST memory that stays valid for the
+ * cache's lifetime, stacked as in coli_moe_weights_t ([n_experts][...]),
+ * 16-byte aligned.  Pinned memory (hipHostMalloc) is needed for the copies to
+ * run asynchronously. */
+typedef struct {
+  const uint8_t *gate_q;
+  const float *gate_s;
+  const uint8_t *up_q;
+  const float *up_s;
+  const uint8_t *down_q;
+  const float *down_s;
+} coli_moe_host_experts_t;
+
+typedef struct {
+  int32_t n_slots;     /* experts resident in HBM at once: min(E, top_k * max_tokens) .. n_experts */
+  int32_t repin_every; /* a re-pinning round every this many forwards; 0 = never */
+  float decay;         /* per-forward decay of the expert frequencies, (0, 1]; 0 = 0.9 */
+} coli_moe_cache_config_t;
+
+typedef struct {
+  int64_t calls;         /* forwards */
+  int64_t needed;        /* sum over forwards of the distinct experts routed to */
+  int64_t hits;          /* of those, resident when the forward began (prefetched ones included) */
+  int64_t misses;        /* copied in by the forward itself */
+  int64_t prefetched;    /* copied in by coli_moe_cache_prefetch */
+  int64_t prefetch_hits; /* prefetched experts that the next forward routed to */
+  int64_t evictions;     /* slots overwritten */
+  int64_t repin_swaps;   /* re-pinning swaps */
+  int64_t bytes_copied;  /* host -> HBM expert bytes */
+  int32_t pinned, resident;
+} coli_moe_cache_stats_t;
+
+/* DEVICE bytes for n_slots slots (the slot tables and the slot map); 0 when
+ * the configuration or n_slots is invalid. */
+size_t coli_moe_cache_slot_bytes(const coli_moe_config_t *cfg, int32_t n_slots);
+
+/*
+ * Create a cache handle.  `resident` holds the DEVICE router, selection bias
+ * and shared expert (its routed tables are ignored); `host` the routed
+ * experts; `slots` caller-owned DEVICE memory of coli_moe_cache_slot_bytes
+ * bytes and `workspace` of coli_moe_workspace_bytes bytes (both 256-byte
+ * aligned).  The library allocates its pinned staging buffers, events and
+ * copy stream here (host and event resources, no device memory).
+ * Errors: -4 bad argument, -2 routing configuration, -1 n_slots below
+ * min(E, top_k * max_tokens) or memory too small, -3 HIP error.
+ */
+int coli_moe_cache_init(coli_moe_cache_t **out, const coli_moe_config_t *cfg, const coli_moe_cache_config_t *cc,
+                        const coli_moe_weights_t *resident, const coli_moe_host_experts_t *host, void *slots,
+                        size_t slot_bytes, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The layer forward through the cache (see above).  Errors as
+ * coli_moe_forward. */
+int coli_moe_cache_forward(coli_moe_cache_t *c, const float *hidden, float *out, int32_t T, void *stream);
+
+/*
+ * Router look-ahead prefetch (PILOT): runs this cache's router, selection and
+ * dispatch on `hidden` [T][h] (DEVICE) -- the state the previous layer
+ * consumes, a stand-in for this layer's own input -- and starts copying the
+ * first n_predict selected experts of every token that are not resident,
+ * without waiting for the copies.  They stay guarded from eviction until the
+ * next forward of this cache, which counts them as hits.  Source: tuning
+ * guide, "路由器前瞻预取" (router look-ahead prefetch: layer L+1's router on
+ * layer L's state recalls 71.6% of the true top-8; PILOT_K experts per step;
+ * PILOT_EVICT_GUARD).  1 <= n_predict <= top_k.  Errors as
+ * coli_moe_forward.
+ */
+int coli_moe_cache_prefetch(coli_moe_cache_t *c, const float *hidden, int32_t T, int32_t n_predict, void *stream);
+
+/* Pin HOST-listed experts (copying in those not resident), in order, until
+ * the pin budget (n_slots - min(E, top_k * max_tokens)) is full.  Returns the
+ * number pinned, or -4 / -3. */
+int coli_moe_cache_pin(coli_moe_cache_t *c, const int32_t *experts, int32_t n, void *stream);
+
+/* Counters; per-expert routing counts of the cache's lifetime (HOST int64
+ * [n_experts], the learning cache's signal); the slot of each expert (HOST
+ * int32 [n_experts], -1 = not resident).  Return 0 or -4. */
+int coli_moe_cache_stats(const coli_moe_cache_t *c, coli_moe_cache_stats_t *stats);
+int coli_moe_cache_usage(const coli_moe_cache_t *c, int64_t *counts);
+int coli_moe_cache_slots(const coli_moe_cache_t *c, int32_t *slot_of);
+
+/* The layer handle the cache runs (for coli_moe_last_routing and the
+ * profiling calls); owned by the cache. */
+coli_moe_t *coli_moe_cache_layer(coli_moe_cache_t *c);
+
+/* Release the cache (waits for its copies).  NULL is a no-op. */
+void coli_moe_cache_free(coli_moe_cache_t *c);
+
+/*
+ * Usage history file (text; the learning cache's record): header records
+ * "-1 n_layers n_experts" and "-2 1 <engine id>" (coli_moe_usage_engine_id(),
+ * FNV-1a 32 of the engine name), then one "layer expert count" record per
+ * non-zero count; an empty history is an empty file.  Readers skip records
+ * whose first field is negative and is not -1 / -2, and reject files of other
+ * dimensions or engines (-2).  counts: HOST int64 [n_layers][n_experts].
+ * Source: tuning guide, learning-cache section (.coli_usage format).
+ * write returns 0 or -4; read the number of count records, or -4 / -2.
+ */
+uint32_t coli_moe_usage_engine_id(void);
+int coli_moe_usage_write(const char *path, int32_t n_layers, int32_t n_experts, const int64_t *counts);
+int coli_moe_usage_read(const char *path, int32_t n_layers, int32_t n_experts, int64_t *counts);
+
+/*
+ * Test only: the cache's residency policy alone, on the host.  Pins `pins`,
+ * then plays n_calls calls, call i needing call_len[i] distinct experts taken
+ * in order from `calls`; miss_out[i] receives call i's misses and slot_out
+ * (HOST [n_experts], may be NULL) the final slot of each expert.  Returns the
+ * re-pinning swaps, or -4 / -1.
+ */
+int coli_moe_test_cache_policy(int32_t n_experts, int32_t n_slots, int32_t reserve, float decay, int32_t repin_every,
+                               const int32_t *pins, int32_t n_pins, const int32_t *calls, const int32_t *call_len,
+                               int32_t n_calls, int32_t *miss_out, int32_t *slot_out);
+
 /* Static description of an error code. */
 const char *coli_moe_error_string(int32_t code);
 

@@ -50,6 +50,23 @@ class coli_moe_weights_t(ctypes.Structure):
         "sh_gate_q", "sh_gate_s", "sh_up_q", "sh_up_s", "sh_down_q", "sh_down_s")]
 
 
+class coli_moe_host_experts_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")]
+
+
+class coli_moe_cache_config_t(ctypes.Structure):
+    _fields_ = [("n_slots", ctypes.c_int32), ("repin_every", ctypes.c_int32), ("decay", ctypes.c_float)]
+
+
+class coli_moe_cache_stats_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("calls", "needed", "hits", "misses", "prefetched", "prefetch_hits",
+                                               "evictions", "repin_swaps", "bytes_copied")] + \
+               [("pinned", ctypes.c_int32), ("resident", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
 _lib = None
 
 
@@ -91,6 +108,35 @@ def load_library():
         L.coli_moe_kernel_name.restype = ctypes.c_char_p
         L.coli_moe_error_string.argtypes = [i32]
         L.coli_moe_error_string.restype = ctypes.c_char_p
+        hp, ccp = ctypes.POINTER(coli_moe_host_experts_t), ctypes.POINTER(coli_moe_cache_config_t)
+        L.coli_moe_cache_slot_bytes.argtypes = [cfgp, i32]
+        L.coli_moe_cache_slot_bytes.restype = sz
+        L.coli_moe_cache_init.argtypes = [ctypes.POINTER(vp), cfgp, ccp, wp, hp, vp, sz, vp, sz, vp]
+        L.coli_moe_cache_init.restype = ctypes.c_int
+        L.coli_moe_cache_forward.argtypes = [vp, vp, vp, i32, vp]
+        L.coli_moe_cache_forward.restype = ctypes.c_int
+        L.coli_moe_cache_prefetch.argtypes = [vp, vp, i32, i32, vp]
+        L.coli_moe_cache_prefetch.restype = ctypes.c_int
+        L.coli_moe_cache_pin.argtypes = [vp, vp, i32, vp]
+        L.coli_moe_cache_pin.restype = ctypes.c_int
+        L.coli_moe_cache_stats.argtypes = [vp, ctypes.POINTER(coli_moe_cache_stats_t)]
+        L.coli_moe_cache_stats.restype = ctypes.c_int
+        L.coli_moe_cache_usage.argtypes = [vp, vp]
+        L.coli_moe_cache_usage.restype = ctypes.c_int
+        L.coli_moe_cache_slots.argtypes = [vp, vp]
+        L.coli_moe_cache_slots.restype = ctypes.c_int
+        L.coli_moe_cache_layer.argtypes = [vp]
+        L.coli_moe_cache_layer.restype = vp
+        L.coli_moe_cache_free.argtypes = [vp]
+        L.coli_moe_cache_free.restype = None
+        L.coli_moe_usage_engine_id.argtypes = []
+        L.coli_moe_usage_engine_id.restype = ctypes.c_uint32
+        L.coli_moe_usage_write.argtypes = [ctypes.c_char_p, i32, i32, vp]
+        L.coli_moe_usage_write.restype = ctypes.c_int
+        L.coli_moe_usage_read.argtypes = [ctypes.c_char_p, i32, i32, vp]
+        L.coli_moe_usage_read.restype = ctypes.c_int
+        L.coli_moe_test_cache_policy.argtypes = [i32, i32, i32, ctypes.c_float, i32, vp, i32, vp, vp, i32, vp, vp]
+        L.coli_moe_test_cache_policy.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -183,6 +229,96 @@ def coli_moe_profile_end(handle):
     return calls, {coli_moe_kernel_name(i): (float(ms[i]), int(n[i])) for i in range(COLI_MOE_N_KERNELS)}
 
 
+def coli_moe_cache_slot_bytes(cfg: coli_moe_config_t, n_slots: int) -> int:
+    return int(load_library().coli_moe_cache_slot_bytes(ctypes.byref(cfg), int(n_slots)))
+
+
+def coli_moe_cache_init(cfg, cache_cfg, resident, host, slots: int, slot_bytes: int, workspace: int,
+                        workspace_bytes: int, stream: int = 0):
+    h = ctypes.c_void_p()
+    _check(load_library().coli_moe_cache_init(ctypes.byref(h), ctypes.byref(cfg), ctypes.byref(cache_cfg),
+                                              ctypes.byref(resident), ctypes.byref(host), slots, slot_bytes,
+                                              workspace, workspace_bytes, stream), "coli_moe_cache_init")
+    return h
+
+
+def coli_moe_cache_forward(cache, hidden: int, out: int, T: int, stream: int = 0) -> int:
+    return _check(load_library().coli_moe_cache_forward(cache, hidden, out, int(T), stream), "coli_moe_cache_forward")
+
+
+def coli_moe_cache_prefetch(cache, hidden: int, T: int, n_predict: int, stream: int = 0) -> int:
+    return _check(load_library().coli_moe_cache_prefetch(cache, hidden, int(T), int(n_predict), stream),
+                  "coli_moe_cache_prefetch")
+
+
+def coli_moe_cache_pin(cache, experts, stream: int = 0) -> int:
+    arr = (ctypes.c_int32 * len(experts))(*[int(e) for e in experts])
+    return _check(load_library().coli_moe_cache_pin(cache, arr, len(experts), stream), "coli_moe_cache_pin")
+
+
+def coli_moe_cache_stats(cache) -> dict:
+    st = coli_moe_cache_stats_t()
+    _check(load_library().coli_moe_cache_stats(cache, ctypes.byref(st)), "coli_moe_cache_stats")
+    return st.as_dict()
+
+
+def coli_moe_cache_usage(cache, n_experts: int):
+    arr = (ctypes.c_int64 * n_experts)()
+    _check(load_library().coli_moe_cache_usage(cache, arr), "coli_moe_cache_usage")
+    return [int(v) for v in arr]
+
+
+def coli_moe_cache_slots(cache, n_experts: int):
+    arr = (ctypes.c_int32 * n_experts)()
+    _check(load_library().coli_moe_cache_slots(cache, arr), "coli_moe_cache_slots")
+    return [int(v) for v in arr]
+
+
+def coli_moe_cache_layer(cache):
+    return load_library().coli_moe_cache_layer(cache)
+
+
+def coli_moe_cache_free(cache) -> None:
+    load_library().coli_moe_cache_free(cache)
+
+
+def coli_moe_usage_engine_id() -> int:
+    return int(load_library().coli_moe_usage_engine_id())
+
+
+def coli_moe_usage_write(path: str, counts) -> int:
+    """counts: int64 array [n_layers][n_experts] (numpy)."""
+    import numpy as np
+    c = np.ascontiguousarray(counts, dtype=np.int64)
+    return _check(load_library().coli_moe_usage_write(path.encode(), c.shape[0], c.shape[1], c.ctypes.data),
+                  "coli_moe_usage_write")
+
+
+def coli_moe_usage_read(path: str, n_layers: int, n_experts: int):
+    """Returns (records, counts int64 [n_layers][n_experts])."""
+    import numpy as np
+    c = np.zeros((n_layers, n_experts), np.int64)
+    n = _check(load_library().coli_moe_usage_read(path.encode(), n_layers, n_experts, c.ctypes.data),
+               "coli_moe_usage_read")
+    return n, c
+
+
+def coli_moe_test_cache_policy(n_experts, n_slots, reserve, decay, repin_every, pins, calls):
+    """The residency policy alone; `calls` is a list of expert lists.
+    Returns (repin swaps, misses per call, final slot per expert)."""
+    flat = [int(e) for c in calls for e in c]
+    lens = [len(c) for c in calls]
+    pa = (ctypes.c_int32 * max(1, len(pins)))(*[int(e) for e in pins])
+    ca = (ctypes.c_int32 * max(1, len(flat)))(*flat)
+    la = (ctypes.c_int32 * max(1, len(lens)))(*lens)
+    miss = (ctypes.c_int32 * max(1, len(calls)))()
+    slots = (ctypes.c_int32 * n_experts)()
+    rc = _check(load_library().coli_moe_test_cache_policy(n_experts, n_slots, reserve, decay, repin_every, pa,
+                                                          len(pins), ca, la, len(calls), miss, slots),
+                "coli_moe_test_cache_policy")
+    return rc, [int(miss[i]) for i in range(len(calls))], [int(v) for v in slots]
+
+
 # ---------------------------------------------------------------------------
 # Convenience wrapper over torch device tensors.
 # ---------------------------------------------------------------------------
@@ -253,6 +389,89 @@ class MoELayer:
     def close(self):
         if getattr(self, "handle", None) is not None:
             coli_moe_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class ExpertCache:
+    """One layer whose routed experts live in pinned host memory, copied on
+    demand into `n_slots` HBM slots (torch device tensors hold the slots and
+    the workspace).  `resident` maps router_w, sel_bias and sh_* to device
+    tensors; `host` maps gate_q ... down_s to pinned host tensors."""
+
+    def __init__(self, cfg: coli_moe_config_t, resident: dict, host: dict, n_slots: int, repin_every: int = 0,
+                 decay: float = 0.0, stream: int | None = None):
+        import torch
+        self.cfg, self.resident, self.host = cfg, resident, host
+        dev = resident["router_w"].device
+        w = coli_moe_weights_t()
+        for name, _ in coli_moe_weights_t._fields_:
+            t = resident.get(name)
+            setattr(w, name, None if t is None else t.data_ptr())
+        hx = coli_moe_host_experts_t()
+        for name, _ in coli_moe_host_experts_t._fields_:
+            setattr(hx, name, host[name].data_ptr())
+        self.weights, self.hx = w, hx
+        sb = coli_moe_cache_slot_bytes(cfg, n_slots)
+        wb = coli_moe_workspace_bytes(cfg)
+        if sb == 0 or wb == 0:
+            raise ColiMoeError(COLI_MOE_EARG, "coli_moe_cache_slot_bytes")
+        self.slots = torch.empty(sb, dtype=torch.uint8, device=dev)
+        self.workspace = torch.empty(wb, dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev).cuda_stream if stream is None else stream
+        cc = coli_moe_cache_config_t(n_slots=n_slots, repin_every=repin_every, decay=decay)
+        self.handle = coli_moe_cache_init(cfg, cc, w, hx, self.slots.data_ptr(), sb, self.workspace.data_ptr(), wb,
+                                          self.stream)
+
+    def forward(self, hidden, out=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(hidden)
+        coli_moe_cache_forward(self.handle, hidden.data_ptr(), out.data_ptr(), hidden.shape[0], self.stream)
+        return out
+
+    __call__ = forward
+
+    def prefetch(self, hidden, n_predict: int):
+        return coli_moe_cache_prefetch(self.handle, hidden.data_ptr(), hidden.shape[0], n_predict, self.stream)
+
+    def pin(self, experts):
+        return coli_moe_cache_pin(self.handle, experts, self.stream)
+
+    def stats(self) -> dict:
+        return coli_moe_cache_stats(self.handle)
+
+    def usage(self):
+        return coli_moe_cache_usage(self.handle, self.cfg.n_experts)
+
+    def slot_map(self):
+        return coli_moe_cache_slots(self.handle, self.cfg.n_experts)
+
+    def last_routing(self):
+        """Device tensors of the last forward's routing and dispatch."""
+        import torch
+        layer = coli_moe_cache_layer(self.handle)
+        dev = self.workspace.device
+        k, E = self.cfg.top_k, self.cfg.n_experts
+        T = coli_moe_last_routing(layer, stream=self.stream)
+        n = T * k
+        i32 = dict(dtype=torch.int32, device=dev)
+        r = dict(idx=torch.empty(n, **i32), w=torch.empty(n, dtype=torch.float32, device=dev),
+                 offsets=torch.empty(E + 1, **i32), sorted_ids=torch.empty(n, **i32),
+                 inv=torch.empty(n, **i32), active=torch.empty(E, **i32), n_active=torch.empty(1, **i32))
+        coli_moe_last_routing(layer, *(r[key].data_ptr() for key in
+                                       ("idx", "w", "offsets", "sorted_ids", "inv", "active", "n_active")),
+                              stream=self.stream)
+        return T, r
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            coli_moe_cache_free(self.handle)
             self.handle = None
 
     def __del__(self):

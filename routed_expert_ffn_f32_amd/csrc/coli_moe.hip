@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "coli_moe.h"
+#include "handle.h"
 #include "internal.h"
 
 namespace {
@@ -40,14 +41,6 @@ const char *const kKernelNames[COLI_MOE_N_KERNELS] = {
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
-
-// Byte offsets of the workspace regions.
-struct Layout {
-  size_t wrP, logits, xq, xs, idx, w, offsets, sorted_ids, inv, active, n_active, mq, ms, midf, y;
-  size_t xb, xexp, xn2, midb, pstats, tiles, n_tiles;  // prefill path
-  size_t queues;                    // row queues of the small-batch gate/up launch
-  size_t total;
-};
 
 // The prefill (MFMA) path takes h and I multiples of 256, and half
 // activation buffers ([max_tokens][h] and [P][I]) under 4 GiB, since its
@@ -121,25 +114,9 @@ Layout layout_of(const coli_moe_config_t &c) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-struct ProfRecord {
-  int kernel;
-  hipEvent_t start, stop;
-};
 
 }  // namespace
 
-struct coli_moe {
-  coli_moe_config_t cfg;
-  coli_moe_weights_t w;
-  char *ws;
-  Layout L;
-  int last_T;
-  // profiling
-  int prof_calls_left;
-  int prof_calls_done;
-  std::vector<ProfRecord> prof;
-  size_t prof_used;
-};
 
 namespace coli {
 thread_local LaunchEvents launch_events = {nullptr, nullptr};
@@ -221,6 +198,7 @@ void set_up(coli_moe_t *m, const coli_moe_config_t &cfg, const coli_moe_weights_
   m->prof_calls_left = 0;
   m->prof_calls_done = 0;
   m->prof_used = 0;
+  m->slot_of = nullptr;
 }
 
 // The workspace state every forward starts from: the lane-permuted router,
@@ -263,45 +241,16 @@ hipError_t scratch_of_current_device(char **out) {
 
 }  // namespace
 
+namespace coli {
 
-extern "C" {
-
-size_t coli_moe_workspace_bytes(const coli_moe_config_t *cfg) {
-  int code;
-  if (!cfg || !config_ok(*cfg, &code)) return 0;
-  return layout_of(*cfg).total;
-}
-
-int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe_weights_t *w,
-                  void *workspace, size_t workspace_bytes, void *stream) {
-  if (!out || !cfg || !w || !workspace) return COLI_MOE_EARG;
-  *out = nullptr;
-  int code = COLI_MOE_OK;
-  if (!config_ok(*cfg, &code)) return code;
-  if ((code = weights_ok(*cfg, *w)) != COLI_MOE_OK) return code;
-  if (!aligned(workspace, kAlign)) return COLI_MOE_EARG;
-  const Layout L = layout_of(*cfg);
-  if (workspace_bytes < L.total) return COLI_MOE_ECAPACITY;
-
-  coli_moe_t *m = new (std::nothrow) coli_moe_t();
-  if (!m) return COLI_MOE_EARG;
-  set_up(m, *cfg, *w, static_cast<char *>(workspace), L);
-  if (stage(m, static_cast<hipStream_t>(stream)) != hipSuccess) {
-    delete m;
-    return COLI_MOE_EDEVICE;
-  }
-  *out = m;
-  return COLI_MOE_OK;
-}
-
-int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, void *stream) {
+int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hipStream_t s, int phase) {
   if (!m || T < 0) return COLI_MOE_EARG;
   if (T > m->cfg.max_tokens) return COLI_MOE_ECAPACITY;
   if (T == 0) return COLI_MOE_OK;
-  if (!hidden || !out || !aligned(hidden, 16) || !aligned(out, 16)) return COLI_MOE_EARG;
+  if (!hidden || !aligned(hidden, 16)) return COLI_MOE_EARG;
+  if ((phase & kPhaseExperts) && (!out || !aligned(out, 16))) return COLI_MOE_EARG;
   const coli_moe_config_t &c = m->cfg;
   const Layout &L = m->L;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int E = c.n_experts, k = c.top_k, h = c.hidden, I = c.inter;
   float *logits = at<float>(m, L.logits);
   uint32_t *xq = at<uint32_t>(m, L.xq);
@@ -319,11 +268,13 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
   const bool small = !prefill && coli::small_batch(T, k, h, I);
   hipError_t e;
   // 1. router logits (and, for the GEMV path, the hidden rows in digit-plane
-  // form); small batches compute both inside their gate/up launch
-  e = timed(m, K_ROUTER_LOGITS, s, [&] {
-    return coli::launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill ? nullptr : xq, xs, s);
-  });
-  if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  // form)
+  if (phase & kPhaseRoute) {
+    e = timed(m, K_ROUTER_LOGITS, s, [&] {
+      return launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill ? nullptr : xq, xs, s);
+    });
+    if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  }
   // Selection and dispatch: one workgroup does both while each of its waves
   // selects at most one token (its counting sort then reads the choices from
   // LDS); larger batches select one token per wave over many workgroups,
@@ -333,32 +284,40 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
       static_assert(coli::kDispatchThreads / coli::kWave * coli::kMaxTopK <= coli::kFusedDispatchMax,
                     "the fused launch's LDS holds every choice");
       return timed(m, K_ROUTER_SELECT, s, [&] {
-        return coli::launch_select_dispatch(logits, bias, T, E, k, rsf, idx, wsel, offsets, sorted_ids, inv,
+        return launch_select_dispatch(logits, bias, T, E, k, rsf, idx, wsel, offsets, sorted_ids, inv,
                                             active, n_active, s);
       });
     }
     hipError_t err = timed(m, K_ROUTER_SELECT, s,
-                           [&] { return coli::launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
+                           [&] { return launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
     if (err != hipSuccess) return err;
     return timed(m, K_DISPATCH, s, [&] {
-      return coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
+      return launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
     });
   };
+  // Routing alone (phase kPhaseRoute without kPhaseExperts): selection and
+  // dispatch written to the workspace, for the host to read.
+  if (!(phase & kPhaseExperts)) {
+    if (select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
+    m->last_T = T;
+    return COLI_MOE_OK;
+  }
+  const bool routed = !(phase & kPhaseRoute);  // selection and dispatch already in the workspace
   if (prefill) {
     // 2. selection and dispatch, 3. half activations and the tile list,
     // 4. grouped GEMMs on MFMA, 5. weighted combine
-    if (select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
+    if (!routed && select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
     coli::PrefillProblem Q = prefill_problem(m, T);
-    e = timed(m, K_PREFILL_PREP, s, [&] { return coli::launch_prefill_prep(hidden, T, h, Q, s); });
+    e = timed(m, K_PREFILL_PREP, s, [&] { return launch_prefill_prep(hidden, T, h, Q, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    e = timed(m, K_BUILD_TILES, s, [&] { return coli::launch_build_tiles(Q, s); });
+    e = timed(m, K_BUILD_TILES, s, [&] { return launch_build_tiles(Q, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    e = timed(m, K_MFMA_GATE_UP, s, [&] { return coli::launch_gate_up_mfma(Q, s); });
+    e = timed(m, K_MFMA_GATE_UP, s, [&] { return launch_gate_up_mfma(Q, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    e = timed(m, K_MFMA_DOWN, s, [&] { return coli::launch_down_mfma(Q, s); });
+    e = timed(m, K_MFMA_DOWN, s, [&] { return launch_down_mfma(Q, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     e = timed(m, K_COMBINE, s,
-              [&] { return coli::launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
+              [&] { return launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     m->last_T = T;
     if (m->prof_calls_left > 0) {
@@ -398,23 +357,24 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
   P.active = active;
   P.n_active = n_active;
   P.queues = at<int32_t>(m, L.queues);
+  P.slot_of = m->slot_of;
 
   if (small) {
     // 2. gate/up (each block routes the batch itself), 3. down + combine
-    e = timed(m, K_GATE_UP, s, [&] { return coli::launch_gemv_gate_up(P, s); });
+    e = timed(m, K_GATE_UP, s, [&] { return launch_gemv_gate_up(P, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    e = timed(m, K_DOWN, s, [&] { return coli::launch_down_combine(P, out, s); });
+    e = timed(m, K_DOWN, s, [&] { return launch_down_combine(P, out, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
   } else {
     // 2. selection and dispatch
-    if (select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
+    if (!routed && select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
     // 3. gate/up, down, weighted combine
-    e = timed(m, K_GATE_UP, s, [&] { return coli::launch_gemv_gate_up(P, s); });
+    e = timed(m, K_GATE_UP, s, [&] { return launch_gemv_gate_up(P, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    e = timed(m, K_DOWN, s, [&] { return coli::launch_gemv_down(P, s); });
+    e = timed(m, K_DOWN, s, [&] { return launch_gemv_down(P, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     e = timed(m, K_COMBINE, s,
-              [&] { return coli::launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
+              [&] { return launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
   }
 
@@ -424,6 +384,54 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
     ++m->prof_calls_done;
   }
   return COLI_MOE_OK;
+}
+
+int config_check(const coli_moe_config_t &c) {
+  int code = COLI_MOE_OK;
+  return config_ok(c, &code) ? COLI_MOE_OK : code;
+}
+int weights_check(const coli_moe_config_t &cfg, const coli_moe_weights_t &w) { return weights_ok(cfg, w); }
+Layout workspace_layout(const coli_moe_config_t &c) { return layout_of(c); }
+void handle_set_up(coli_moe_t *m, const coli_moe_config_t &cfg, const coli_moe_weights_t &w, char *ws,
+                   const Layout &L) {
+  set_up(m, cfg, w, ws, L);
+}
+hipError_t handle_stage(coli_moe_t *m, hipStream_t s) { return stage(m, s); }
+
+}  // namespace coli
+
+extern "C" {
+
+size_t coli_moe_workspace_bytes(const coli_moe_config_t *cfg) {
+  int code;
+  if (!cfg || !config_ok(*cfg, &code)) return 0;
+  return layout_of(*cfg).total;
+}
+
+int coli_moe_init(coli_moe_t **out, const coli_moe_config_t *cfg, const coli_moe_weights_t *w,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+  if (!out || !cfg || !w || !workspace) return COLI_MOE_EARG;
+  *out = nullptr;
+  int code = COLI_MOE_OK;
+  if (!config_ok(*cfg, &code)) return code;
+  if ((code = weights_ok(*cfg, *w)) != COLI_MOE_OK) return code;
+  if (!aligned(workspace, kAlign)) return COLI_MOE_EARG;
+  const Layout L = layout_of(*cfg);
+  if (workspace_bytes < L.total) return COLI_MOE_ECAPACITY;
+
+  coli_moe_t *m = new (std::nothrow) coli_moe_t();
+  if (!m) return COLI_MOE_EARG;
+  set_up(m, *cfg, *w, static_cast<char *>(workspace), L);
+  if (stage(m, static_cast<hipStream_t>(stream)) != hipSuccess) {
+    delete m;
+    return COLI_MOE_EDEVICE;
+  }
+  *out = m;
+  return COLI_MOE_OK;
+}
+
+int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, void *stream) {
+  return coli::forward_phases(m, hidden, out, T, static_cast<hipStream_t>(stream), coli::kPhaseAll);
 }
 
 int coli_moe_forward_noalloc(const coli_moe_config_t *cfg, const coli_moe_weights_t *w, const float *hidden,

@@ -175,10 +175,11 @@ __device__ __forceinline__ Slot expert_slot(const DecodeProblem &P, int e, int p
   Slot S;
   S.p_begin = p_begin;
   S.cnt = cnt;
-  S.qa = P.gate.q + e * qstride;
-  S.sa = P.gate.s + e * sstride;
-  S.qb = P.up.q + e * qstride;
-  S.sb = P.up.s + e * sstride;
+  const size_t x = table_index(P.slot_of, e);
+  S.qa = P.gate.q + x * qstride;
+  S.sa = P.gate.s + x * sstride;
+  S.qb = P.up.q + x * qstride;
+  S.sb = P.up.s + x * sstride;
   return S;
 }
 
@@ -394,10 +395,11 @@ __device__ __forceinline__ void gu_set_slot(const DecodeProblem &P, const SmallR
   const int s = min(c.slot - hs, kSmallAssign - 1);
   const int e = uniform(R.active[s]);
   const size_t qstride = (size_t)P.I * (P.h >> 1), sstride = (size_t)P.I * (P.h >> 6);
-  c.qg = P.gate.q + e * qstride;
-  c.sg = P.gate.s + e * sstride;
-  c.qu = P.up.q + e * qstride;
-  c.su = P.up.s + e * sstride;
+  const size_t x = table_index(P.slot_of, e);
+  c.qg = P.gate.q + x * qstride;
+  c.sg = P.gate.s + x * sstride;
+  c.qu = P.up.q + x * qstride;
+  c.su = P.up.s + x * sstride;
   c.p_begin = uniform(R.seg_begin[s]);
   c.cnt = uniform(R.seg_begin[s + 1]) - c.p_begin;
 }
@@ -719,8 +721,9 @@ __device__ __forceinline__ DnSlot dn_slot(const DecodeProblem &P, const DnTable 
   d.t = qs / (P.k + P.has_shared);
   const int e = uniform(D.e[qs]);
   if (e >= 0) {
-    d.q = P.down.q + e * ((size_t)P.h * (P.I >> 1));
-    d.s = P.down.s + e * ((size_t)P.h * (P.I >> 6));
+    const size_t x = table_index(P.slot_of, e);
+    d.q = P.down.q + x * ((size_t)P.h * (P.I >> 1));
+    d.s = P.down.s + x * ((size_t)P.h * (P.I >> 6));
   } else {
     d.q = P.sh_down.q;
     d.s = P.sh_down.s;
@@ -984,8 +987,8 @@ __global__ __launch_bounds__(kDnWaves * 64) void down_kernel(DecodeProblem P) {
     if (slot >= *P.n_active) return;
     const int e = P.active[slot];
     const size_t qstride = (size_t)P.h * (P.I >> 1), sstride = (size_t)P.h * (P.I >> 6);
-    q = P.down.q + e * qstride;
-    s = P.down.s + e * sstride;
+    q = P.down.q + table_index(P.slot_of, e) * qstride;
+    s = P.down.s + table_index(P.slot_of, e) * sstride;
     p_begin = P.offsets[e];
     cnt = P.offsets[e + 1] - p_begin;
   }
@@ -1018,8 +1021,8 @@ __global__ __launch_bounds__(64) void down_tok_kernel(DecodeProblem P) {
     if (slot >= *P.n_active) return;
     const int e = P.active[slot];
     const size_t qstride = (size_t)P.h * (P.I >> 1), sstride = (size_t)P.h * (P.I >> 6);
-    q = P.down.q + e * qstride;
-    s = P.down.s + e * sstride;
+    q = P.down.q + table_index(P.slot_of, e) * qstride;
+    s = P.down.s + table_index(P.slot_of, e) * sstride;
     p_begin = P.offsets[e];
     cnt = P.offsets[e + 1] - p_begin;
   }

@@ -84,6 +84,13 @@ struct ExpertTables {
   const float *s;    // [rows][cols/64] per expert
 };
 
+// Index of routed expert e's tables in the stacked arrays: e itself, or its
+// cache slot when the tables are the slots of an expert cache (slot_of[e],
+// valid for every expert a call routes to).
+__device__ __forceinline__ size_t table_index(const int32_t *slot_of, int e) {
+  return (size_t)(slot_of ? slot_of[e] : e);
+}
+
 struct DecodeProblem {
   ExpertTables gate, up, down;           // routed experts, stacked
   ExpertTables sh_gate, sh_up, sh_down;  // shared expert
@@ -106,6 +113,7 @@ struct DecodeProblem {
   // small batches: row queues of the gate/up launch (kRowQueueWords int32,
   // zero when it starts; the down launch clears them again)
   int32_t *queues;
+  const int32_t *slot_of;  // expert -> table index (NULL: identity)
 };
 constexpr int kRowQueueWords = 64 * 64;
 

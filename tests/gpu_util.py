@@ -62,6 +62,10 @@ class DeviceLayer:
             return [{k: v[e] for k, v in self.host_routed.items()} if e in experts else None for e in range(E)]
         return [synth.expert(self.shape, self.seed, e, self.layer) if e in experts else None for e in range(E)]
 
+    def oracle_route(self, x_rows: np.ndarray) -> np.ndarray:
+        idx, _ = oracle.route(self.shape, self.wr, self.bias, x_rows)
+        return idx
+
     def oracle_forward(self, x_rows: np.ndarray):
         idx, _ = oracle.route(self.shape, self.wr, self.bias, x_rows)
         needed = set(int(e) for e in np.unique(idx))
