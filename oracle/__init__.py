@@ -65,6 +65,8 @@ def _load():
         L.coli_oracle_router_logits.restype = i32
         L.coli_oracle_select.argtypes = [vp, vp, i32, i32, i32, f32, vp, vp]
         L.coli_oracle_select.restype = i32
+        L.coli_oracle_select_limited.argtypes = [vp, vp, i32, i32, i32, i32, f32, f32, vp, vp]
+        L.coli_oracle_select_limited.restype = i32
         L.coli_oracle_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.coli_oracle_dispatch.restype = i32
         L.coli_oracle_unpack_code.argtypes = [vp, i32]
@@ -73,6 +75,8 @@ def _load():
         L.coli_oracle_expert_ffn.restype = None
         L.coli_oracle_forward.argtypes = [ctypes.POINTER(Layer), vp, i32, vp, vp, vp]
         L.coli_oracle_forward.restype = i32
+        L.coli_oracle_forward_limited.argtypes = [ctypes.POINTER(Layer), vp, i32, i32, f32, vp, vp, vp]
+        L.coli_oracle_forward_limited.restype = i32
         L.coli_oracle_threads.argtypes = []
         L.coli_oracle_threads.restype = i32
         _lib = L
@@ -111,15 +115,21 @@ def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
     return out
 
 
-def select(logits: np.ndarray, bias, k: int, rsf: float):
-    """Returns (idx [T,k] int32, w [T,k] float32)."""
+def select(logits: np.ndarray, bias, k: int, rsf: float, k_use: int | None = None, top_p: float = 1.0):
+    """Returns (idx [T,k] int32, w [T,k] float32).  k_use / top_p: the
+    run-time routing limits (dropped slots: idx -1, w 0)."""
     logits = _f32(logits)
     T, E = logits.shape
     b = None if bias is None else _f32(bias)
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float32)
-    rc = _load().coli_oracle_select(logits.ctypes.data, None if b is None else b.ctypes.data,
-                                    T, E, k, rsf, idx.ctypes.data, w.ctypes.data)
+    if k_use is None and top_p == 1.0:
+        rc = _load().coli_oracle_select(logits.ctypes.data, None if b is None else b.ctypes.data,
+                                        T, E, k, rsf, idx.ctypes.data, w.ctypes.data)
+    else:
+        rc = _load().coli_oracle_select_limited(logits.ctypes.data, None if b is None else b.ctypes.data,
+                                                T, E, k, k if k_use is None else k_use, top_p, rsf,
+                                                idx.ctypes.data, w.ctypes.data)
     if rc:
         raise ValueError(f"coli_oracle_select: {rc}")
     return idx, w
@@ -173,12 +183,14 @@ def expert_ffn(tables: dict, x: np.ndarray) -> np.ndarray:
     return y
 
 
-def forward(shape, wr, bias, routed: dict | list, shared: dict | None, x: np.ndarray):
+def forward(shape, wr, bias, routed: dict | list, shared: dict | None, x: np.ndarray,
+            k_use: int | None = None, top_p: float = 1.0):
     """The layer forward on tokens x [T, h].
 
     `routed` is either stacked tables (dict of [E, ...] arrays) or a list of E
-    per-expert dicts (None for experts no token selects).  Returns
-    (out [T, h] float32, idx [T, k] int32, w [T, k] float32)."""
+    per-expert dicts (None for experts no token selects).  k_use / top_p: the
+    run-time routing limits.  Returns (out [T, h] float32, idx [T, k] int32,
+    w [T, k] float32)."""
     x = _f32(x)
     T, h = x.shape
     E, k = shape.n_experts, shape.top_k
@@ -201,13 +213,17 @@ def forward(shape, wr, bias, routed: dict | list, shared: dict | None, x: np.nda
     out = np.empty((T, h), np.float32)
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float32)
-    rc = _load().coli_oracle_forward(ctypes.byref(L), x.ctypes.data, T, out.ctypes.data,
-                                     idx.ctypes.data, w.ctypes.data)
+    if k_use is None and top_p == 1.0:
+        rc = _load().coli_oracle_forward(ctypes.byref(L), x.ctypes.data, T, out.ctypes.data,
+                                         idx.ctypes.data, w.ctypes.data)
+    else:
+        rc = _load().coli_oracle_forward_limited(ctypes.byref(L), x.ctypes.data, T, k if k_use is None else k_use,
+                                                 top_p, out.ctypes.data, idx.ctypes.data, w.ctypes.data)
     if rc:
         raise ValueError(f"coli_oracle_forward: {rc}")
     return out, idx, w
 
 
-def route(shape, wr, bias, x):
+def route(shape, wr, bias, x, k_use: int | None = None, top_p: float = 1.0):
     """Routing only: (idx, w) for tokens x."""
-    return select(router_logits(x, wr), bias, shape.top_k, shape.rsf)
+    return select(router_logits(x, wr), bias, shape.top_k, shape.rsf, k_use, top_p)

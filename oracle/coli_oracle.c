@@ -30,6 +30,10 @@
  *       for MoE models", section 2.2 -- routing yields a [batch, top_k]
  *       integer index array; section 3.1 -- router stored as a
  *       [hidden_size, num_experts] float32 matrix.
+ *  [K]  "Colibri 调优与运行时旋钮实战指南" (Colibri tuning and runtime knobs
+ *       guide), the knob table (explicit
+ *       smaller k and adaptive expert top-p, lossy overrides of the
+ *       routing).
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes of the repository):
@@ -187,11 +191,30 @@ static int key_cmp(const void *a, const void *b) {
  * Source: [T] "Three key engineering decisions" item 1 (sigmoid, noaux_tc,
  * n_group = 1, routed_scaling_factor); [P] section 2.2 ([batch, top_k]
  * index array).
+ *
+ * Run-time routing limits: two lossy overrides of the routing, an explicit
+ * smaller k and adaptive expert top-p, named as engine knobs in the knob
+ * table of [K] (top-p cuts the
+ * expert bytes streamed; both are warned about as lossy).  The page names
+ * the knobs and their effect only; the readings here:
+ *  - k_use < k: the k_use experts first in the order above are the
+ *    candidates, in slots 0..k_use-1; den sums their scores; slots
+ *    k_use..k-1 are dropped;
+ *  - top-p, 0 < p < 1: in slot order, cum_j = ((s_0 + s_1) + ...) + s_(j-1)
+ *    is the score of the candidates before slot j (float32, cum_0 = 0);
+ *    slot 0 is always kept and slot j >= 1 is kept while cum_j < p * den
+ *    (one float32 product), so the kept slots are the shortest prefix whose
+ *    score reaches the share p of the candidates' score.  p = 1: no top-p;
+ *  - the m kept slots are renormalised over themselves:
+ *    w_j = (s_j / cum_m) * rsf, cum_m summed in slot order as above;
+ *  - a dropped slot has idx -1 and w 0.
+ * With k_use = k and p = 1 this is the selection above.
+ * Returns -2 for k or k_use out of [1, E] / [1, k], or p outside (0, 1].
  */
-int coli_oracle_select(const float *logits, const float *bias, int32_t T, int32_t E, int32_t k,
-                       float rsf, int32_t *idx, float *w) {
+int coli_oracle_select_limited(const float *logits, const float *bias, int32_t T, int32_t E, int32_t k,
+                               int32_t k_use, float top_p, float rsf, int32_t *idx, float *w) {
   if (T < 0 || E <= 0 || !logits || !idx || !w) return ORACLE_EINVAL;
-  if (k < 1 || k > E) return ORACLE_EROUTE;
+  if (k < 1 || k > E || k_use < 1 || k_use > k || !(top_p > 0.0f && top_p <= 1.0f)) return ORACLE_EROUTE;
   sel_key_t *keys = (sel_key_t *)malloc(sizeof(sel_key_t) * (size_t)E);
   float *s = (float *)malloc(sizeof(float) * (size_t)E);
   if (!keys || !s) {
@@ -208,15 +231,38 @@ int coli_oracle_select(const float *logits, const float *bias, int32_t T, int32_
     }
     qsort(keys, (size_t)E, sizeof(sel_key_t), key_cmp);
     float den = 0.0f;
-    for (int32_t j = 0; j < k; j++) den = den + s[keys[j].e];
+    for (int32_t j = 0; j < k_use; j++) den = den + s[keys[j].e];
+    int32_t m = k_use;
+    float kept = den;
+    if (top_p < 1.0f) {
+      const float thr = top_p * den;
+      m = 1;
+      kept = s[keys[0].e];
+      while (m < k_use && kept < thr) {
+        kept = kept + s[keys[m].e];
+        m++;
+      }
+    }
     for (int32_t j = 0; j < k; j++) {
-      idx[(size_t)t * k + j] = keys[j].e;
-      w[(size_t)t * k + j] = (s[keys[j].e] / den) * rsf;
+      const size_t a = (size_t)t * k + j;
+      if (j < m) {
+        idx[a] = keys[j].e;
+        w[a] = (s[keys[j].e] / kept) * rsf;
+      } else {
+        idx[a] = -1;
+        w[a] = 0.0f;
+      }
     }
   }
   free(keys);
   free(s);
   return ORACLE_OK;
+}
+
+int coli_oracle_select(const float *logits, const float *bias, int32_t T, int32_t E, int32_t k,
+                       float rsf, int32_t *idx, float *w) {
+  if (k < 1 || k > E) return (T < 0 || E <= 0 || !logits || !idx || !w) ? ORACLE_EINVAL : ORACLE_EROUTE;
+  return coli_oracle_select_limited(logits, bias, T, E, k, k, 1.0f, rsf, idx, w);
 }
 
 /* ---------------------------------------------------------------------- */
@@ -226,10 +272,14 @@ int coli_oracle_select(const float *logits, const float *bias, int32_t T, int32_
 /*
  * Assignment a = t*k + j (token t, slot j) goes to expert idx[a].
  * counts[e] = number of a with idx[a] == e; offsets = exclusive prefix sum
- * (E + 1 entries, offsets[E] = T*k); sorted_ids lists the a grouped by
- * expert ascending and, inside a group, by a ascending; inv[a] is the
- * position of a in sorted_ids; active lists the experts with counts > 0 in
- * ascending order, n_active of them.
+ * (E + 1 entries); sorted_ids lists the a grouped by expert ascending and,
+ * inside a group, by a ascending; inv[a] is the position of a in
+ * sorted_ids; active lists the experts with counts > 0 in ascending order,
+ * n_active of them.
+ * A negative idx[a] is a dropped slot (routing limits): it goes to no
+ * expert, and the dropped assignments follow all the groups in sorted_ids
+ * (a ascending), so offsets[E] is the number of kept assignments (T*k when
+ * none is dropped).
  * Source: [C] section 3.3 step 3 (per-expert counts, prefix sum to offsets,
  * scatter by expert id) and section 2.2 (grouping example).
  */
@@ -242,16 +292,17 @@ int coli_oracle_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, in
   int64_t n = (int64_t)T * k;
   for (int32_t e = 0; e < E; e++) counts[e] = 0;
   for (int64_t a = 0; a < n; a++) {
-    if (idx[a] < 0 || idx[a] >= E) return ORACLE_EROUTE;
-    counts[idx[a]]++;
+    if (idx[a] >= E) return ORACLE_EROUTE;
+    if (idx[a] >= 0) counts[idx[a]]++;
   }
   offsets[0] = 0;
   for (int32_t e = 0; e < E; e++) offsets[e + 1] = offsets[e] + counts[e];
   int32_t *fill = (int32_t *)calloc((size_t)E, sizeof(int32_t));
   if (!fill) return -1;
+  int32_t dropped = 0;
   for (int64_t a = 0; a < n; a++) {
     int32_t e = idx[a];
-    int32_t pos = offsets[e] + fill[e]++;
+    int32_t pos = e >= 0 ? offsets[e] + fill[e]++ : offsets[E] + dropped++;
     sorted_ids[pos] = (int32_t)a;
     inv[a] = pos;
   }
@@ -343,17 +394,19 @@ typedef struct {
  * active expert over its group, then the weighted assembly per token
  * ([C] section 3.3 steps 2-5; [T] "Task flow example").
  * idx_out / w_out (optional) receive the routing, [T][k].
- * Returns 0, -1 (allocation), -2 (k out of range), -4 (bad argument or an
- * expert table missing for a selected expert).
+ * k_use / top_p: the run-time routing limits of coli_oracle_select_limited
+ * (k_use = k, top_p = 1: none); dropped slots have no FFN and add nothing.
+ * Returns 0, -1 (allocation), -2 (k, k_use or top_p out of range), -4 (bad
+ * argument or an expert table missing for a selected expert).
  */
-int coli_oracle_forward(const coli_oracle_layer_t *L, const float *x, int32_t T, float *out,
-                        int32_t *idx_out, float *w_out) {
+int coli_oracle_forward_limited(const coli_oracle_layer_t *L, const float *x, int32_t T, int32_t k_use,
+                                float top_p, float *out, int32_t *idx_out, float *w_out) {
   if (!L || T < 0 || (T > 0 && (!x || !out))) return ORACLE_EINVAL;
   const int32_t h = L->hidden, E = L->n_experts, k = L->top_k, I = L->inter;
   if (h <= 0 || h % 64 || I <= 0 || I % 64 || E <= 0 || !L->router_w || !L->experts ||
       (L->n_shared != 0 && L->n_shared != 1))
     return ORACLE_EINVAL;
-  if (k < 1 || k > E) return ORACLE_EROUTE;
+  if (k < 1 || k > E || k_use < 1 || k_use > k || !(top_p > 0.0f && top_p <= 1.0f)) return ORACLE_EROUTE;
   if (T == 0) return ORACLE_OK;
   int rc = ORACLE_OK;
   size_t n = (size_t)T * k;
@@ -374,7 +427,7 @@ int coli_oracle_forward(const coli_oracle_layer_t *L, const float *x, int32_t T,
   }
   int32_t n_active = 0;
   coli_oracle_router_logits(x, L->router_w, T, h, E, logits);
-  rc = coli_oracle_select(logits, L->sel_bias, T, E, k, L->routed_scaling_factor, idx, w);
+  rc = coli_oracle_select_limited(logits, L->sel_bias, T, E, k, k_use, top_p, L->routed_scaling_factor, idx, w);
   if (rc) goto done;
   rc = coli_oracle_dispatch(idx, T, k, E, counts, offsets, sorted_ids, inv, active, &n_active);
   if (rc) goto done;
@@ -385,10 +438,11 @@ int coli_oracle_forward(const coli_oracle_layer_t *L, const float *x, int32_t T,
       goto done;
     }
   }
-  /* expert FFN over each group: position p of the sorted order holds
-   * assignment a = sorted_ids[p] of token a / k */
+  /* expert FFN over each group: position p < offsets[E] of the sorted order
+   * holds assignment a = sorted_ids[p] of token a / k (the positions after
+   * offsets[E] are dropped slots) */
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t p = 0; p < (int64_t)n; p++) {
+  for (int64_t p = 0; p < (int64_t)offsets[E]; p++) {
     int32_t a = sorted_ids[p];
     coli_oracle_expert_ffn(&L->experts[idx[a]], h, I, x + (size_t)(a / k) * h, y + (size_t)p * h);
   }
@@ -407,7 +461,7 @@ int coli_oracle_forward(const coli_oracle_layer_t *L, const float *x, int32_t T,
       double acc = 0.0;
       for (int32_t j = 0; j < k; j++) {
         size_t a = (size_t)t * k + j;
-        acc += (double)w[a] * y[(size_t)inv[a] * h + r];
+        if (idx[a] >= 0) acc += (double)w[a] * y[(size_t)inv[a] * h + r];
       }
       if (L->n_shared) acc += ysh[(size_t)t * h + r];
       out[(size_t)t * h + r] = (float)acc;
@@ -427,6 +481,12 @@ done:
   free(y);
   free(ysh);
   return rc;
+}
+
+int coli_oracle_forward(const coli_oracle_layer_t *L, const float *x, int32_t T, float *out, int32_t *idx_out,
+                        float *w_out) {
+  if (!L) return ORACLE_EINVAL;
+  return coli_oracle_forward_limited(L, x, T, L->top_k, 1.0f, out, idx_out, w_out);
 }
 
 /* Threads the oracle's parallel loops use (for reporting). */

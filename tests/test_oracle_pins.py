@@ -230,6 +230,104 @@ def test_n_group_one_equals_plain_topk():
 
 
 # --------------------------------------------------------------------------
+# Run-time routing limits: explicit smaller k, adaptive expert top-p.
+# --------------------------------------------------------------------------
+
+def test_limits_off_equal_plain_selection():
+    rng = np.random.default_rng(41)
+    logits = (1.6 * rng.standard_normal((20, 64))).astype(np.float32)
+    bias = (0.05 * rng.standard_normal(64)).astype(np.float32)
+    i0, w0 = oracle.select(logits, bias, 8, 2.5)
+    i1, w1 = oracle.select(logits, bias, 8, 2.5, k_use=8, top_p=1.0)
+    assert np.array_equal(i0, i1) and np.array_equal(w0.view(np.uint32), w1.view(np.uint32))
+
+
+@pytest.mark.parametrize("E,k,k_use", [(64, 8, 4), (256, 8, 1), (16, 6, 5)])
+def test_smaller_k_is_brute_force_topk_of_that_k(E, k, k_use):
+    """An explicit smaller k routes exactly like a layer built with that k
+    (brute-force full sort), in the first k_use slots; the rest are dropped."""
+    rng = np.random.default_rng(E + k_use)
+    T = 12
+    logits = (1.6 * rng.standard_normal((T, E))).astype(np.float32)
+    bias = (0.05 * rng.standard_normal(E)).astype(np.float32)
+    idx, w = oracle.select(logits, bias, k, 1.5, k_use=k_use)
+    bi, bw = _brute_select(logits, bias, k_use, 1.5)
+    assert np.array_equal(idx[:, :k_use], bi)
+    assert np.array_equal(w[:, :k_use].view(np.uint32), bw.view(np.uint32))
+    assert np.all(idx[:, k_use:] == -1) and np.all(w[:, k_use:] == 0)
+
+
+def test_top_p_closed_forms():
+    """Scores that are exact in float32: a logit of 20 gives s = 1 (e^-20 is
+    below half an ulp of 1), a logit of 0 gives s = 1/2.  Logits
+    [20, 0, 0, 20, 0, -3], no bias, k = 4: slots hold experts 0, 3, 1, 2
+    (ties by index) with scores 1, 1, 1/2, 1/2, total 3.  Keeping the
+    shortest prefix whose score reaches p of the total, renormalised:
+      p = 0.25 -> 1 slot (1 >= 0.75), weight rsf;
+      p = 0.5  -> 2 slots (2 >= 1.5), weights rsf/2 each;
+      p = 2/3  -> 2 slots: float32(2/3) * 3 rounds to exactly 2, which the
+                  first two slots reach (reaching the share is enough);
+      p = 0.7  -> 3 slots (2 < 2.1 <= 2.5), weights 2/5, 2/5, 1/5 of rsf;
+      p = 0.9  -> 4 slots (2.5 < 2.7), weights 1/3, 1/3, 1/6, 1/6 of rsf;
+    and with k_use = 3 first (total 2.5), p = 0.9 -> 3 slots (2 < 2.25)."""
+    logits = np.array([[20.0, 0.0, 0.0, 20.0, 0.0, -3.0]], np.float32)
+    rsf = 2.5
+    assert np.float32(np.float32(2 / 3) * np.float32(3)) == np.float32(2)
+    cases = [(4, 0.25, [1.0]), (4, 0.5, [0.5, 0.5]), (4, 2 / 3, [0.5, 0.5]), (4, 0.7, [0.4, 0.4, 0.2]),
+             (4, 0.9, [1 / 3, 1 / 3, 1 / 6, 1 / 6]), (3, 0.9, [0.4, 0.4, 0.2])]
+    for k_use, p, frac in cases:
+        idx, w = oracle.select(logits, None, 4, rsf, k_use=k_use, top_p=p)
+        m = len(frac)
+        assert idx[0].tolist() == [0, 3, 1, 2][:m] + [-1] * (4 - m), (k_use, p)
+        assert np.allclose(w[0, :m], np.array(frac) * rsf, rtol=2e-7, atol=0), (k_use, p)
+        assert np.all(w[0, m:] == 0)
+
+
+def test_top_p_invariants_and_monotone():
+    """On random scores: the kept slots are a prefix of the plain selection,
+    the shortest one whose score reaches the share p (checked in float64
+    with a margin of a few float32 roundings), weights sum to rsf and keep
+    the ratios of the scores, and a larger p never keeps fewer slots."""
+    rng = np.random.default_rng(9)
+    E, k, rsf, T = 256, 8, 2.5, 48
+    logits = (1.6 * rng.standard_normal((T, E))).astype(np.float32)
+    bias = (0.05 * rng.standard_normal(E)).astype(np.float32)
+    i_all, _ = oracle.select(logits, bias, k, rsf)
+    s = 1.0 / (1.0 + np.exp(-logits.astype(np.float64)))
+    prev_m = np.ones(T, int)
+    for p in (0.05, 0.3, 0.5, 0.7, 0.9, 0.99):
+        idx, w = oracle.select(logits, bias, k, rsf, top_p=p)
+        m = (idx >= 0).sum(axis=1)
+        assert np.all(m >= 1) and np.all(m >= prev_m)
+        prev_m = m
+        for t in range(T):
+            mt = m[t]
+            assert np.array_equal(idx[t, :mt], i_all[t, :mt]) and np.all(idx[t, mt:] == -1)
+            st = s[t, i_all[t]]
+            cum = np.cumsum(st) / st.sum()
+            margin = 1e-6
+            assert cum[mt - 1] >= p - margin
+            if mt > 1:
+                assert cum[mt - 2] < p + margin
+            assert abs(float(w[t, :mt].astype(np.float64).sum()) - rsf) <= 2 * k * 2.0 ** -23 * rsf
+            assert np.allclose(w[t, :mt] / w[t, 0], st[:mt] / st[0], rtol=2e-6, atol=0)
+
+
+def test_top_p_tiny_keeps_one_slot_with_weight_rsf():
+    rng = np.random.default_rng(3)
+    logits = (1.6 * rng.standard_normal((16, 64))).astype(np.float32)
+    idx, w = oracle.select(logits, None, 8, 2.5, top_p=1e-6)
+    assert np.all(idx[:, 1:] == -1) and np.all(w[:, 0] == np.float32(2.5)) and np.all(w[:, 1:] == 0)
+
+
+def test_limits_reject_out_of_range():
+    logits = np.zeros((2, 8), np.float32)
+    for kw in (dict(k_use=0), dict(k_use=5), dict(top_p=0.0), dict(top_p=1.5), dict(top_p=-0.2)):
+        with pytest.raises(ValueError, match="-2"):
+            oracle.select(logits, None, 4, 1.0, **kw)
+
+
+# --------------------------------------------------------------------------
 # Dispatch: the pages' worked examples, invariants, brute force.
 # --------------------------------------------------------------------------
 
@@ -280,6 +378,34 @@ def test_dispatch_skewed_and_empty():
     assert d["n_active"] == 1 and d["counts"][0] == 40
     d0 = oracle.dispatch(np.zeros((0, 4), np.int32), E)
     assert d0["n_active"] == 0 and d0["offsets"].tolist() == [0] * (E + 1)
+
+
+def test_dispatch_dropped_slots_follow_all_groups():
+    """Dropped slots (idx -1) go to no expert: brute-force stable sort with
+    the dropped key placed after every expert; offsets[E] counts the kept
+    assignments and the dropped ones fill the tail in ascending order."""
+    rng = np.random.default_rng(77)
+    for T, k, E in ((1, 8, 256), (9, 4, 16), (64, 8, 64)):
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        m = rng.integers(1, k + 1, size=T)
+        for t in range(T):
+            idx[t, m[t]:] = -1
+        d = oracle.dispatch(idx, E)
+        flat = idx.reshape(-1)
+        n_kept = int((flat >= 0).sum())
+        brute = sorted(range(flat.size), key=lambda a: flat[a] if flat[a] >= 0 else E)
+        assert d["sorted_ids"].tolist() == brute
+        off = d["offsets"]
+        assert off[0] == 0 and off[E] == n_kept and np.all(np.diff(off) >= 0)
+        assert np.array_equal(np.diff(off), d["counts"])
+        assert d["sorted_ids"][n_kept:].tolist() == [a for a in range(flat.size) if flat[a] < 0]
+        assert np.array_equal(d["sorted_ids"][d["inv"]], np.arange(flat.size))
+        assert d["active"].tolist() == sorted(set(flat[flat >= 0].tolist()))
+    # every slot dropped but slot 0 of one token
+    idx = np.full((3, 2), -1, np.int32)
+    idx[1, 0] = 5
+    d = oracle.dispatch(idx, 8)
+    assert d["offsets"].tolist() == [0] * 6 + [1] * 3 and d["sorted_ids"].tolist() == [2, 0, 1, 3, 4, 5]
 
 
 # --------------------------------------------------------------------------
@@ -435,3 +561,26 @@ def test_forward_rejects_bad_k():
     routed = synth.routed_tables(shape, 1)
     with pytest.raises(ValueError, match="-2"):
         oracle.forward(shape, wr, b, routed, None, synth.hidden(shape, 1, 2))
+
+
+@pytest.mark.parametrize("k_use,top_p", [(8, 0.7), (3, 1.0), (5, 0.5)])
+def test_forward_with_routing_limits_equals_mixture_of_kept(k_use, top_p):
+    """With routing limits the output is the mixture of the kept experts
+    only, with the kept weights, plus the shared expert: computed here with
+    numpy float64 per token, no grouping; dropped slots add nothing."""
+    shape = synth.LayerShape(hidden=128, n_experts=16, top_k=8, inter=64, n_shared=1, rsf=2.5, bias_sigma=0.05)
+    wr, b = synth.router(shape, 23)
+    routed = synth.routed_tables(shape, 23)
+    sh = synth.shared_tables(shape, 23)
+    x = synth.hidden(shape, 23, 5)
+    out, idx, w = oracle.forward(shape, wr, b, routed, sh, x, k_use=k_use, top_p=top_p)
+    ri, rw = oracle.route(shape, wr, b, x, k_use=k_use, top_p=top_p)
+    assert np.array_equal(idx, ri) and np.array_equal(w, rw)
+    assert np.all((idx >= 0).sum(axis=1) <= k_use)
+    for t in range(x.shape[0]):
+        mix = _ffn_numpy(sh, x[t])
+        for j in range(shape.top_k):
+            if idx[t, j] >= 0:
+                te = {kk: v[idx[t, j]] for kk, v in routed.items()}
+                mix = mix + float(w[t, j]) * _ffn_numpy(te, x[t])
+        assert np.allclose(out[t], mix, rtol=1e-6, atol=1e-6 * np.abs(mix).max())
