@@ -11,8 +11,9 @@ change from call to call and the 256 MB Infinity Cache cannot serve them).
 Also measured in the same run (extra fields of the JSON line):
   decode_batches  the same 8-layer stack at T = 2, 4 and 64 tokens per call;
   prefill         T = 4096 tokens on the GLM-like layer with Zipf-skewed
-                  expert load (bf16 MFMA path): tokens/s and the grouped-GEMM
-                  kernels' FLOP rate against the bf16 dense peak.
+                  expert load (fp16 MFMA path): tokens/s and the grouped-GEMM
+                  kernels' FLOP rate against the fp16 dense peak and against
+                  the rate this GPU sustains on varied fp16 operands.
 
 Prints one JSON line: MoE-layer tokens/s (value), expert-weight HBM GB/s, the
 roofline of the dominant kernel (per-launch algorithmic bytes over its mean
@@ -37,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
-BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_gemv_gate_up.txt")
 # sources of the dominant kernel: a counter summary taken on other sources
 # describes other code
@@ -140,8 +141,10 @@ def kernel_profile(cm, handles, run, n_calls):
 def measured_peaks(cm, torch, dev):
     """This GPU's own rates, measured in the same run with the library's
     probes, beside the published peaks: the HBM read rate over an 8 GiB
-    buffer (every byte read once) and the back-to-back bf16 MFMA rate (one
-    wave per SIMD on every CU); each the best of five launches timed with
+    buffer (every byte read once), the back-to-back bf16 MFMA rate on
+    all-ones operands and the fp16 rate on operands that vary from one MFMA
+    to the next (one wave per SIMD on every CU; the clock falls with the
+    power that varied data draws); each the best of five launches timed with
     HIP events, each probe's result checked."""
     stream = torch.cuda.current_stream().cuda_stream
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -169,10 +172,18 @@ def measured_peaks(cm, torch, dev):
     torch.cuda.synchronize()
     waves_ok = int(sink.item())
     flops = blocks * 4 * iters * cm.MFMA_PROBE_MFMAS_PER_ROUND * 32768
+    iters16 = iters // 2
+    sink.zero_()
+    f16_ms = best_ms(lambda: cm.coli_moe_probe_mfma_f16(iters16, blocks, 12345, sink.data_ptr(), stream))
+    torch.cuda.synchronize()
+    waves16 = int(sink.item())
+    flops16 = blocks * 4 * iters16 * cm.MFMA_F16_PROBE_MFMAS_PER_ROUND * 32768
     return {"hbm_read_GBps": round(nbytes / (hbm_ms / 1e3) / 1e9, 1), "hbm_buffer_bytes": nbytes,
-            "mfma_bf16_TFLOPs": round(flops / (mfma_ms / 1e3) / 1e12, 1),
+            "mfma_bf16_ones_TFLOPs": round(flops / (mfma_ms / 1e3) / 1e12, 1),
             "mfma_probe_waves_checked": f"{waves_ok} of {6 * blocks * 4}",
-            "published": {"hbm_GBps": HBM_PEAK_GBPS, "bf16_dense_TFLOPs": BF16_PEAK_TFLOPS}}
+            "mfma_f16_varied_TFLOPs": round(flops16 / (f16_ms / 1e3) / 1e12, 1),
+            "mfma_f16_probe_waves_finite": f"{waves16} of {6 * blocks * 4}",
+            "published": {"hbm_GBps": HBM_PEAK_GBPS, "f16_bf16_dense_TFLOPs": F16_PEAK_TFLOPS}}
 
 
 def main():
@@ -380,8 +391,8 @@ def main():
     # ---- prefill on its own layer ------------------------------------------
     if not args.no_extra:
         result["prefill"] = prefill(args, cm, torch, np, synth, dev)
-        result["prefill"]["mfma_gemm_frac_of_measured_mfma"] = round(
-            result["prefill"]["mfma_gemm_tflops"] / peaks["mfma_bf16_TFLOPs"], 4)
+        result["prefill"]["mfma_gemm_frac_of_measured_f16_varied"] = round(
+            result["prefill"]["mfma_gemm_tflops"] / peaks["mfma_f16_varied_TFLOPs"], 4)
 
     if not args.no_extra and not args.no_cache:
         result["expert_cache"] = cache_rows(args, cm, torch, np, synth, dev)
@@ -419,14 +430,14 @@ def prefill(args, cm, torch, np, synth, dev):
     dn = kern.get("expert_mfma_down", (0.0, 1))
     gu_us, dn_us = 1e3 * gu[0] / gu[1], 1e3 * dn[0] / dn[1]
     mfma_tflops = (flops_gu + flops_dn) / ((gu_us + dn_us) * 1e-6) / 1e12
-    res = {"workload": f"GLM-5.2-like layer prefill T={T}, Zipf(1.1)-skewed expert load, bf16 MFMA path",
+    res = {"workload": f"GLM-5.2-like layer prefill T={T}, Zipf(1.1)-skewed expert load, fp16 MFMA path",
            "tokens_per_s": round(T * n / (ms / 1e3), 1),
            "ms_per_layer_call": round(ms / n, 3),
            "distinct_experts": n_active,
            "ffn_tflop_per_call": round((flops_gu + flops_dn) / 1e12, 4),
            "kernel_avg_us": {nm: round(1e3 * t / c, 2) for nm, (t, c) in kern.items()},
            "mfma_gemm_tflops": round(mfma_tflops, 1),
-           "mfma_gemm_frac_of_bf16_peak": round(mfma_tflops / BF16_PEAK_TFLOPS, 4)}
+           "mfma_gemm_frac_of_f16_peak": round(mfma_tflops / F16_PEAK_TFLOPS, 4)}
     lay.close()
     del tensors
     log(f"prefill: {res}")

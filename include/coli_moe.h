@@ -216,11 +216,19 @@ int coli_moe_probe_read(const coli_moe_t *m, const int32_t *experts, int32_t n, 
  * all-ones operands; each wave whose results all equal 16 * iters adds 1 to
  * the DEVICE word *sink.  1 <= iters < 2^20, 1 <= blocks <= 2^20.
  *
- * Both only enqueue on `stream`.  Errors: -4 NULL/misaligned pointer or a
- * size out of range, -3 HIP launch error.
+ * coli_moe_probe_mfma_f16 is the same launch shape with
+ * v_mfma_f32_32x32x16_f16 on operands that change from one MFMA to the next
+ * (pseudo-random halves derived from `seed`, |v| in [2^-4, 2^11)): each
+ * wave runs `iters` rounds of 16 MFMAs and adds 1 to *sink when all its
+ * accumulators are finite.  Power draw depends on the data, so this is the
+ * rate a GEMM on real operands can approach; the all-ones rate is higher.
+ *
+ * All three only enqueue on `stream`.  Errors: -4 NULL/misaligned pointer or
+ * a size out of range, -3 HIP launch error.
  */
 int coli_moe_probe_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 int coli_moe_probe_mfma(int32_t iters, int32_t blocks, uint32_t *sink, void *stream);
+int coli_moe_probe_mfma_f16(int32_t iters, int32_t blocks, uint32_t seed, uint32_t *sink, void *stream);
 
 /*
  * Kernel timing.  coli_moe_profile_begin makes the next `max_calls` forwards

@@ -100,6 +100,8 @@ def load_library():
         L.coli_moe_probe_stream.restype = ctypes.c_int
         L.coli_moe_probe_mfma.argtypes = [i32, i32, vp, vp]
         L.coli_moe_probe_mfma.restype = ctypes.c_int
+        L.coli_moe_probe_mfma_f16.argtypes = [i32, i32, ctypes.c_uint32, vp, vp]
+        L.coli_moe_probe_mfma_f16.restype = ctypes.c_int
         L.coli_moe_profile_begin.argtypes = [vp, i32]
         L.coli_moe_profile_begin.restype = ctypes.c_int
         L.coli_moe_profile_end.argtypes = [vp, vp, vp]
@@ -215,6 +217,17 @@ def coli_moe_probe_mfma(iters: int, blocks: int, sink: int, stream: int = 0) -> 
     """blocks x 4 waves of iters x 8 back-to-back bf16 MFMAs (32768 flops
     each); each wave whose results check adds 1 to the device word at sink."""
     return _check(load_library().coli_moe_probe_mfma(int(iters), int(blocks), sink, stream), "coli_moe_probe_mfma")
+
+
+MFMA_F16_PROBE_MFMAS_PER_ROUND = 16
+
+
+def coli_moe_probe_mfma_f16(iters: int, blocks: int, seed: int, sink: int, stream: int = 0) -> int:
+    """blocks x 4 waves of iters x 16 back-to-back f16 MFMAs on operands that
+    change from one MFMA to the next; each wave whose accumulators are all
+    finite adds 1 to the device word at sink."""
+    return _check(load_library().coli_moe_probe_mfma_f16(int(iters), int(blocks), int(seed) & 0xFFFFFFFF, sink, stream),
+                  "coli_moe_probe_mfma_f16")
 
 
 def coli_moe_profile_begin(handle, max_calls: int) -> int:

@@ -531,6 +531,14 @@ int coli_moe_probe_mfma(int32_t iters, int32_t blocks, uint32_t *sink, void *str
              : COLI_MOE_EDEVICE;
 }
 
+int coli_moe_probe_mfma_f16(int32_t iters, int32_t blocks, uint32_t seed, uint32_t *sink, void *stream) {
+  if (!sink || !aligned(sink, 4) || iters < 1 || iters >= (1 << 20) || blocks < 1 || blocks > (1 << 20))
+    return COLI_MOE_EARG;
+  return coli::launch_mfma_probe_f16(iters, blocks, seed, sink, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? COLI_MOE_OK
+             : COLI_MOE_EDEVICE;
+}
+
 int coli_moe_profile_begin(coli_moe_t *m, int32_t max_calls) {
   if (!m || max_calls < 0) return COLI_MOE_EARG;
   const size_t need = (size_t)max_calls * COLI_MOE_N_KERNELS;

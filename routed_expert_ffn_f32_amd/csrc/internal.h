@@ -136,6 +136,7 @@ constexpr int kProbeStreamBlocks = 256 * 8;
 constexpr int kMfmaChains = 8;  // MFMAs per round of the MFMA probe
 hipError_t launch_stream_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_mfma_probe(int iters, int blocks, uint32_t *sink, hipStream_t s);
+hipError_t launch_mfma_probe_f16(int iters, int blocks, uint32_t seed, uint32_t *sink, hipStream_t s);
 hipError_t launch_read_probe(const DecodeProblem &P, const int32_t *experts, int n, uint32_t *sink,
                              hipStream_t s);
 // Small batches: out[t] = sum_j w[t,j] Wd_e mid[inv(t,j)] + Wd_sh mid[T*k + t].
