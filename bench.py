@@ -388,6 +388,37 @@ def main():
             log(f"decode T={Tb}: {res[str(Tb)]}")
         result["decode_batches"] = res
 
+    # ---- run-time routing limits (lossy), decode T=1 on the same stack ------
+    if not args.no_extra:
+        import warnings
+        res = {}
+        for k_use, top_p in ((k, 0.7), (k, 0.5), (6, 1.0), (4, 1.0)):
+            with warnings.catch_warnings():
+                warnings.simplefilter("ignore")
+                for lay in layers:
+                    lay.set_routing(k_use, top_p)
+            pool = 16
+            xb, ob, na = make_pool(1, pool)
+            steps = max(20, K // 2)
+            run_stack(xb, ob, 0, 5)
+            ms = time_calls(torch, lambda s: run_stack(xb, ob, 5 + s, 1), steps)
+            n_calls = steps * L
+            reads = sum(int(na[l, ((5 + s) * L + l) % pool]) + shape.n_shared for s in range(steps) for l in range(L))
+            res[f"k{k_use}_p{top_p}"] = {"k_use": k_use, "top_p": top_p,
+                                         "tokens_per_s": round(n_calls / (ms / 1e3), 1),
+                                         "us_per_layer_call": round(1e3 * ms / n_calls, 2),
+                                         "mean_routed_experts_per_token": round(float(na.mean()), 2),
+                                         "expert_bytes_vs_plain": round((float(na.mean()) + shape.n_shared) / (k + shape.n_shared), 4),
+                                         "expert_weight_GBps": round(reads * eb / (ms / 1e3) / 1e9, 1)}
+            del xb, ob
+            log(f"routing limits {res[f'k{k_use}_p{top_p}']}")
+        for lay in layers:
+            lay.set_routing()
+        result["routing_limits_decode_T1"] = {
+            "note": "lossy overrides (explicit smaller k, adaptive expert top-p); the synthetic router's scores are "
+                    "nearly flat, so top-p keeps more experts here than a trained router's peaked scores would",
+            **res}
+
     # ---- prefill on its own layer ------------------------------------------
     if not args.no_extra:
         result["prefill"] = prefill(args, cm, torch, np, synth, dev)

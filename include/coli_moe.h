@@ -160,6 +160,32 @@ int coli_moe_forward(coli_moe_t *m, const float *hidden, float *out, int32_t T, 
 int coli_moe_forward_noalloc(const coli_moe_config_t *cfg, const coli_moe_weights_t *w, const float *hidden,
                              float *out, int32_t T, void *stream);
 
+/*
+ * Run-time routing limits of the handle's later forwards: two lossy
+ * overrides of the routing, an explicit smaller k and adaptive expert top-p
+ * ("Colibri 调优与运行时旋钮实战指南" -- Colibri tuning and runtime knobs
+ * guide -- knob table; the engine warns that both change the model's
+ * output).  1 <= k_use <= top_k, 0 < top_p <= 1; (top_k, 1) restores the
+ * plain routing (the default).  Per token:
+ *  - the k_use experts first in the selection order are the candidates,
+ *    in slots 0..k_use-1; den is the sum of their sigmoid scores, added in
+ *    slot order in float32;
+ *  - top_p < 1 keeps slot 0, then slot j while the candidates before it
+ *    score less than top_p * den (float32 product; the running sum in slot
+ *    order, float32): the shortest prefix of slots whose score reaches the
+ *    share top_p;
+ *  - the kept slots' weights are renormalised over them,
+ *    w_j = (s_j / kept sum) * routed_scaling_factor;
+ *  - the other slots of the k are dropped: idx -1, w 0, no expert work.
+ * The routing arrays keep their [T][top_k] layout; dispatch puts the
+ * dropped assignments after every expert's group in sorted_ids (ascending),
+ * so offsets[n_experts] counts the kept ones.  Dropped experts' weights are
+ * never read, which is the point: fewer expert bytes per token.  Not
+ * thread-safe with the handle's forwards (set it between calls on the
+ * handle's stream order).  Errors: -4 NULL handle, -2 out of range.
+ */
+int coli_moe_set_routing(coli_moe_t *m, int32_t k_use, float top_p);
+
 /* Release the handle (host memory only).  NULL is a no-op.  The caller must
  * make sure no enqueued forward of the handle is still running. */
 void coli_moe_free(coli_moe_t *m);
@@ -168,9 +194,10 @@ void coli_moe_free(coli_moe_t *m);
  * Copy the routing and dispatch of the handle's last forward (T tokens) into
  * caller DEVICE buffers, enqueued on `stream` (for parity checks).  Any
  * pointer may be NULL to skip it.  Sizes: idx and w [T*k] (assignment
- * a = t*k + j, slot order = selection rank), offsets [E+1], sorted_ids and
- * inv [T*k], active [E] (experts with tokens, ascending; n_active of them are
- * valid), n_active [1].  Returns the T of the last forward (>= 0) or -4.
+ * a = t*k + j, slot order = selection rank; -1 and 0 in slots the routing
+ * limits dropped), offsets [E+1], sorted_ids and inv [T*k], active [E]
+ * (experts with tokens, ascending; n_active of them are valid), n_active
+ * [1].  Returns the T of the last forward (>= 0) or -4.
  */
 int coli_moe_last_routing(const coli_moe_t *m, int32_t *idx, float *w, int32_t *offsets,
                           int32_t *sorted_ids, int32_t *inv, int32_t *active, int32_t *n_active,
@@ -178,11 +205,12 @@ int coli_moe_last_routing(const coli_moe_t *m, int32_t *idx, float *w, int32_t *
 
 /*
  * The dispatch kernel alone on caller data: a stable counting sort of the
- * assignments a = t*k + j of DEVICE idx [T*k] (values in [0, E)) by expert,
- * written to DEVICE offsets [E+1], sorted_ids [T*k], inv [T*k], active [E],
- * n_active [1] (same meaning as above).  1 <= E <= 512, 1 <= k <= 32,
- * 0 <= T*k <= 2^20.  (cf-1.com Colibri article, section 3.3, step 3.)
- * Errors: -4.  Out-of-range idx values give unspecified (but in-bounds)
+ * assignments a = t*k + j of DEVICE idx [T*k] (values in [0, E), or
+ * negative for a dropped slot) by expert, written to DEVICE offsets [E+1],
+ * sorted_ids [T*k], inv [T*k], active [E], n_active [1] (same meaning as
+ * above; dropped assignments follow every group).  1 <= E <= 512,
+ * 1 <= k <= 32, 0 <= T*k <= 2^20.  (cf-1.com Colibri article, section 3.3,
+ * step 3.)  Errors: -4.  Values >= E give unspecified (but in-bounds)
  * results.
  */
 int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *offsets,

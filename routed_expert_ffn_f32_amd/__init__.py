@@ -90,6 +90,8 @@ def load_library():
         L.coli_moe_forward_noalloc.restype = ctypes.c_int
         L.coli_moe_free.argtypes = [vp]
         L.coli_moe_free.restype = None
+        L.coli_moe_set_routing.argtypes = [vp, i32, ctypes.c_float]
+        L.coli_moe_set_routing.restype = ctypes.c_int
         L.coli_moe_last_routing.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.coli_moe_last_routing.restype = ctypes.c_int
         L.coli_moe_test_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
@@ -183,6 +185,19 @@ def coli_moe_forward_noalloc(cfg: coli_moe_config_t, weights: coli_moe_weights_t
 
 def coli_moe_free(handle) -> None:
     load_library().coli_moe_free(handle)
+
+
+def coli_moe_set_routing(handle, k_use: int, top_p: float = 1.0) -> int:
+    """Run-time routing limits (explicit smaller k, adaptive expert top-p) of
+    the handle's later forwards; (top_k, 1.0) is the plain routing."""
+    return _check(load_library().coli_moe_set_routing(handle, int(k_use), float(top_p)), "coli_moe_set_routing")
+
+
+def _warn_lossy(k_use: int, top_k: int, top_p: float) -> None:
+    if k_use < top_k or top_p < 1.0:
+        import warnings
+        warnings.warn(f"lossy routing override: k {k_use} of {top_k}, expert top-p {top_p}: outputs differ from the "
+                      f"layer's plain routing", stacklevel=3)
 
 
 def coli_moe_last_routing(handle, idx=None, w=None, offsets=None, sorted_ids=None, inv=None,
@@ -383,6 +398,13 @@ class MoELayer:
 
     __call__ = forward
 
+    def set_routing(self, k_use: int | None = None, top_p: float = 1.0):
+        """Lossy run-time routing limits for later forwards (warns when they
+        change the routing); no arguments restore the plain routing."""
+        k_use = self.cfg.top_k if k_use is None else int(k_use)
+        coli_moe_set_routing(self.handle, k_use, top_p)
+        _warn_lossy(k_use, self.cfg.top_k, top_p)
+
     def last_routing(self):
         """Device tensors of the last forward's routing and dispatch."""
         import torch
@@ -464,6 +486,13 @@ class ExpertCache:
 
     def slot_map(self):
         return coli_moe_cache_slots(self.handle, self.cfg.n_experts)
+
+    def set_routing(self, k_use: int | None = None, top_p: float = 1.0):
+        """Lossy run-time routing limits of the cached layer (see
+        MoELayer.set_routing)."""
+        k_use = self.cfg.top_k if k_use is None else int(k_use)
+        coli_moe_set_routing(coli_moe_cache_layer(self.handle), k_use, top_p)
+        _warn_lossy(k_use, self.cfg.top_k, top_p)
 
     def last_routing(self):
         """Device tensors of the last forward's routing and dispatch."""

@@ -199,6 +199,8 @@ void set_up(coli_moe_t *m, const coli_moe_config_t &cfg, const coli_moe_weights_
   m->prof_calls_done = 0;
   m->prof_used = 0;
   m->slot_of = nullptr;
+  m->k_use = cfg.top_k;
+  m->top_p = 1.0f;
 }
 
 // The workspace state every forward starts from: the lane-permuted router,
@@ -263,6 +265,7 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
   float *y = at<float>(m, L.y);
   const float *bias = m->w.sel_bias;
   const float rsf = c.routed_scaling_factor;
+  const coli::RouteLimits lim{m->k_use, m->top_p};
 
   const bool prefill = T >= c.prefill_threshold && prefill_shape(c);
   const bool small = !prefill && coli::small_batch(T, k, h, I);
@@ -284,12 +287,12 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
       static_assert(coli::kDispatchThreads / coli::kWave * coli::kMaxTopK <= coli::kFusedDispatchMax,
                     "the fused launch's LDS holds every choice");
       return timed(m, K_ROUTER_SELECT, s, [&] {
-        return launch_select_dispatch(logits, bias, T, E, k, rsf, idx, wsel, offsets, sorted_ids, inv,
+        return launch_select_dispatch(logits, bias, T, E, k, rsf, lim, idx, wsel, offsets, sorted_ids, inv,
                                             active, n_active, s);
       });
     }
     hipError_t err = timed(m, K_ROUTER_SELECT, s,
-                           [&] { return launch_router_select(logits, bias, T, E, k, rsf, idx, wsel, s); });
+                           [&] { return launch_router_select(logits, bias, T, E, k, rsf, lim, idx, wsel, s); });
     if (err != hipSuccess) return err;
     return timed(m, K_DISPATCH, s, [&] {
       return launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
@@ -317,7 +320,7 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
     e = timed(m, K_MFMA_DOWN, s, [&] { return launch_down_mfma(Q, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     e = timed(m, K_COMBINE, s,
-              [&] { return launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
+              [&] { return launch_combine(y, wsel, idx, inv, T, k, h, c.n_shared, out, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     m->last_T = T;
     if (m->prof_calls_left > 0) {
@@ -341,6 +344,7 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
   P.n_routed_slots = E < T * k ? E : T * k;
   P.has_shared = c.n_shared;
   P.rsf = rsf;
+  P.lim = lim;
   P.logits = logits;
   P.bias = bias;
   P.xq = xq;
@@ -374,7 +378,7 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
     e = timed(m, K_DOWN, s, [&] { return launch_gemv_down(P, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     e = timed(m, K_COMBINE, s,
-              [&] { return launch_combine(y, wsel, inv, T, k, h, c.n_shared, out, s); });
+              [&] { return launch_combine(y, wsel, idx, inv, T, k, h, c.n_shared, out, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
   }
 
@@ -397,6 +401,14 @@ void handle_set_up(coli_moe_t *m, const coli_moe_config_t &cfg, const coli_moe_w
   set_up(m, cfg, w, ws, L);
 }
 hipError_t handle_stage(coli_moe_t *m, hipStream_t s) { return stage(m, s); }
+
+int set_route_limits(coli_moe_t *m, int32_t k_use, float top_p) {
+  if (!m) return COLI_MOE_EARG;
+  if (k_use < 1 || k_use > m->cfg.top_k || !(top_p > 0.0f && top_p <= 1.0f)) return COLI_MOE_EROUTING;
+  m->k_use = k_use;
+  m->top_p = top_p;
+  return COLI_MOE_OK;
+}
 
 }  // namespace coli
 
@@ -453,6 +465,8 @@ int coli_moe_forward_noalloc(const coli_moe_config_t *cfg, const coli_moe_weight
   if (stage(&m, s) != hipSuccess) return COLI_MOE_EDEVICE;
   return coli_moe_forward(&m, hidden, out, T, stream);
 }
+
+int coli_moe_set_routing(coli_moe_t *m, int32_t k_use, float top_p) { return coli::set_route_limits(m, k_use, top_p); }
 
 void coli_moe_free(coli_moe_t *m) {
   if (!m) return;

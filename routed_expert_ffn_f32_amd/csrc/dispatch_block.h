@@ -11,6 +11,10 @@
 //   inv[n]         position of assignment a in sorted_ids
 //   active[E]      experts with at least one assignment, ascending
 //   n_active[1]    how many
+// A negative id is a dropped slot (run-time routing limits): it sorts as an
+// extra key E after every expert, so the dropped assignments fill
+// sorted_ids from offsets[E] on (a ascending) and offsets[E] counts the kept
+// ones.
 //
 // Wave w owns a contiguous range of assignments.  Within a 64-assignment
 // chunk, lanes with equal keys are found with ballots over the key bits; the
@@ -36,20 +40,25 @@ __device__ __forceinline__ uint64_t match_mask(int key, bool valid, int key_bits
   return m;
 }
 
-// `idx` may point to global or shared memory.  Keys outside [0, E) are
-// clamped into it (unspecified but in-bounds result).
+// The key of an id: the id, a negative one E (dropped), one past the
+// experts clamped to E - 1 (unspecified but in-bounds result).
+__device__ __forceinline__ int dispatch_key(int id, int E) { return id < 0 ? E : min(id, E - 1); }
+
+// `idx` may point to global or shared memory.
 __device__ __forceinline__ void dispatch_block(const int32_t *idx, int n, int E, int32_t *__restrict__ offsets,
                                                int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv,
                                                int32_t *__restrict__ active, int32_t *__restrict__ n_active) {
-  constexpr int kWaves = kDispatchThreads / kWave;  // 16
-  __shared__ int32_t hist[kWaves][kMaxExperts];     // counts, then start positions
+  constexpr int kWaves = kDispatchThreads / kWave;      // 16
+  static_assert(kMaxExperts < kDispatchThreads, "one thread per key");
+  __shared__ int32_t hist[kWaves][kMaxExperts + 1];     // counts, then start positions (key E: dropped)
   __shared__ int32_t wave_sum[kWaves];
   __shared__ int32_t wave_act[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NK = E + 1;  // keys
   int key_bits = 0;
-  while ((1 << key_bits) < E) ++key_bits;
+  while ((1 << key_bits) < NK) ++key_bits;
 
-  for (int e = lane; e < E; e += 64) hist[wave][e] = 0;
+  for (int e = lane; e < NK; e += 64) hist[wave][e] = 0;
   const int per_wave = ((n + kWaves - 1) / kWaves + 63) & ~63;
   const int lo = min(n, wave * per_wave), hi = min(n, lo + per_wave);
   __syncthreads();
@@ -58,24 +67,24 @@ __device__ __forceinline__ void dispatch_block(const int32_t *idx, int n, int E,
   for (int base = lo; base < hi; base += 64) {
     const int a = base + lane;
     const bool valid = a < hi;
-    int key = valid ? idx[a] : 0;
-    key = min(max(key, 0), E - 1);
+    const int key = valid ? dispatch_key(idx[a], E) : 0;
     const uint64_t m = match_mask(key, valid, key_bits);
     const bool leader = valid && ((m & ((1ull << lane) - 1)) == 0);
     if (leader) hist[wave][key] += __popcll(m);
   }
   __syncthreads();
 
-  // per expert: start of each wave's share (exclusive over waves), total count
+  // per key: start of each wave's share (exclusive over waves), total count
   int count = 0;
-  if (tid < E) {
+  if (tid < NK) {
     for (int w = 0; w < kWaves; ++w) {
       const int v = hist[w][tid];
       hist[w][tid] = count;
       count += v;
     }
   }
-  // exclusive scan of the counts over experts (one expert per thread)
+  // exclusive scan of the counts over keys (one key per thread); the
+  // dropped key is no active expert
   const int flag = (tid < E && count > 0) ? 1 : 0;
   int incl = count, incl_f = flag;
 #pragma unroll
@@ -98,15 +107,12 @@ __device__ __forceinline__ void dispatch_block(const int32_t *idx, int n, int E,
   }
   const int start = before + incl - count;  // offsets[tid]
   const int act_pos = before_f + incl_f - flag;
-  if (tid < E) {
-    offsets[tid] = start;
+  if (tid < NK) {
+    offsets[tid] = start;  // tid = E: the kept assignments
     if (flag) active[act_pos] = tid;
     for (int w = 0; w < kWaves; ++w) hist[w][tid] += start;
   }
-  if (tid == E - 1) {
-    offsets[E] = start + count;
-    *n_active = act_pos + flag;
-  }
+  if (tid == E) *n_active = act_pos;
   __syncthreads();
 
   // pass 2: scatter; equal keys of a chunk take consecutive positions in lane
@@ -114,8 +120,7 @@ __device__ __forceinline__ void dispatch_block(const int32_t *idx, int n, int E,
   for (int base = lo; base < hi; base += 64) {
     const int a = base + lane;
     const bool valid = a < hi;
-    int key = valid ? idx[a] : 0;
-    key = min(max(key, 0), E - 1);
+    const int key = valid ? dispatch_key(idx[a], E) : 0;
     const uint64_t m = match_mask(key, valid, key_bits);
     const int rank = __popcll(m & ((1ull << lane) - 1));
     const int pos = hist[wave][key] + rank;

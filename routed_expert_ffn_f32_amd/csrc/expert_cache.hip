@@ -294,7 +294,8 @@ int coli_moe_cache_prefetch(coli_moe_cache_t *c, const float *hidden, int32_t T,
   for (int t = 0; t < T; ++t)
     for (int j = 0; j < n_predict; ++j) {
       const int e = idx[t * k + j];
-      if (e < 0 || e >= E) return COLI_MOE_EDEVICE;
+      if (e < 0) continue;  // a slot the routing limits dropped
+      if (e >= E) return COLI_MOE_EDEVICE;
       if (c->policy->slot_of(e) >= 0) continue;
       coli::CacheLoad ld;
       if (c->policy->prefetch(e, c->guard, ld) < 0) continue;  // no slot free of pins and guards

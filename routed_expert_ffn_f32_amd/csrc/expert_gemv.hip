@@ -579,7 +579,7 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   bool have_routing = true;
   if (XREG) {
     if (wave == 0) {
-      route_small_b1(P.E, P.k, P.rsf, R);
+      route_small_b1(P.E, P.k, P.rsf, P.lim, R);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // R written before the flag
       __hip_atomic_store(&routed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
       have_routing = spins < (1 << 22);
     }
   } else {
-    route_small_b(T, P.E, P.k, P.rsf, R);
+    route_small_b(T, P.E, P.k, P.rsf, P.lim, R);
     gu_load(bs, cs, has0, h);
   }
   // rows of the call (a wave without the routing stops after the shared ones)
@@ -672,20 +672,26 @@ __device__ __forceinline__ void dn_load(DnBuf<NCHD> &b, const uint8_t *q, const 
 // shared-expert slot first (those rows need no routing, so they can be
 // requested before the routing has arrived), then its k routed assignments
 // in slot order.  The block keeps the routing of every slot in LDS: expert
-// (-1 for the shared expert), position of the intermediate row, combine
-// weight; one entry per thread of the block (entries past the last slot are
-// written and never read).
+// (-1 for the shared expert, kDnDropped for a slot the routing limits
+// dropped), position of the intermediate row, combine weight; one entry per
+// thread of the block (entries past the last slot are written and never
+// read).  A dropped slot reads no weights (its loads have an empty range
+// and return zeros), has weight 0 and points at position 0, always a kept
+// assignment's row, so that it adds exactly zero.
 struct DnTable {
   int32_t e[kDcWaves * 64];
   int32_t p[kDcWaves * 64];
   float w[kDcWaves * 64];
 };
 
+constexpr int kDnDropped = -2;
+
 struct DnSlot {
   const uint8_t *q;
   const float *s;
   int t;
   float w;
+  bool live;  // false: a dropped slot, no rows read
 };
 
 // Thread q reads the routing of slot q (every slot has a thread: the block
@@ -706,27 +712,31 @@ __device__ __forceinline__ void dn_table_load(const DecodeProblem &P, uint32_t (
 __device__ __forceinline__ void dn_table_store(const DecodeProblem &P, const uint32_t (&v)[3], DnTable &D) {
   const int ks = P.k + P.has_shared;
   const int qs = threadIdx.x, t = qs / ks, j = qs % ks - P.has_shared;
-  const bool routed = j >= 0;
-  D.e[qs] = routed ? (int)v[0] : -1;
-  D.p[qs] = routed ? (int)v[1] : P.T * P.k + t;
+  const bool routed = j >= 0, dropped = routed && (int)v[0] < 0;
+  D.e[qs] = dropped ? kDnDropped : routed ? (int)v[0] : -1;
+  D.p[qs] = dropped ? 0 : routed ? (int)v[1] : P.T * P.k + t;
   D.w[qs] = routed ? __uint_as_float(v[2]) : 1.0f;
 }
 
 __device__ __forceinline__ DnSlot dn_shared_slot(const DecodeProblem &P, int t) {
-  return DnSlot{P.sh_down.q, P.sh_down.s, t, 1.0f};
+  return DnSlot{P.sh_down.q, P.sh_down.s, t, 1.0f, true};
 }
 
 __device__ __forceinline__ DnSlot dn_slot(const DecodeProblem &P, const DnTable &D, int qs) {
   DnSlot d;
   d.t = qs / (P.k + P.has_shared);
   const int e = uniform(D.e[qs]);
+  d.live = e != kDnDropped;
   if (e >= 0) {
     const size_t x = table_index(P.slot_of, e);
     d.q = P.down.q + x * ((size_t)P.h * (P.I >> 1));
     d.s = P.down.s + x * ((size_t)P.h * (P.I >> 6));
-  } else {
+  } else if (e == -1) {
     d.q = P.sh_down.q;
     d.s = P.sh_down.s;
+  } else {
+    d.q = P.down.q;
+    d.s = P.down.s;
   }
   d.w = __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, D.w[qs])));
   return d;
@@ -841,7 +851,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(Decode
     const bool v = qs < n_slots;
     ring[u] = v ? dn_slot(P, tab, qs) : DnSlot{};
 #pragma unroll
-    for (int r = 0; r < RM; ++r) dn_load(buf[u][r], ring[u].q, ring[u].s, r0 + r, v && r < nr, I);
+    for (int r = 0; r < RM; ++r) dn_load(buf[u][r], ring[u].q, ring[u].s, r0 + r, v && ring[u].live && r < nr, I);
   };
 
   // prologue: the routing table and the first batch of intermediate words,
@@ -1082,8 +1092,8 @@ __global__ __launch_bounds__(64) void down_tok_kernel(DecodeProblem P) {
 // kMaxTopK, uniform per block), then all expert rows, then summed in slot
 // order and the shared row added last.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w,
-                                                      const int32_t *__restrict__ inv, int T, int k, int h,
-                                                      int has_shared, float *__restrict__ out) {
+                                                      const int32_t *__restrict__ idx, const int32_t *__restrict__ inv,
+                                                      int T, int k, int h, int has_shared, float *__restrict__ out) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (c >= h) return;
@@ -1091,15 +1101,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   for (int j0 = 0; j0 < k; j0 += 8) {
     float wj[8];
     float4 v[8];
+    bool live[8];  // a slot of the token that the routing kept
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int a = t * k + min(j0 + u, k - 1);
+      live[u] = j0 + u < k && idx[a] >= 0;
       wj[u] = w[a];
-      v[u] = *reinterpret_cast<const float4 *>(y + (size_t)inv[a] * h + c);
+      v[u] = live[u] ? *reinterpret_cast<const float4 *>(y + (size_t)inv[a] * h + c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (j0 + u < k) {
+      if (live[u]) {
         acc.x = __builtin_fmaf(wj[u], v[u].x, acc.x);
         acc.y = __builtin_fmaf(wj[u], v[u].y, acc.y);
         acc.z = __builtin_fmaf(wj[u], v[u].z, acc.z);
@@ -1318,11 +1330,11 @@ hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s) {
     return launch(down_kernel<4>, grid, kDnWaves * 64, 0, s, P);
 }
 
-hipError_t launch_combine(const float *y, const float *w, const int32_t *inv, int T, int k, int h,
-                          int has_shared, float *out, hipStream_t s) {
+hipError_t launch_combine(const float *y, const float *w, const int32_t *idx, const int32_t *inv, int T, int k,
+                          int h, int has_shared, float *out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   dim3 grid((h / 4 + 255) / 256, T);
-  return launch(combine_kernel, grid, 256, 0, s, y, w, inv, T, k, h, has_shared, out);
+  return launch(combine_kernel, grid, 256, 0, s, y, w, idx, inv, T, k, h, has_shared, out);
 }
 
 

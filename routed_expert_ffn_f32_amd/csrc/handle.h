@@ -37,6 +37,9 @@ struct coli_moe {
   // routed expert e's tables sit at index slot_of[e] of the stacked tables
   // (device array; NULL: at index e)
   const int32_t *slot_of;
+  // run-time routing limits (k_use = top_k, top_p = 1: none)
+  int32_t k_use;
+  float top_p;
 };
 
 namespace coli {
@@ -56,5 +59,7 @@ Layout workspace_layout(const coli_moe_config_t &c);
 void handle_set_up(coli_moe_t *m, const coli_moe_config_t &cfg, const coli_moe_weights_t &w, char *ws,
                    const Layout &L);
 hipError_t handle_stage(coli_moe_t *m, hipStream_t s);
+// Sets the handle's run-time routing limits (COLI_MOE_* code).
+int set_route_limits(coli_moe_t *m, int32_t k_use, float top_p);
 
 }  // namespace coli

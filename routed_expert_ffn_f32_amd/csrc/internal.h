@@ -44,6 +44,26 @@ constexpr int kSmallAssign = 64;         // and T*k at most one wave of assignme
 // Routing (router.hip)
 // ---------------------------------------------------------------------------
 
+// Run-time routing limits, two lossy overrides of the routing named as
+// engine knobs in the knob table of "Colibri 调优与运行时旋钮实战指南"
+// (Colibri tuning and runtime knobs guide): an explicit smaller k and
+// adaptive expert top-p.  With k_use <= k and 0 < top_p <= 1:
+//  - the k_use experts first in the order (c desc, e asc) are the
+//    candidates, in slots 0..k_use-1, and den sums their scores in slot
+//    order;
+//  - top_p < 1: cum_j = ((s_0 + s_1) + ...) + s_(j-1) is the score of the
+//    candidates before slot j; slot 0 is kept, slot j >= 1 while
+//    cum_j < top_p * den (cum never decreases, so the kept slots are a
+//    prefix of m slots: the shortest one reaching the share top_p);
+//  - the kept slots are renormalised over themselves, w_j = (s_j / cum_m)
+//    * rsf; every other slot of the k is dropped: expert -1, weight 0.
+// k_use = k, top_p = 1 is the plain selection.
+struct RouteLimits {
+  int k_use;
+  float top_p;
+};
+
+
 // Floats of the lane-permuted router copy for (h, E).
 size_t router_permuted_floats(int h, int E);
 
@@ -62,16 +82,18 @@ hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, 
 
 // One wave per token: sigmoid scores, biased key, top-k (key desc, index
 // asc), renormalised weights times rsf.
+// Routing limits as in RouteLimits; idx and w keep their [T][k] layout.
 hipError_t launch_router_select(const float *logits, const float *bias, int T, int E, int k, float rsf,
-                                int32_t *idx, float *w, hipStream_t s);
+                                RouteLimits lim, int32_t *idx, float *w, hipStream_t s);
 
 // Selection of T tokens and the dispatch in one workgroup (T*k <= kFusedDispatchMax).
 hipError_t launch_select_dispatch(const float *logits, const float *bias, int T, int E, int k, float rsf,
-                                  int32_t *idx, float *w, int32_t *offsets, int32_t *sorted_ids, int32_t *inv,
-                                  int32_t *active, int32_t *n_active, hipStream_t s);
+                                  RouteLimits lim, int32_t *idx, float *w, int32_t *offsets, int32_t *sorted_ids,
+                                  int32_t *inv, int32_t *active, int32_t *n_active, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Dispatch (dispatch.hip): stable counting sort of assignments by expert.
+// Dispatch (dispatch.hip): stable counting sort of assignments by expert;
+// negative ids (dropped slots) follow every expert's group.
 // ---------------------------------------------------------------------------
 hipError_t launch_dispatch(const int32_t *idx, int n, int E, int32_t *offsets, int32_t *sorted_ids,
                            int32_t *inv, int32_t *active, int32_t *n_active, hipStream_t s);
@@ -98,6 +120,7 @@ struct DecodeProblem {
   int n_routed_slots;  // min(E, T*k): grid slots for routed experts
   int has_shared;
   float rsf;
+  RouteLimits lim;      // run-time routing limits (small batches route in the gate/up launch)
   const float *logits;  // [T][E] router logits (small batches route from them)
   const float *bias;    // [E] selection bias or NULL
   const uint32_t *xq;   // hidden rows as digit planes [T][6][h/8]
@@ -143,9 +166,10 @@ hipError_t launch_read_probe(const DecodeProblem &P, const int32_t *experts, int
 hipError_t launch_down_combine(const DecodeProblem &P, float *out, hipStream_t s);
 // Larger batches: y[p] = Wd mid[p] ...
 hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s);
-// ... then out[t] = sum_j w[t*k+j] y[inv[t*k+j]] + (shared ? y[T*k + t] : 0).
-hipError_t launch_combine(const float *y, const float *w, const int32_t *inv, int T, int k, int h,
-                          int has_shared, float *out, hipStream_t s);
+// ... then out[t] = sum_j w[t*k+j] y[inv[t*k+j]] + (shared ? y[T*k + t] : 0),
+// the sum over the slots j with idx[t*k+j] >= 0 (dropped slots add nothing).
+hipError_t launch_combine(const float *y, const float *w, const int32_t *idx, const int32_t *inv, int T, int k,
+                          int h, int has_shared, float *out, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Prefill path (expert_mfma.hip): grouped GEMMs on fp16 MFMA.

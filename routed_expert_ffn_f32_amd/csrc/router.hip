@@ -76,14 +76,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
 
 __global__ __launch_bounds__(256) void router_select_kernel(const float *__restrict__ logits,
                                                             const float *__restrict__ bias, int T, int E,
-                                                            int k, float rsf, int32_t *__restrict__ idx,
-                                                            float *__restrict__ wout) {
+                                                            int k, float rsf, RouteLimits lim,
+                                                            int32_t *__restrict__ idx, float *__restrict__ wout) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + uniform(threadIdx.x >> 6);  // scalar: the loads' buffer resources
   if (t >= T) return;
   int e;
   float w;
-  select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w);
+  select_token(logits + (size_t)t * E, bias, E, k, rsf, lim, e, w);
   if (lane < k) {
     idx[(size_t)t * k + lane] = e;
     wout[(size_t)t * k + lane] = w;
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float *__restr
 // (16 waves); the selected ids go through LDS to the counting sort.
 __global__ __launch_bounds__(kDispatchThreads) void select_dispatch_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int T, int E, int k, float rsf,
-    int32_t *__restrict__ idx, float *__restrict__ wout, int32_t *__restrict__ offsets,
+    RouteLimits lim, int32_t *__restrict__ idx, float *__restrict__ wout, int32_t *__restrict__ offsets,
     int32_t *__restrict__ sorted_ids, int32_t *__restrict__ inv, int32_t *__restrict__ active,
     int32_t *__restrict__ n_active) {
   __shared__ int32_t sel[kFusedDispatchMax];
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kDispatchThreads) void select_dispatch_kernel(
   for (int t = wave; t < T; t += kDispatchThreads / kWave) {
     int e;
     float w;
-    select_token(logits + (size_t)t * E, bias, E, k, rsf, e, w);
+    select_token(logits + (size_t)t * E, bias, E, k, rsf, lim, e, w);
     if (lane < k) {
       idx[(size_t)t * k + lane] = e;
       wout[(size_t)t * k + lane] = w;
@@ -207,16 +207,16 @@ hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, 
 }
 
 hipError_t launch_router_select(const float *logits, const float *bias, int T, int E, int k, float rsf,
-                                int32_t *idx, float *w, hipStream_t s) {
+                                RouteLimits lim, int32_t *idx, float *w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  return launch(router_select_kernel, (T + 3) / 4, 256, 0, s, logits, bias, T, E, k, rsf, idx, w);
+  return launch(router_select_kernel, (T + 3) / 4, 256, 0, s, logits, bias, T, E, k, rsf, lim, idx, w);
 }
 
 hipError_t launch_select_dispatch(const float *logits, const float *bias, int T, int E, int k, float rsf,
-                                  int32_t *idx, float *w, int32_t *offsets, int32_t *sorted_ids, int32_t *inv,
-                                  int32_t *active, int32_t *n_active, hipStream_t s) {
-  return launch(select_dispatch_kernel, 1, kDispatchThreads, 0, s, logits, bias, T, E, k, rsf, idx, w, offsets, sorted_ids,
-                                                        inv, active, n_active);
+                                  RouteLimits lim, int32_t *idx, float *w, int32_t *offsets, int32_t *sorted_ids,
+                                  int32_t *inv, int32_t *active, int32_t *n_active, hipStream_t s) {
+  return launch(select_dispatch_kernel, 1, kDispatchThreads, 0, s, logits, bias, T, E, k, rsf, lim, idx, w, offsets,
+                sorted_ids, inv, active, n_active);
 }
 
 }  // namespace coli

@@ -64,6 +64,7 @@ __device__ __forceinline__ uint32_t ordered_bits(float c) {
 
 constexpr int kSelMaxKeys = kMaxExperts / kWave;  // keys per lane
 
+
 // The logits and selection biases of one token, lane l holding experts
 // l + 64 i (i < kSelMaxKeys; zeros past E).  Issued early by callers that
 // want the loads in flight while they do other work.
@@ -106,8 +107,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // lowest expert among the lanes holding it) and removes it from its lane, so
 // the rounds yield the slots in rank order.  Every real key is >= 0x00800000
 // (the image of -FLT_MAX), removed or invalid keys count as 0.
-__device__ __forceinline__ void select_token_regs(const SelectInput &in, int E, int k, float rsf, int &e_out,
-                                                  float &w_out) {
+//
+// Routing limits (lim): the tournament runs k_use rounds; lane j also keeps
+// cum_j (den before its slot was added), from which the kept prefix and
+// its denominator follow; dropped slots j < k return (-1, 0).
+__device__ __forceinline__ void select_token_regs(const SelectInput &in, int E, int k, float rsf,
+                                                  const RouteLimits &lim, int &e_out, float &w_out) {
   const int lane = threadIdx.x & 63, nk = (E + 63) >> 6;
   float s[kSelMaxKeys];
   uint32_t u[kSelMaxKeys];
@@ -120,9 +125,9 @@ __device__ __forceinline__ void select_token_regs(const SelectInput &in, int E, 
     s[i] = valid ? sigmoid_spec(in.l[i]) : 0.0f;
     u[i] = valid ? ordered_bits(s[i] + in.b[i]) : 0u;
   }
-  float den = 0.0f, my_s = 0.0f;
+  float den = 0.0f, my_s = 0.0f, my_cum = 0.0f;
   int my_e = 0;
-  for (int j = 0; j < k; ++j) {
+  for (int j = 0; j < lim.k_use; ++j) {
     uint32_t bu = 0u;
     int bi = 0;
     float bs = 0.0f;
@@ -150,19 +155,28 @@ __device__ __forceinline__ void select_token_regs(const SelectInput &in, int E, 
       }
     }
     const float s_win = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs), wl));
-    den = den + s_win;
     if (lane == j) {
       my_e = e_win;
       my_s = s_win;
+      my_cum = den;
     }
+    den = den + s_win;
     if (lane == wl) {
 #pragma unroll
       for (int i = 0; i < kSelMaxKeys; ++i)
         if (i == bi) u[i] = 0u;
     }
   }
-  e_out = lane < k ? my_e : 0;
-  w_out = lane < k ? (my_s / den) * rsf : 0.0f;
+  bool keep = lane < lim.k_use;
+  if (lim.top_p < 1.0f) {
+    const float thr = lim.top_p * den;
+    keep = keep && (lane == 0 || my_cum < thr);
+    const int m = __popcll(__ballot(keep));
+    // cum_m: the same float32 sum as den after round m - 1
+    den = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_cum + my_s), m - 1));
+  }
+  e_out = lane < k ? (keep ? my_e : -1) : 0;
+  w_out = keep ? (my_s / den) * rsf : 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -273,14 +287,16 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Phase B: n <= 64 candidates (cu, ce, cs in LDS, ascending expert order)
 // -> slot j (j < k) of the token in se[j], sw[j] = (s_j / den) * rsf with
 // den = ((s_0 + s_1) + s_2) + ... in slot order, and slot_of[p] = the slot
-// of the p-th selected expert in ascending expert order.  One wave: lane c
+// of the p-th kept expert in ascending expert order.  One wave: lane c
 // holds candidate c and counts the candidates the order (key desc, expert
-// asc) puts before it -- its slot when that count is below k (equal keys:
-// the lower lane is the lower expert).  `scratch` holds kMaxTopK words of
-// LDS.
-__device__ __forceinline__ void select_merge(const uint32_t *cu, const int32_t *ce, const float *cs, int n, int k,
-                                             float rsf, int32_t *se, float *sw, uint32_t *scratch,
-                                             int32_t *slot_of) {
+// asc) puts before it -- its slot when that count is below k_use (equal
+// keys: the lower lane is the lower expert).  Routing limits as in
+// select_token_regs: slots past the kept prefix get (-1, 0).  Returns the
+// number of kept slots (uniform); se, sw and slot_of are readable by the
+// calling wave on return.  `scratch` holds kMaxTopK words of LDS.
+__device__ __forceinline__ int select_merge(const uint32_t *cu, const int32_t *ce, const float *cs, int n, int k,
+                                            float rsf, const RouteLimits &lim, int32_t *se, float *sw,
+                                            uint32_t *scratch, int32_t *slot_of) {
   const int lane = threadIdx.x & 63;
   const bool valid = lane < n;
   const uint32_t u = valid ? cu[lane] : 0u;
@@ -299,27 +315,45 @@ __device__ __forceinline__ void select_merge(const uint32_t *cu, const int32_t *
       rank += j < n && (uj[i] > u || (uj[i] == u && j < lane));
     }
   }
-  const bool win = valid && rank < k;
-  const uint64_t wins = __ballot(win);
+  const bool win = valid && rank < lim.k_use;
   const int below = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const uint64_t lt_mask = below == 0 ? 0ull : (~0ull >> (64 - below));
   float *ss = reinterpret_cast<float *>(scratch);  // scores in slot order
-  if (win) {
-    se[rank] = e;
-    ss[rank] = sv;
-    slot_of[__popcll(wins & lt_mask)] = rank;
-  }
+  if (win) ss[rank] = sv;
   wave_lds_sync();
-  float den = 0.0f;
-  for (int j = 0; j < k; ++j) den = den + ss[j];
-  if (win) sw[rank] = (sv / den) * rsf;
+  float den = 0.0f, my_cum = 0.0f;
+  for (int j = 0; j < lim.k_use; ++j) {
+    if (j == rank) my_cum = den;
+    den = den + ss[j];
+  }
+  bool keep = win;
+  int m = lim.k_use;
+  if (lim.top_p < 1.0f) {
+    const float thr = lim.top_p * den;
+    keep = win && (rank == 0 || my_cum < thr);
+    m = __popcll(__ballot(keep));
+    den = 0.0f;
+    for (int j = 0; j < m; ++j) den = den + ss[j];
+  }
+  const uint64_t keeps = __ballot(keep);
+  if (keep) {
+    se[rank] = e;
+    sw[rank] = (sv / den) * rsf;
+    slot_of[__popcll(keeps & lt_mask)] = rank;
+  }
+  if (lane >= m && lane < k) {  // dropped slots
+    se[lane] = -1;
+    sw[lane] = 0.0f;
+  }
+  wave_lds_sync();  // se, sw, slot_of readable by the whole wave
+  return m;
 }
 
 __device__ __forceinline__ void select_token(const float *__restrict__ l, const float *__restrict__ bias, int E,
-                                             int k, float rsf, int &e_out, float &w_out) {
+                                             int k, float rsf, const RouteLimits &lim, int &e_out, float &w_out) {
   SelectInput in;
   select_load(l, bias, E, in);
-  select_token_regs(in, E, k, rsf, e_out, w_out);
+  select_token_regs(in, E, k, rsf, lim, e_out, w_out);
 }
 
 }  // namespace coli

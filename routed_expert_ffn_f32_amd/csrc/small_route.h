@@ -88,27 +88,40 @@ __device__ __forceinline__ void route_small_a(const SelectInput &in, int T, int 
   block_barrier();
 }
 
-// Phase B and the sort (after route_small_a).
-__device__ __forceinline__ void route_small_b(int T, int E, int k, float rsf, SmallRouting &R) {
+// One token: the merge lists the kept experts in ascending order, each with
+// exactly one assignment (its slot), and the dropped slots are the slots
+// m..k-1 (a suffix), which follow every expert's group in ascending order.
+__device__ __forceinline__ void route_small_one_token(int k, int m, SmallRouting &R) {
+  const int lane = threadIdx.x & 63;
+  if (lane < m) {
+    const int sl = R.slot_of[0][lane];
+    R.sorted_ids[lane] = sl;
+    R.inv[sl] = lane;
+    R.active[lane] = R.idx[sl];
+    R.seg_begin[lane] = lane;
+  } else if (lane < k) {
+    R.sorted_ids[lane] = lane;
+    R.inv[lane] = lane;
+  }
+  if (lane == 0) {
+    R.n_active = m;
+    R.seg_begin[m] = m;
+  }
+}
+
+// Phase B and the sort (after route_small_a).  Dropped slots (expert -1,
+// routing limits) take the positions after every expert's group, in
+// ascending order, and start no group.
+__device__ __forceinline__ void route_small_b(int T, int E, int k, float rsf, const RouteLimits &lim,
+                                              SmallRouting &R) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wt = small_select_plan(T, E, k).wt;
+  int m = 0;
   if (wave < T)
-    select_merge(R.cu[wave], R.ce[wave], R.cs[wave], wt * k, k, rsf, R.idx + wave * k, R.w + wave * k,
-                 R.scratch[wave], R.slot_of[wave]);
+    m = select_merge(R.cu[wave], R.ce[wave], R.cs[wave], wt * k, k, rsf, lim, R.idx + wave * k, R.w + wave * k,
+                     R.scratch[wave], R.slot_of[wave]);
   if (T == 1) {
-    // one token: the merge gives the experts in ascending order already, and
-    // every expert has exactly one assignment
-    if (wave == 0 && lane < k) {
-      const int sl = R.slot_of[0][lane];
-      R.sorted_ids[lane] = sl;
-      R.inv[sl] = lane;
-      R.active[lane] = R.idx[sl];
-      R.seg_begin[lane] = lane;
-      if (lane == 0) {
-        R.n_active = k;
-        R.seg_begin[k] = k;
-      }
-    }
+    if (wave == 0) route_small_one_token(k, m, R);
     block_barrier();
     return;
   }
@@ -116,7 +129,9 @@ __device__ __forceinline__ void route_small_b(int T, int E, int k, float rsf, Sm
   const int n = T * k;
   if (wave == 0) {
     const bool valid = lane < n;
-    const int key = valid ? R.idx[lane] : 0x7fffffff;
+    const int id = valid ? R.idx[lane] : -1;
+    const bool kept = valid && id >= 0;
+    const int key = kept ? id : 0x7fffffff;
     int lt = 0, eq_before = 0;
     uint64_t m_lt = 0;
     for (int b = 0; b < n; ++b) {
@@ -125,8 +140,9 @@ __device__ __forceinline__ void route_small_b(int T, int E, int k, float rsf, Sm
       eq_before += kb == key && b < lane;
       m_lt |= (uint64_t)(kb < key) << b;
     }
-    const bool start = valid && eq_before == 0;
+    const bool start = kept && eq_before == 0;
     const uint64_t starts = __ballot(start);
+    const int n_kept = __popcll(__ballot(kept));
     if (valid) {
       R.sorted_ids[lt + eq_before] = lane;
       R.inv[lane] = lt + eq_before;
@@ -138,7 +154,7 @@ __device__ __forceinline__ void route_small_b(int T, int E, int k, float rsf, Sm
     }
     if (lane == 0) {
       R.n_active = __popcll(starts);
-      R.seg_begin[__popcll(starts)] = n;
+      R.seg_begin[__popcll(starts)] = n_kept;
     }
   }
   block_barrier();
@@ -146,23 +162,11 @@ __device__ __forceinline__ void route_small_b(int T, int E, int k, float rsf, Sm
 
 // Phase B for one token, by the calling wave alone and without a block
 // barrier (after route_small_a): the merge, then the assignments in expert
-// order (one token: each selected expert has exactly one assignment).
-__device__ __forceinline__ void route_small_b1(int E, int k, float rsf, SmallRouting &R) {
-  const int lane = threadIdx.x & 63;
+// order.
+__device__ __forceinline__ void route_small_b1(int E, int k, float rsf, const RouteLimits &lim, SmallRouting &R) {
   const int wt = small_select_plan(1, E, k).wt;
-  select_merge(R.cu[0], R.ce[0], R.cs[0], wt * k, k, rsf, R.idx, R.w, R.scratch[0], R.slot_of[0]);
-  wave_lds_sync();
-  if (lane < k) {
-    const int sl = R.slot_of[0][lane];
-    R.sorted_ids[lane] = sl;
-    R.inv[sl] = lane;
-    R.active[lane] = R.idx[sl];
-    R.seg_begin[lane] = lane;
-  }
-  if (lane == 0) {
-    R.n_active = k;
-    R.seg_begin[k] = k;
-  }
+  const int m = select_merge(R.cu[0], R.ce[0], R.cs[0], wt * k, k, rsf, lim, R.idx, R.w, R.scratch[0], R.slot_of[0]);
+  route_small_one_token(k, m, R);
 }
 
 // Where the routing of a call goes (device arrays of the C ABI's layout).
@@ -183,7 +187,7 @@ __device__ __forceinline__ void publish_routing(const SmallRouting &R, int T, in
   }
   for (int e = threadIdx.x; e <= E; e += blockDim.x) {
     int c = 0;
-    for (int a = 0; a < n; ++a) c += R.idx[a] < e;
+    for (int a = 0; a < n; ++a) c += R.idx[a] >= 0 && R.idx[a] < e;  // dropped slots (-1) in no group
     o.offsets[e] = c;
   }
   for (int s = threadIdx.x; s < R.n_active; s += blockDim.x) o.active[s] = R.active[s];

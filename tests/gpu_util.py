@@ -55,6 +55,15 @@ class DeviceLayer:
                              routed_scaling_factor=shape.rsf, max_tokens=max_tokens,
                              prefill_threshold=prefill_threshold)
         self.moe = cm.MoELayer(cfg, t)
+        self.limits = {}  # run-time routing limits of the oracle calls (k_use, top_p)
+
+    def set_routing(self, k_use: int | None = None, top_p: float = 1.0):
+        """Routing limits on the device layer and in the oracle calls."""
+        import warnings
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            self.moe.set_routing(k_use, top_p)
+        self.limits = {} if (k_use in (None, self.shape.top_k) and top_p == 1.0) else dict(k_use=k_use, top_p=top_p)
 
     def routed_for(self, experts) -> list:
         E = self.shape.n_experts
@@ -63,13 +72,14 @@ class DeviceLayer:
         return [synth.expert(self.shape, self.seed, e, self.layer) if e in experts else None for e in range(E)]
 
     def oracle_route(self, x_rows: np.ndarray) -> np.ndarray:
-        idx, _ = oracle.route(self.shape, self.wr, self.bias, x_rows)
+        idx, _ = oracle.route(self.shape, self.wr, self.bias, x_rows, **self.limits)
         return idx
 
     def oracle_forward(self, x_rows: np.ndarray):
-        idx, _ = oracle.route(self.shape, self.wr, self.bias, x_rows)
-        needed = set(int(e) for e in np.unique(idx))
-        return oracle.forward(self.shape, self.wr, self.bias, self.routed_for(needed), self.host_shared, x_rows)
+        idx, _ = oracle.route(self.shape, self.wr, self.bias, x_rows, **self.limits)
+        needed = set(int(e) for e in np.unique(idx) if e >= 0)
+        return oracle.forward(self.shape, self.wr, self.bias, self.routed_for(needed), self.host_shared, x_rows,
+                              **self.limits)
 
     def close(self):
         self.moe.close()
@@ -109,7 +119,7 @@ def assert_routing_matches(layer: DeviceLayer, x: np.ndarray, T: int):
     torch.cuda.synchronize()
     assert Tr == T
     g = routing_from_device(r, T, layer.shape.top_k)
-    idx_o, w_o = oracle.route(layer.shape, layer.wr, layer.bias, x)
+    idx_o, w_o = oracle.route(layer.shape, layer.wr, layer.bias, x, **layer.limits)
     assert np.array_equal(g["idx"], idx_o), "expert indices differ"
     assert np.array_equal(g["w"].view(np.uint32), w_o.view(np.uint32)), "routing weights differ"
     d = oracle.dispatch(idx_o, layer.shape.n_experts)
