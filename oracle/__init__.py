@@ -44,7 +44,7 @@ class Layer(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
                 ("router_w", ctypes.c_void_p), ("sel_bias", ctypes.c_void_p),
-                ("experts", ctypes.POINTER(Expert))]
+                ("experts", ctypes.POINTER(Expert)), ("weight_format", ctypes.c_int32)]
 
 
 _lib = None
@@ -73,6 +73,10 @@ def _load():
         L.coli_oracle_unpack_code.restype = i32
         L.coli_oracle_expert_ffn.argtypes = [ctypes.POINTER(Expert), i32, i32, vp, vp]
         L.coli_oracle_expert_ffn.restype = None
+        L.coli_oracle_expert_ffn_fmt.argtypes = [ctypes.POINTER(Expert), i32, i32, i32, vp, vp]
+        L.coli_oracle_expert_ffn_fmt.restype = None
+        L.coli_oracle_int8_code.argtypes = [vp, i32]
+        L.coli_oracle_int8_code.restype = i32
         L.coli_oracle_forward.argtypes = [ctypes.POINTER(Layer), vp, i32, vp, vp, vp]
         L.coli_oracle_forward.restype = i32
         L.coli_oracle_forward_limited.argtypes = [ctypes.POINTER(Layer), vp, i32, i32, f32, vp, vp, vp]
@@ -159,6 +163,11 @@ def unpack_code(row: np.ndarray, c: int) -> int:
     return int(_load().coli_oracle_unpack_code(row.ctypes.data, c))
 
 
+def int8_code(row: np.ndarray, c: int) -> int:
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    return int(_load().coli_oracle_int8_code(row.ctypes.data, c))
+
+
 def _expert_struct(t: dict | None, keep: list) -> Expert:
     if t is None:
         return Expert()
@@ -171,15 +180,16 @@ def _expert_struct(t: dict | None, keep: list) -> Expert:
     return Expert(**arrs)
 
 
-def expert_ffn(tables: dict, x: np.ndarray) -> np.ndarray:
-    """One expert on one token, float64 output [h]."""
+def expert_ffn(tables: dict, x: np.ndarray, weight_format: int = 0) -> np.ndarray:
+    """One expert on one token, float64 output [h] (tables in storage format
+    weight_format: 0 int4 gs64, 1 int8 per row)."""
     keep = []
     ex = _expert_struct(tables, keep)
     x = _f32(x)
     h = x.shape[0]
     I = tables["gate_q"].shape[0]
     y = np.empty(h, np.float64)
-    _load().coli_oracle_expert_ffn(ctypes.byref(ex), h, I, x.ctypes.data, y.ctypes.data)
+    _load().coli_oracle_expert_ffn_fmt(ctypes.byref(ex), int(weight_format), h, I, x.ctypes.data, y.ctypes.data)
     return y
 
 
@@ -209,7 +219,8 @@ def forward(shape, wr, bias, routed: dict | list, shared: dict | None, x: np.nda
     L = Layer(hidden=h, n_experts=E, top_k=k, inter=shape.inter, n_shared=shape.n_shared,
               routed_scaling_factor=shape.rsf, router_w=wr_c.ctypes.data,
               sel_bias=None if b_c is None else b_c.ctypes.data,
-              experts=ctypes.cast(arr, ctypes.POINTER(Expert)))
+              experts=ctypes.cast(arr, ctypes.POINTER(Expert)),
+              weight_format=getattr(shape, "weight_format", 0))
     out = np.empty((T, h), np.float32)
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float32)

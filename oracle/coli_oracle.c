@@ -30,6 +30,10 @@
  *       for MoE models", section 2.2 -- routing yields a [batch, top_k]
  *       integer index array; section 3.1 -- router stored as a
  *       [hidden_size, num_experts] float32 matrix.
+ *  [N]  "Colibrì：蜂鸟驮巨兽——纯C语言打造的7440亿参数MoE本地推理引擎", the
+ *       kernels paragraph (hand-written int8, packed int4 and packed int2
+ *       kernels with per-row scaling) and the MTP paragraph (the MTP head
+ *       must be int8).
  *  [K]  "Colibri 调优与运行时旋钮实战指南" (Colibri tuning and runtime knobs
  *       guide), the knob table (explicit
  *       smaller k and adaptive expert top-p, lossy overrides of the
@@ -51,7 +55,10 @@
  *  - int4 storage: byte c/2 of a row holds weight c in its low nibble for
  *    even c and in its high nibble for odd c, a 4-bit two's-complement code;
  *    scale [c/64] is a float32 for the 64 consecutive weights of the group
- *    along the input (reduction) axis; weight = code * scale.
+ *    along the input (reduction) axis; weight = code * scale;
+ *  - int8 storage (the multi-token prediction head's format, [T], [N]):
+ *    byte c of a row is weight c as an 8-bit two's-complement code, one
+ *    float32 scale per (output) row; weight = code * scale[row].
  *
  * Precision: routing is an exact float32 program (the pages keep the router
  * in float32), so that a GPU can reproduce it bit for bit; the expert FFN and
@@ -339,38 +346,61 @@ typedef struct {
   const float *down_s;   /* [hidden][inter/64] */
 } coli_oracle_expert_t;
 
+/* ---------------------------------------------------------------------- */
+/* int8 with one scale per row.                                             */
+/* ---------------------------------------------------------------------- */
+
+/* Code of weight c of an int8 row: byte c read as 8-bit two's complement.
+ * Format: [T] "Three key engineering decisions" item 1 and the MTP
+ * subsection (the multi-token prediction head must be int8), [N] (the
+ * engine's quantised kernels: int8, packed int4, packed int2, per-row
+ * scaling); reading: one float32 scale per output row, weight = code *
+ * scale[row]. */
+int32_t coli_oracle_int8_code(const uint8_t *row, int32_t c) {
+  const int32_t b = row[c];
+  return b >= 128 ? b - 256 : b;
+}
+
+/* Weight c of row r of a [rows][cols] matrix in format fmt (0: int4 gs64,
+ * 1: int8 per row), dequantised in float64. */
+static double weight_at(int32_t fmt, const uint8_t *codes, const float *scales, int32_t r, int32_t cols,
+                        int32_t c) {
+  if (fmt == 1) return (double)coli_oracle_int8_code(codes + (size_t)r * cols, c) * (double)scales[r];
+  return dq(codes + (size_t)r * (cols / 2), scales + (size_t)r * (cols / 64), c);
+}
+
 /*
  * One SwiGLU expert on one token, float64 throughout:
  *   g_i = sum_c Wg[i][c] x[c],  u_i = sum_c Wu[i][c] x[c]   (i < inter)
  *   m_i = silu(g_i) * u_i,      silu(z) = z / (1 + e^-z)
  *   y_r = sum_i Wd[r][i] m_i    (r < hidden)
+ * with the tables in storage format fmt (0: int4 gs64, 1: int8 per row).
  * Source: [C] section 2.1 (expert FFN with three matrices); the gated
  * (SwiGLU) form and the matrix roles are the reading stated at the top.
  */
-void coli_oracle_expert_ffn(const coli_oracle_expert_t *ex, int32_t h, int32_t I, const float *x,
-                            double *y) {
+void coli_oracle_expert_ffn_fmt(const coli_oracle_expert_t *ex, int32_t fmt, int32_t h, int32_t I,
+                                const float *x, double *y) {
   double *m = (double *)malloc(sizeof(double) * (size_t)I);
   for (int32_t i = 0; i < I; i++) {
-    const uint8_t *gq = ex->gate_q + (size_t)i * (h / 2);
-    const float *gs = ex->gate_s + (size_t)i * (h / 64);
-    const uint8_t *uq = ex->up_q + (size_t)i * (h / 2);
-    const float *us = ex->up_s + (size_t)i * (h / 64);
     double g = 0.0, u = 0.0;
     for (int32_t c = 0; c < h; c++) {
-      g += dq(gq, gs, c) * (double)x[c];
-      u += dq(uq, us, c) * (double)x[c];
+      g += weight_at(fmt, ex->gate_q, ex->gate_s, i, h, c) * (double)x[c];
+      u += weight_at(fmt, ex->up_q, ex->up_s, i, h, c) * (double)x[c];
     }
     double silu = g / (1.0 + exp(-g));
     m[i] = silu * u;
   }
   for (int32_t r = 0; r < h; r++) {
-    const uint8_t *q = ex->down_q + (size_t)r * (I / 2);
-    const float *s = ex->down_s + (size_t)r * (I / 64);
     double acc = 0.0;
-    for (int32_t i = 0; i < I; i++) acc += dq(q, s, i) * m[i];
+    for (int32_t i = 0; i < I; i++) acc += weight_at(fmt, ex->down_q, ex->down_s, r, I, i) * m[i];
     y[r] = acc;
   }
   free(m);
+}
+
+void coli_oracle_expert_ffn(const coli_oracle_expert_t *ex, int32_t h, int32_t I, const float *x,
+                            double *y) {
+  coli_oracle_expert_ffn_fmt(ex, 0, h, I, x, y);
 }
 
 /* ---------------------------------------------------------------------- */
@@ -385,6 +415,7 @@ typedef struct {
   /* n_experts + n_shared entries each, shared expert last; an entry may be
    * NULL for an expert that no token of the call selects. */
   const coli_oracle_expert_t *experts;
+  int32_t weight_format; /* 0: int4 gs64, 1: int8 with a scale per row */
 } coli_oracle_layer_t;
 
 /*
@@ -404,7 +435,7 @@ int coli_oracle_forward_limited(const coli_oracle_layer_t *L, const float *x, in
   if (!L || T < 0 || (T > 0 && (!x || !out))) return ORACLE_EINVAL;
   const int32_t h = L->hidden, E = L->n_experts, k = L->top_k, I = L->inter;
   if (h <= 0 || h % 64 || I <= 0 || I % 64 || E <= 0 || !L->router_w || !L->experts ||
-      (L->n_shared != 0 && L->n_shared != 1))
+      (L->n_shared != 0 && L->n_shared != 1) || (L->weight_format != 0 && L->weight_format != 1))
     return ORACLE_EINVAL;
   if (k < 1 || k > E || k_use < 1 || k_use > k || !(top_p > 0.0f && top_p <= 1.0f)) return ORACLE_EROUTE;
   if (T == 0) return ORACLE_OK;
@@ -444,7 +475,8 @@ int coli_oracle_forward_limited(const coli_oracle_layer_t *L, const float *x, in
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t p = 0; p < (int64_t)offsets[E]; p++) {
     int32_t a = sorted_ids[p];
-    coli_oracle_expert_ffn(&L->experts[idx[a]], h, I, x + (size_t)(a / k) * h, y + (size_t)p * h);
+    coli_oracle_expert_ffn_fmt(&L->experts[idx[a]], L->weight_format, h, I, x + (size_t)(a / k) * h,
+                               y + (size_t)p * h);
   }
   if (L->n_shared) {
     const coli_oracle_expert_t *sh = &L->experts[E];
@@ -453,7 +485,8 @@ int coli_oracle_forward_limited(const coli_oracle_layer_t *L, const float *x, in
       goto done;
     }
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int32_t t = 0; t < T; t++) coli_oracle_expert_ffn(sh, h, I, x + (size_t)t * h, ysh + (size_t)t * h);
+    for (int32_t t = 0; t < T; t++)
+      coli_oracle_expert_ffn_fmt(sh, L->weight_format, h, I, x + (size_t)t * h, ysh + (size_t)t * h);
   }
   /* weighted assembly per token */
   for (int32_t t = 0; t < T; t++) {

@@ -4,7 +4,8 @@ Test and benchmark infrastructure shared by the oracle side and the GPU side.
 It holds none of the layer's arithmetic: it draws numbers (SplitMix64 counter
 streams, Box-Muller normals; see gen.c) and writes them in the layer's storage
 format (int4 codes, two per byte, low nibble = even column, plus one float32
-scale per 64 consecutive input elements).
+scale per 64 consecutive input elements; or int8 codes with one float32 scale
+per row).
 
 Every tensor is its own stream, named by (seed, tag) with
 tag = layer << 40 | kind << 32 | index, so any tensor (say one expert of one
@@ -39,6 +40,9 @@ KIND_HIDDEN = 6
 KIND_ZIPF_PERM = 7
 
 WEIGHT_SIGMA = 0.02
+
+WEIGHTS_INT4_GS64 = 0   # storage formats of the expert tables
+WEIGHTS_INT8_ROW = 1
 ROUTER_SIGMA = 0.02
 HIDDEN_SIGMA = 1.0
 
@@ -79,6 +83,10 @@ def _load():
         L.synth_permutation.restype = None
         L.synth_quantize_rows.argtypes = [vp, i32, i32, vp, vp]
         L.synth_quantize_rows.restype = i32
+        L.synth_quant_matrix_i8.argtypes = [u64, u64, i32, i32, f32, vp, vp]
+        L.synth_quant_matrix_i8.restype = i32
+        L.synth_quantize_rows_i8.argtypes = [vp, i32, i32, vp, vp]
+        L.synth_quantize_rows_i8.restype = i32
         _lib = L
     return _lib
 
@@ -133,10 +141,42 @@ def quantize_rows(w: np.ndarray):
     return codes, scales
 
 
-def quant_matrix(seed: int, tg: int, rows: int, cols: int, sigma: float):
+def quant_matrix(seed: int, tg: int, rows: int, cols: int, sigma: float, weight_format: int = 0):
+    """The matrix of stream (seed, tg) in storage format weight_format (0:
+    int4 gs64, codes [rows, cols/2] and scales [rows, cols/64]; 1: int8 with
+    a scale per row, codes [rows, cols] and scales [rows])."""
+    if weight_format == WEIGHTS_INT8_ROW:
+        codes = np.empty((rows, cols), np.uint8)
+        scales = np.empty(rows, np.float32)
+        quant_matrix_i8_into(seed, tg, rows, cols, sigma, codes, scales)
+        return codes, scales
     codes = np.empty((rows, cols // 2), np.uint8)
     scales = np.empty((rows, cols // 64), np.float32)
     quant_matrix_into(seed, tg, rows, cols, sigma, codes, scales)
+    return codes, scales
+
+
+def quant_matrix_i8_into(seed: int, tg: int, rows: int, cols: int, sigma: float,
+                         codes: np.ndarray, scales: np.ndarray) -> None:
+    """Draw w[r][c] = sigma * N_{r*cols+c} and quantise to int8 with one scale
+    per row (s = absmax / 127, q = clamp(rne(w / s), -127, 127)) into caller
+    arrays (uint8 [rows, cols], float32 [rows])."""
+    assert cols % 64 == 0
+    assert codes.dtype == np.uint8 and codes.flags.c_contiguous and codes.size == rows * cols
+    assert scales.dtype == np.float32 and scales.flags.c_contiguous and scales.size == rows
+    if _load().synth_quant_matrix_i8(seed, tg, rows, cols, sigma, codes.ctypes.data, scales.ctypes.data) != 0:
+        raise ValueError("synth_quant_matrix_i8 failed")
+
+
+def quantize_rows_i8(w: np.ndarray):
+    """Quantise a caller-given float32 matrix [rows, cols] to int8 with one
+    scale per row; returns (codes [rows, cols] uint8, scales [rows])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    codes = np.empty((rows, cols), np.uint8)
+    scales = np.empty(rows, np.float32)
+    if _load().synth_quantize_rows_i8(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data):
+        raise ValueError("synth_quantize_rows_i8 failed")
     return codes, scales
 
 
@@ -158,11 +198,14 @@ class LayerShape:
     rsf: float
     bias_sigma: float
     zipf_beta: float = 0.0
+    weight_format: int = WEIGHTS_INT4_GS64
 
     @property
     def expert_bytes(self) -> int:
         """Codes + float32 scales of one expert (gate + up + down)."""
         w = 3 * self.hidden * self.inter
+        if self.weight_format == WEIGHTS_INT8_ROW:
+            return w + 4 * (2 * self.inter + self.hidden)
         return w // 2 + 4 * (w // 64)
 
 
@@ -174,6 +217,10 @@ GLM = LayerShape(hidden=6144, n_experts=256, top_k=8, inter=2048, n_shared=1, rs
 # tests/golden/zipf_calibration.py (bisection on the realised load slope).
 GLM_PREFILL_ZIPF_BETA = 0.054741911590099335
 GLM_PREFILL = dataclasses.replace(GLM, zipf_beta=GLM_PREFILL_ZIPF_BETA)
+# The same layer shape with int8 tables (one scale per row): the multi-token
+# prediction head's MoE layer, which must be int8.
+GLM_MTP_I8 = dataclasses.replace(GLM, weight_format=WEIGHTS_INT8_ROW)
+TINY_I8 = dataclasses.replace(TINY, weight_format=WEIGHTS_INT8_ROW)
 
 WORKLOADS = {
     "tiny": dict(shape=TINY, tokens=(4,), layers=1),
@@ -212,19 +259,31 @@ def hidden(shape: LayerShape, seed: int, T: int, layer: int = 0, batch: int = 0)
 
 
 def expert(shape: LayerShape, seed: int, e: int, layer: int = 0) -> dict:
-    """Tables of expert e (e == n_experts is the shared expert)."""
-    h, I = shape.hidden, shape.inter
-    gq, gs = quant_matrix(seed, tag(layer, KIND_GATE, e), I, h, WEIGHT_SIGMA)
-    uq, us = quant_matrix(seed, tag(layer, KIND_UP, e), I, h, WEIGHT_SIGMA)
-    dq, ds = quant_matrix(seed, tag(layer, KIND_DOWN, e), h, I, WEIGHT_SIGMA)
+    """Tables of expert e (e == n_experts is the shared expert), in the
+    shape's storage format."""
+    h, I, f = shape.hidden, shape.inter, shape.weight_format
+    gq, gs = quant_matrix(seed, tag(layer, KIND_GATE, e), I, h, WEIGHT_SIGMA, f)
+    uq, us = quant_matrix(seed, tag(layer, KIND_UP, e), I, h, WEIGHT_SIGMA, f)
+    dq, ds = quant_matrix(seed, tag(layer, KIND_DOWN, e), h, I, WEIGHT_SIGMA, f)
     return dict(gate_q=gq, gate_s=gs, up_q=uq, up_s=us, down_q=dq, down_s=ds)
 
 
 def routed_tables(shape: LayerShape, seed: int, layer: int = 0, experts=None) -> dict:
     """Stacked tables of the routed experts: gate_q/up_q [E][I][h/2],
-    gate_s/up_s [E][I][h/64], down_q [E][h][I/2], down_s [E][h][I/64].
+    gate_s/up_s [E][I][h/64], down_q [E][h][I/2], down_s [E][h][I/64] (int8
+    tables: gate_q/up_q [E][I][h], gate_s/up_s [E][I], down_q [E][h][I],
+    down_s [E][h]).
     `experts` restricts generation to a subset (others stay zero)."""
     h, I, E = shape.hidden, shape.inter, shape.n_experts
+    if shape.weight_format == WEIGHTS_INT8_ROW:
+        t = dict(gate_q=np.zeros((E, I, h), np.uint8), gate_s=np.zeros((E, I), np.float32),
+                 up_q=np.zeros((E, I, h), np.uint8), up_s=np.zeros((E, I), np.float32),
+                 down_q=np.zeros((E, h, I), np.uint8), down_s=np.zeros((E, h), np.float32))
+        for e in (range(E) if experts is None else experts):
+            quant_matrix_i8_into(seed, tag(layer, KIND_GATE, e), I, h, WEIGHT_SIGMA, t["gate_q"][e], t["gate_s"][e])
+            quant_matrix_i8_into(seed, tag(layer, KIND_UP, e), I, h, WEIGHT_SIGMA, t["up_q"][e], t["up_s"][e])
+            quant_matrix_i8_into(seed, tag(layer, KIND_DOWN, e), h, I, WEIGHT_SIGMA, t["down_q"][e], t["down_s"][e])
+        return t
     t = dict(gate_q=np.zeros((E, I, h // 2), np.uint8), gate_s=np.zeros((E, I, h // 64), np.float32),
              up_q=np.zeros((E, I, h // 2), np.uint8), up_s=np.zeros((E, I, h // 64), np.float32),
              down_q=np.zeros((E, h, I // 2), np.uint8), down_s=np.zeros((E, h, I // 64), np.float32))

@@ -26,6 +26,7 @@
  * Built with -ffp-contract=off so no multiply-add is fused behind our back.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -219,6 +220,57 @@ int synth_quant_matrix(uint64_t seed, uint64_t tag, int rows, int cols, float si
       }
     }
   }
+  return 0;
+}
+
+/* int8 storage with one scale per row: s = absmax(row) / 127,
+ * q = clamp(rne(w / s), -127, 127) as a two's-complement byte (an all-zero
+ * row gives s = 0, q = 0; -128 never occurs here but is legal input). */
+__attribute__((target_clones("avx2", "default")))
+static void quant_row_i8(const float *w, int cols, uint8_t *codes, float *scale) {
+  float amax = 0.0f;
+  for (int c = 0; c < cols; c++) {
+    float a = fabsf(w[c]);
+    amax = a > amax ? a : amax;
+  }
+  float s = amax / 127.0f;
+  *scale = s;
+  for (int c = 0; c < cols; c++) {
+    int32_t q = 0;
+    if (s > 0.0f) {
+      float r = rintf(w[c] / s);
+      r = r < -127.0f ? -127.0f : r;
+      r = r > 127.0f ? 127.0f : r;
+      q = (int32_t)r;
+    }
+    codes[c] = (uint8_t)(q & 0xFF);
+  }
+}
+
+/* As synth_quant_matrix, int8 with a scale per row: codes [rows][cols],
+ * scales [rows].  cols must be a positive multiple of 64.  Returns 0 or -1. */
+int synth_quant_matrix_i8(uint64_t seed, uint64_t tag, int rows, int cols, float sigma,
+                          uint8_t *codes, float *scales) {
+  if (rows < 0 || cols <= 0 || cols % 64 || cols > 65536) return -1;
+  uint64_t key = synth_stream_key(seed, tag);
+#pragma omp parallel
+  {
+    float *wbuf = (float *)malloc(sizeof(float) * (size_t)cols);
+#pragma omp for schedule(static)
+    for (int r = 0; r < rows; r++) {
+      uint64_t first = (uint64_t)r * cols;
+      normal_range(key, first, first + cols, sigma, wbuf);
+      quant_row_i8(wbuf, cols, codes + (size_t)r * cols, scales + r);
+    }
+    free(wbuf);
+  }
+  return 0;
+}
+
+/* Caller-given float weights [rows, cols], int8 per row (crafted inputs). */
+int synth_quantize_rows_i8(const float *w, int rows, int cols, uint8_t *codes, float *scales) {
+  if (rows < 0 || cols <= 0) return -1;
+  for (int r = 0; r < rows; r++) quant_row_i8(w + (size_t)r * cols, cols, codes + (size_t)r * cols, scales + r);
   return 0;
 }
 

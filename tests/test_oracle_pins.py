@@ -584,3 +584,111 @@ def test_forward_with_routing_limits_equals_mixture_of_kept(k_use, top_p):
                 te = {kk: v[idx[t, j]] for kk, v in routed.items()}
                 mix = mix + float(w[t, j]) * _ffn_numpy(te, x[t])
         assert np.allclose(out[t], mix, rtol=1e-6, atol=1e-6 * np.abs(mix).max())
+
+
+# --------------------------------------------------------------------------
+# int8 tables with one scale per row (the MTP head's format).
+# --------------------------------------------------------------------------
+
+def test_int8_code_all_bytes():
+    """Every byte reads as its two's-complement value (numpy's int8 view is
+    the independent reference)."""
+    row = np.arange(256, dtype=np.uint8)
+    want = row.view(np.int8).astype(int).tolist()
+    assert [oracle.int8_code(row, c) for c in range(256)] == want
+
+
+def test_int8_quantiser_properties():
+    rng = np.random.default_rng(12)
+    w = (0.02 * rng.standard_normal((40, 192))).astype(np.float32)
+    w[3] = 0.0
+    codes, scales = synth.quantize_rows_i8(w)
+    q = codes.view(np.int8).astype(np.float64)
+    assert q.min() >= -127 and q.max() <= 127
+    assert np.all(scales[3] == 0) and np.all(q[3] == 0)
+    s = scales.astype(np.float64)[:, None]
+    assert np.all(np.abs(w - q * s) <= s / 2 * (1 + 1e-6) + 1e-30)
+    # the row's largest weight maps to +-127
+    nz = np.arange(40) != 3
+    assert np.all(np.abs(q[nz]).max(axis=1) == 127)
+
+
+def _dequant_i8(codes, scales):
+    return codes.view(np.int8).astype(np.float64) * scales.astype(np.float64)[:, None]
+
+
+def _ffn_numpy_i8(t, x):
+    wg, wu, wd = _dequant_i8(t["gate_q"], t["gate_s"]), _dequant_i8(t["up_q"], t["up_s"]), _dequant_i8(t["down_q"], t["down_s"])
+    x = x.astype(np.float64)
+    g, u = wg @ x, wu @ x
+    return wd @ (g / (1.0 + np.exp(-g)) * u)
+
+
+def test_int8_expert_ffn_closed_form():
+    """Gate codes 3, up codes -2, down codes 5 (every byte), row scales 0.25,
+    x = 0.01: g = 0.75 * h * 0.01, u = -2 g / 3, m = silu(g) u,
+    y_r = 1.25 * I * m."""
+    h, I = 128, 64
+    t = dict(gate_q=np.full((I, h), 3, np.uint8), gate_s=np.full(I, 0.25, np.float32),
+             up_q=np.full((I, h), 254, np.uint8), up_s=np.full(I, 0.25, np.float32),
+             down_q=np.full((h, I), 5, np.uint8), down_s=np.full(h, 0.25, np.float32))
+    x = np.full(h, 0.01, np.float32)
+    xs = float(np.float32(0.01)) * h
+    g = 0.75 * xs
+    u = -0.5 * xs
+    m = g / (1 + math.exp(-g)) * u
+    y = oracle.expert_ffn(t, x, weight_format=1)
+    assert np.allclose(y, 1.25 * I * m, rtol=1e-13, atol=0)
+
+
+def test_int8_expert_ffn_matches_numpy_float64():
+    shape = synth.TINY_I8
+    t = synth.expert(shape, 5, 2)
+    assert t["gate_q"].shape == (shape.inter, shape.hidden) and t["gate_s"].shape == (shape.inter,)
+    x = synth.hidden(shape, 5, 3)
+    for r in range(3):
+        assert np.allclose(oracle.expert_ffn(t, x[r], weight_format=1), _ffn_numpy_i8(t, x[r]), rtol=1e-12,
+                           atol=1e-15)
+
+
+def test_int8_all_codes_including_minus_128():
+    """Random bytes (every code, -128 included) and random row scales."""
+    rng = np.random.default_rng(13)
+    h, I = 128, 64
+    t = dict(gate_q=rng.integers(0, 256, (I, h), dtype=np.uint8), gate_s=rng.uniform(1e-4, 1e-3, I).astype(np.float32),
+             up_q=rng.integers(0, 256, (I, h), dtype=np.uint8), up_s=rng.uniform(1e-4, 1e-3, I).astype(np.float32),
+             down_q=rng.integers(0, 256, (h, I), dtype=np.uint8), down_s=rng.uniform(1e-4, 1e-3, h).astype(np.float32))
+    x = rng.standard_normal(h).astype(np.float32)
+    assert np.allclose(oracle.expert_ffn(t, x, weight_format=1), _ffn_numpy_i8(t, x), rtol=1e-12, atol=1e-15)
+
+
+def test_int8_single_expert_layer_is_scaled_swiglu():
+    shape = synth.LayerShape(hidden=128, n_experts=1, top_k=1, inter=192, n_shared=1, rsf=2.5, bias_sigma=0.0,
+                             weight_format=synth.WEIGHTS_INT8_ROW)
+    wr, b = synth.router(shape, 3)
+    routed = synth.routed_tables(shape, 3)
+    sh = synth.shared_tables(shape, 3)
+    x = synth.hidden(shape, 3, 5)
+    out, idx, w = oracle.forward(shape, wr, b, routed, sh, x)
+    assert np.all(idx == 0) and np.all(w == np.float32(2.5))
+    t0 = {k: v[0] for k, v in routed.items()}
+    for r in range(5):
+        ref = 2.5 * _ffn_numpy_i8(t0, x[r]) + _ffn_numpy_i8(sh, x[r])
+        assert np.allclose(out[r], ref, rtol=2e-7, atol=1e-7 * np.abs(ref).max())
+
+
+def test_int8_forced_all_experts_equals_dense_mixture():
+    E = 6
+    shape = synth.LayerShape(hidden=128, n_experts=E, inter=64, n_shared=1, rsf=2.5, top_k=E, bias_sigma=0.0,
+                             weight_format=synth.WEIGHTS_INT8_ROW)
+    wr, b = synth.router(shape, 24)
+    routed = synth.routed_tables(shape, 24)
+    sh = synth.shared_tables(shape, 24)
+    x = synth.hidden(shape, 24, 4)
+    out, _, _ = oracle.forward(shape, wr, b, routed, sh, x)
+    s = 1.0 / (1.0 + np.exp(-(x.astype(np.float64) @ wr.astype(np.float64))))
+    for t in range(4):
+        mix = _ffn_numpy_i8(sh, x[t])
+        for e in range(E):
+            mix += s[t, e] / s[t].sum() * shape.rsf * _ffn_numpy_i8({k: v[e] for k, v in routed.items()}, x[t])
+        assert np.allclose(out[t], mix, rtol=1e-5, atol=1e-5 * np.abs(mix).max())
