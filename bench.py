@@ -10,10 +10,18 @@ change from call to call and the 256 MB Infinity Cache cannot serve them).
 
 Also measured in the same run (extra fields of the JSON line):
   decode_batches  the same 8-layer stack at T = 2, 4 and 64 tokens per call;
+  routing_limits_decode_T1  the stack at T = 1 with the lossy routing
+                  overrides (adaptive expert top-p, explicit smaller k);
   prefill         T = 4096 tokens on the GLM-like layer with Zipf-skewed
                   expert load (fp16 MFMA path): tokens/s and the grouped-GEMM
                   kernels' FLOP rate against the fp16 dense peak and against
-                  the rate this GPU sustains on varied fp16 operands.
+                  the rate this GPU sustains on varied fp16 operands;
+  small_configs   the tiny layer (T = 4) and the OLMoE-like layer (T = 16,
+                  8 weight copies in turn so that HBM serves every call);
+  int8_mtp_layer  the GLM-like layer with int8 tables (the MTP head's
+                  format) at T = 1..4;
+  expert_cache    the GLM-like layer served from pinned host memory through
+                  an HBM expert cache, and the router look-ahead prefetch.
 
 Prints one JSON line: MoE-layer tokens/s (value), expert-weight HBM GB/s, the
 roofline of the dominant kernel (per-launch algorithmic bytes over its mean
@@ -24,6 +32,7 @@ the CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
     python bench.py --copy-calibration   # plain 1 GiB device copy (counter scale)
     python bench.py --prefill-only       # the prefill layer alone (for counter runs)
+    python bench.py --int8-only          # the int8 (MTP-head format) layer alone
 """
 from __future__ import annotations
 
@@ -64,6 +73,8 @@ def parse():
     ap.add_argument("--no-cache", action="store_true", help="skip the expert-cache rows")
     ap.add_argument("--cache-only", action="store_true",
                     help="only the expert-cache rows (host-backed GLM-like layer): print their JSON object and exit")
+    ap.add_argument("--int8-only", action="store_true",
+                    help="only the int8-table layer (the MTP head's format): print its JSON object and exit")
     return ap.parse_args()
 
 
@@ -213,6 +224,9 @@ def main():
         return
     if args.cache_only:
         print(json.dumps(cache_rows(args, cm, torch, np, synth, dev)), flush=True)
+        return
+    if args.int8_only:
+        print(json.dumps(int8_rows(args, cm, torch, np, synth, dev)), flush=True)
         return
     shape = synth.GLM
     L, K, W = args.layers, args.steps, args.warmup
@@ -425,6 +439,10 @@ def main():
         result["prefill"]["mfma_gemm_frac_of_measured_f16_varied"] = round(
             result["prefill"]["mfma_gemm_tflops"] / peaks["mfma_f16_varied_TFLOPs"], 4)
 
+    if not args.no_extra:
+        result["small_configs"] = small_config_rows(args, cm, torch, np, synth, dev)
+        result["int8_mtp_layer"] = int8_rows(args, cm, torch, np, synth, dev)
+
     if not args.no_extra and not args.no_cache:
         result["expert_cache"] = cache_rows(args, cm, torch, np, synth, dev)
 
@@ -472,6 +490,123 @@ def prefill(args, cm, torch, np, synth, dev):
     lay.close()
     del tensors
     log(f"prefill: {res}")
+    return res
+
+
+def small_config_rows(args, cm, torch, np, synth, dev):
+    """The two small configurations: the tiny layer at T = 4 (launch-latency
+    bound: microseconds per forward) and the OLMoE-like layer at T = 16
+    (HBM-bound).  The OLMoE-like layer's 226 MB would sit in the 256 MB
+    Infinity Cache, so 8 independent copies (8 seeded layers, 1.8 GB) are
+    called in turn: each call's experts come from HBM.  Each layer's output
+    is checked against the oracle once, outside the timed region."""
+    import oracle
+    res = {}
+    for name, shape, T, n_layers in (("tiny", synth.TINY, 4, 1), ("olmoe_like", synth.OLMOE, 16, 8)):
+        h, E, k = shape.hidden, shape.n_experts, shape.top_k
+        lays, keep = [], []
+        for l in range(n_layers):
+            wr, b = synth.router(shape, args.seed, l)
+            t = {"router_w": torch.from_numpy(wr).to(dev), "sel_bias": torch.from_numpy(b).to(dev)}
+            routed = synth.routed_tables(shape, args.seed, l)
+            t.update({n: torch.from_numpy(v).to(dev) for n, v in routed.items()})
+            shared = synth.shared_tables(shape, args.seed, l)
+            if shared is not None:
+                t.update({"sh_" + n: torch.from_numpy(v).to(dev) for n, v in shared.items()})
+            cfg = cm.make_config(hidden=h, n_experts=E, top_k=k, inter=shape.inter, n_shared=shape.n_shared,
+                                 routed_scaling_factor=shape.rsf, max_tokens=T)
+            lays.append(cm.MoELayer(cfg, t))
+            keep.append(t)
+            if l == 0:  # parity of the timed configuration, once
+                x0 = synth.hidden(shape, args.seed, T, layer=l, batch=77)
+                got = lays[0](torch.from_numpy(x0).to(dev)).cpu().numpy()
+                ref, _, _ = oracle.forward(shape, wr, b, routed, shared, x0)
+                den = np.maximum(np.abs(ref), np.sqrt((ref.astype(np.float64) ** 2).mean(axis=1, keepdims=True)))
+                parity = float((np.abs(got - ref) / den).max())
+            del routed, shared
+        pool = 16
+        xs = [[torch.from_numpy(synth.hidden(shape, args.seed, T, layer=l, batch=500 + i)).to(dev) for i in range(pool)]
+              for l in range(n_layers)]
+        out = torch.empty((T, h), dtype=torch.float32, device=dev)
+        na = np.zeros((n_layers, pool), np.int64)
+        for l in range(n_layers):
+            for i in range(pool):
+                lays[l](xs[l][i], out)
+                _, r = lays[l].last_routing()
+                na[l, i] = int(r["n_active"].item())
+        n = max(200, args.steps)
+        call = lambda c: lays[c % n_layers](xs[c % n_layers][(c // n_layers) % pool], out)
+        for c in range(10):
+            call(c)
+        ms = time_calls(torch, call, n)
+        reads = sum(int(na[c % n_layers, (c // n_layers) % pool]) + shape.n_shared for c in range(n))
+        nbytes = reads * shape.expert_bytes + n * (h * E * 4)
+        res[name] = {"workload": f"{name} layer h={h} E={E} k={k} I={shape.inter} shared={shape.n_shared}, T={T}"
+                                 + (f", {n_layers} weight copies called in turn" if n_layers > 1 else ""),
+                     "tokens_per_s": round(T * n / (ms / 1e3), 1), "us_per_call": round(1e3 * ms / n, 3),
+                     "mean_distinct_experts": round(float(na.mean()), 2),
+                     "weights_GBps": round(nbytes / (ms / 1e3) / 1e9, 1),
+                     "weights_frac_of_hbm_peak": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "max_rel_err_vs_oracle": parity}
+        log(f"{name}: {res[name]}")
+        for lay in lays:
+            lay.close()
+        del lays, keep, xs
+    return res
+
+
+def int8_rows(args, cm, torch, np, synth, dev):
+    """The GLM-like layer with int8 tables (one scale per row, the multi-token
+    prediction head's format), resident: draft (T = 1) and verify (T = 2..4)
+    calls on a pool of fresh inputs; tokens/s, expert-weight GB/s, and the
+    gate/up launch's algorithmic bytes over its HIP-event time."""
+    shape = synth.GLM_MTP_I8
+    h, I, E, k = shape.hidden, shape.inter, shape.n_experts, shape.top_k
+    t0 = time.time()
+    wr, b = synth.router(shape, args.seed, 0)
+    tensors = {"router_w": torch.from_numpy(wr).to(dev), "sel_bias": torch.from_numpy(b).to(dev)}
+    tensors.update({n: torch.from_numpy(v).to(dev) for n, v in synth.routed_tables(shape, args.seed, 0).items()})
+    tensors.update({"sh_" + n: torch.from_numpy(v).to(dev) for n, v in synth.shared_tables(shape, args.seed, 0).items()})
+    cfg = cm.make_config(hidden=h, n_experts=E, top_k=k, inter=I, n_shared=shape.n_shared,
+                         routed_scaling_factor=shape.rsf, max_tokens=4, weight_format=cm.COLI_MOE_WEIGHTS_INT8_ROW)
+    lay = cm.MoELayer(cfg, tensors)
+    log(f"int8 MTP layer resident ({time.time() - t0:.1f} s)")
+    eb = shape.expert_bytes
+    gate_up_w = 2 * (I * h + 4 * I)
+    res = {"workload": f"GLM-5.2-like MoE layer with int8 tables (scale per row), h={h} E={E} k={k} I={I}, 1 layer resident",
+           "expert_bytes": eb}
+    pool = 32
+    for T in (1, 2, 3, 4):
+        xs = [torch.from_numpy(synth.hidden(shape, args.seed, T, batch=9000 + 100 * T + i)).to(dev) for i in range(pool)]
+        out = torch.empty((T, h), dtype=torch.float32, device=dev)
+        na = []
+        for x in xs:
+            lay(x, out)
+            _, r = lay.last_routing()
+            na.append(int(r["n_active"].item()))
+        n = max(40, args.steps)
+        for i in range(5):
+            lay(xs[i % pool], out)
+        ms = time_calls(torch, lambda i: lay(xs[i % pool], out), n)
+        reads = sum(na[i % pool] + shape.n_shared for i in range(n))
+        kern = kernel_profile(cm, [lay.handle], lambda: [lay(xs[i % pool], out) for i in range(n)], n)
+        gu = kern.get("expert_gemv_gate_up", (0.0, 1))
+        dn = kern.get("expert_gemv_down", (0.0, 1))
+        gu_us, dn_us = 1e3 * gu[0] / gu[1], 1e3 * dn[0] / dn[1]
+        mean_e = float(np.mean(na)) + shape.n_shared
+        gu_bytes = mean_e * gate_up_w + T * (3 * h + h // 8) + (T * k + T * shape.n_shared) * I * 4
+        row = {"tokens_per_s": round(T * n / (ms / 1e3), 1), "us_per_call": round(1e3 * ms / n, 2),
+               "mean_distinct_experts": round(float(np.mean(na)), 2),
+               "expert_weight_GBps": round(reads * eb / (ms / 1e3) / 1e9, 1),
+               "kernel_avg_us": {nm: round(1e3 * t / c, 2) for nm, (t, c) in kern.items()},
+               "gate_up_GBps": round(gu_bytes / gu_us / 1e3, 1),
+               "gate_up_frac_of_hbm_peak": round(gu_bytes / gu_us / 1e3 / HBM_PEAK_GBPS, 4),
+               "down_GBps": round((mean_e * h * (I + 4) + (T * k + T) * I * 4) / dn_us / 1e3, 1)}
+        res[f"T{T}"] = row
+        log(f"int8 MTP layer T={T}: {row}")
+        del xs
+    lay.close()
+    del tensors
     return res
 
 

@@ -53,7 +53,7 @@ extern "C" {
 /* Error codes (0 = success). */
 #define COLI_MOE_OK 0
 #define COLI_MOE_ECAPACITY (-1) /* T > max_tokens, or the workspace is too small */
-#define COLI_MOE_EROUTING (-2)  /* top_k < 1 or > n_experts or > 32, n_group != 1, group_size != 64 */
+#define COLI_MOE_EROUTING (-2)  /* top_k < 1 or > n_experts or > 32, n_group != 1, group_size not the format's */
 #define COLI_MOE_EDEVICE (-3)   /* a HIP launch or runtime call failed */
 #define COLI_MOE_EARG (-4)      /* NULL or misaligned pointer, unsupported dimension */
 
@@ -64,12 +64,38 @@ typedef struct {
   int32_t top_k;             /* k: experts per token, 1..min(E, 32) */
   int32_t inter;             /* I: expert intermediate size, multiple of 64, 64..16384 */
   int32_t n_shared;          /* shared experts: 0 or 1 */
-  int32_t group_size;        /* weights per scale: must be 64 */
+  int32_t group_size;        /* weights per scale: 64 for int4 gs64, 0 (a whole row) for int8 */
   int32_t n_group;           /* expert groups of noaux_tc: must be 1 */
   int32_t max_tokens;        /* most tokens one forward may take, >= 1 */
   int32_t prefill_threshold; /* T >= this takes the MFMA (fp16) path; 0 = 256 */
   float routed_scaling_factor;
+  int32_t weight_format;     /* COLI_MOE_WEIGHTS_*: storage of the expert tables */
 } coli_moe_config_t;
+
+/*
+ * Expert table formats (weight_format).
+ *
+ * COLI_MOE_WEIGHTS_INT4_GS64 (0): the routed experts' format of the
+ *   teardown page ("Three key engineering decisions", item 1): int4 codes,
+ *   one float32 scale per 64 weights along the input axis (layout below).
+ *
+ * COLI_MOE_WEIGHTS_INT8_ROW (1): int8 codes with one float32 scale per
+ *   output row, the precision the same page requires of the MTP head
+ *   ("MTP head must be int8": int4 drafts are almost never accepted) and
+ *   one of the engine's per-row-scaled kernel formats.  A matrix
+ *   [rows][cols] is rows of cols int8 two's-complement codes (byte c =
+ *   column c), scale s[row]; weight = q * s[row].  Tables: gate_q, up_q
+ *   [E][inter][hidden] bytes, gate_s, up_s [E][inter] floats, down_q
+ *   [E][hidden][inter] bytes, down_s [E][hidden] floats (shared expert
+ *   alike).  group_size must be 0.  Every forward runs the GEMV kernels'
+ *   small-batch launches (draft and verify shapes: 1 to 4 tokens);
+ *   larger T runs them on consecutive groups of up to 4 tokens, each group
+ *   reading its experts again, then publishes the routing of the whole
+ *   batch.  Requires inter <= 4096 and a hidden row's planes to fit
+ *   (hidden <= 16384); no prefill path and no expert cache.
+ */
+#define COLI_MOE_WEIGHTS_INT4_GS64 0
+#define COLI_MOE_WEIGHTS_INT8_ROW 1
 
 /*
  * Weight tables, all DEVICE pointers, borrowed (the caller owns them and

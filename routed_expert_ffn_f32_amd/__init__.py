@@ -41,7 +41,8 @@ class coli_moe_config_t(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("n_group", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
-                ("prefill_threshold", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float)]
+                ("prefill_threshold", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
+                ("weight_format", ctypes.c_int32)]
 
 
 class coli_moe_weights_t(ctypes.Structure):
@@ -354,12 +355,19 @@ def coli_moe_test_cache_policy(n_experts, n_slots, reserve, decay, repin_every, 
 _WEIGHT_KEYS = ("gate_q", "gate_s", "up_q", "up_s", "down_q", "down_s")
 
 
+COLI_MOE_WEIGHTS_INT4_GS64 = 0
+COLI_MOE_WEIGHTS_INT8_ROW = 1
+
+
 def make_config(hidden, n_experts, top_k, inter, n_shared, routed_scaling_factor, max_tokens,
-                prefill_threshold=0, group_size=64, n_group=1) -> coli_moe_config_t:
+                prefill_threshold=0, group_size=None, n_group=1,
+                weight_format=COLI_MOE_WEIGHTS_INT4_GS64) -> coli_moe_config_t:
+    if group_size is None:
+        group_size = 0 if weight_format == COLI_MOE_WEIGHTS_INT8_ROW else 64
     return coli_moe_config_t(hidden=hidden, n_experts=n_experts, top_k=top_k, inter=inter, n_shared=n_shared,
                              group_size=group_size, n_group=n_group, max_tokens=max_tokens,
                              prefill_threshold=prefill_threshold,
-                             routed_scaling_factor=routed_scaling_factor)
+                             routed_scaling_factor=routed_scaling_factor, weight_format=weight_format)
 
 
 class MoELayer:

@@ -52,9 +52,19 @@ bool prefill_shape(const coli_moe_config_t &c) {
          P * (uint64_t)c.inter * 2 < (1ull << 32);
 }
 
-// True when the handle's workspace holds the prefill buffers.
+bool int8_tables(const coli_moe_config_t &c) { return c.weight_format == COLI_MOE_WEIGHTS_INT8_ROW; }
+
+// True when the handle's workspace holds the prefill buffers (int4 tables).
 bool prefill_enabled(const coli_moe_config_t &c) {
-  return prefill_shape(c) && (c.prefill_threshold == 0 ? 256 : c.prefill_threshold) <= c.max_tokens;
+  return !int8_tables(c) && prefill_shape(c) && (c.prefill_threshold == 0 ? 256 : c.prefill_threshold) <= c.max_tokens;
+}
+
+// Tokens per group of an int8 forward: the most (up to the small-batch
+// limits) that take the small-batch launches; 0 if not even one does.
+int int8_group(const coli_moe_config_t &c) {
+  for (int g = coli::kSmallT; g >= 1; --g)
+    if (coli::small_batch(g, c.top_k, c.hidden, c.inter, true)) return g;
+  return 0;
 }
 
 bool config_ok(const coli_moe_config_t &c, int *code) {
@@ -64,9 +74,17 @@ bool config_ok(const coli_moe_config_t &c, int *code) {
     *code = COLI_MOE_EARG;
     return false;
   }
+  if (c.weight_format != COLI_MOE_WEIGHTS_INT4_GS64 && c.weight_format != COLI_MOE_WEIGHTS_INT8_ROW) {
+    *code = COLI_MOE_EARG;
+    return false;
+  }
   if (c.top_k < 1 || c.top_k > c.n_experts || c.top_k > coli::kMaxTopK || c.n_group != 1 ||
-      c.group_size != 64) {
+      c.group_size != (int8_tables(c) ? 0 : 64)) {
     *code = COLI_MOE_EROUTING;
+    return false;
+  }
+  if (int8_tables(c) && int8_group(c) == 0) {
+    *code = COLI_MOE_EARG;
     return false;
   }
   if ((int64_t)c.max_tokens * c.top_k > (1 << 20)) {
@@ -267,14 +285,15 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
   const float rsf = c.routed_scaling_factor;
   const coli::RouteLimits lim{m->k_use, m->top_p};
 
-  const bool prefill = T >= c.prefill_threshold && prefill_shape(c);
-  const bool small = !prefill && coli::small_batch(T, k, h, I);
+  const bool int8 = int8_tables(c);
+  const bool prefill = !int8 && T >= c.prefill_threshold && prefill_shape(c);
+  const bool small = !prefill && coli::small_batch(T, k, h, I, int8);
   hipError_t e;
   // 1. router logits (and, for the GEMV path, the hidden rows in digit-plane
   // form)
   if (phase & kPhaseRoute) {
     e = timed(m, K_ROUTER_LOGITS, s, [&] {
-      return launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill ? nullptr : xq, xs, s);
+      return launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill ? nullptr : xq, xs, int8, s);
     });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
   }
@@ -343,6 +362,7 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
   P.E = E;
   P.n_routed_slots = E < T * k ? E : T * k;
   P.has_shared = c.n_shared;
+  P.int8 = int8 ? 1 : 0;
   P.rsf = rsf;
   P.lim = lim;
   P.logits = logits;
@@ -369,6 +389,25 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     e = timed(m, K_DOWN, s, [&] { return launch_down_combine(P, out, s); });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
+  } else if (int8) {
+    // int8 tables: consecutive groups of G tokens through the small-batch
+    // launches (each group routes itself; the router launch above covered
+    // every token), then the selection and dispatch of the whole batch, so
+    // that the routing arrays describe the call
+    const int G = int8_group(c);
+    for (int t0 = 0; t0 < T; t0 += G) {
+      coli::DecodeProblem Pg = P;
+      Pg.T = std::min(G, T - t0);
+      Pg.n_routed_slots = std::min(E, Pg.T * k);
+      Pg.logits = logits + (size_t)t0 * E;
+      Pg.xq = xq + (size_t)t0 * (3 * (h / 4));
+      Pg.xs = xs + (size_t)t0 * (h / 32);
+      e = timed(m, K_GATE_UP, s, [&] { return launch_gemv_gate_up(Pg, s); });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+      e = timed(m, K_DOWN, s, [&] { return launch_down_combine(Pg, out + (size_t)t0 * h, s); });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+    }
+    if (select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
   } else {
     // 2. selection and dispatch
     if (!routed && select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
@@ -513,7 +552,9 @@ int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, 
 }
 
 int coli_moe_probe_read(const coli_moe_t *mc, const int32_t *experts, int32_t n, void *stream) {
-  if (!mc || !experts || n < 1 || n > 64 || mc->cfg.hidden > 8192) return COLI_MOE_EARG;
+  if (!mc || !experts || n < 1 || n > 64 || mc->cfg.hidden > 8192 ||
+      mc->cfg.weight_format != COLI_MOE_WEIGHTS_INT4_GS64)
+    return COLI_MOE_EARG;
   coli_moe_t *m = const_cast<coli_moe_t *>(mc);
   coli::DecodeProblem P{};
   P.gate = {m->w.gate_q, m->w.gate_s};

@@ -170,7 +170,9 @@ int call_reserve(const coli_moe_config_t &cfg) {
 extern "C" {
 
 size_t coli_moe_cache_slot_bytes(const coli_moe_config_t *cfg, int32_t n_slots) {
-  if (!cfg || coli::config_check(*cfg) != COLI_MOE_OK || n_slots < 1 || n_slots > cfg->n_experts) return 0;
+  if (!cfg || coli::config_check(*cfg) != COLI_MOE_OK || n_slots < 1 || n_slots > cfg->n_experts ||
+      cfg->weight_format != COLI_MOE_WEIGHTS_INT4_GS64)
+    return 0;
   return slot_layout(*cfg, n_slots).total;
 }
 
@@ -181,6 +183,7 @@ int coli_moe_cache_init(coli_moe_cache_t **out, const coli_moe_config_t *cfg, co
   *out = nullptr;
   int code = coli::config_check(*cfg);
   if (code != COLI_MOE_OK) return code;
+  if (cfg->weight_format != COLI_MOE_WEIGHTS_INT4_GS64) return COLI_MOE_EARG;  // slots hold int4 gs64 tables
   const int S = cc->n_slots;
   if (S < 1 || S > cfg->n_experts) return COLI_MOE_EARG;
   if (S < call_reserve(*cfg)) return COLI_MOE_ECAPACITY;

@@ -368,7 +368,6 @@ constexpr int kSbBlocksLds = kSbBlocks / 2; // gate/up grid, T = 2..4 (8 waves p
 constexpr int kDcWaves = 8;     // down: waves per block
 constexpr int kDcBlocks = 256;   // down: blocks (at most; fewer when h is small)
 constexpr int kDcLds = 64 * 1024;           // down: LDS for the digit planes of a slot group
-constexpr int kSbMaxXChunks = 4;            // T = 1 keeps the planes of h <= 64*32*4 columns in registers
 constexpr int kSbMaxXLds = 96 * 1024;       // bytes of hidden-row planes staged in LDS
 constexpr int kDcMaxChunks = 4;             // down: I <= 64*32*4
 constexpr int kDcMaxRing = 2;    // down: slots in flight per wave, at most
@@ -381,6 +380,7 @@ struct GuCursor {
   int p_begin, cnt;         // positions p_begin .. p_begin + cnt - 1 of mid
 };
 
+template <class F>
 __device__ __forceinline__ void gu_set_slot(const DecodeProblem &P, const SmallRouting &R, GuCursor &c) {
   const int hs = P.has_shared;
   if (c.slot < hs) {
@@ -394,7 +394,7 @@ __device__ __forceinline__ void gu_set_slot(const DecodeProblem &P, const SmallR
   }
   const int s = min(c.slot - hs, kSmallAssign - 1);
   const int e = uniform(R.active[s]);
-  const size_t qstride = (size_t)P.I * (P.h >> 1), sstride = (size_t)P.I * (P.h >> 6);
+  const size_t qstride = (size_t)P.I * F::row_bytes(P.h), sstride = (size_t)P.I * F::row_scales(P.h);
   const size_t x = table_index(P.slot_of, e);
   c.qg = P.gate.q + x * qstride;
   c.sg = P.gate.s + x * sstride;
@@ -404,72 +404,89 @@ __device__ __forceinline__ void gu_set_slot(const DecodeProblem &P, const SmallR
   c.cnt = uniform(R.seg_begin[s + 1]) - c.p_begin;
 }
 
-template <int NCH>
+// NS: scales per lane (one per chunk for int4 gs64, the row's one for int8)
+template <int NCH, class F = FmtI4>
 struct GuBuf {
+  static constexpr int NS = F::kRowScale ? 1 : NCH;
   uint4 g[NCH], u[NCH];
-  float gs[NCH], us[NCH];
+  float gs[NS], us[NS];
 };
 
 // Codes and scales of row c.r of the slot's gate and up matrices for this
 // lane's chunks; an invalid row (or chunks past the row) reads zeros.
-template <int NCH>
-__device__ __forceinline__ void gu_load(GuBuf<NCH> &b, const GuCursor &c, bool valid, int h) {
+template <int NCH, class F>
+__device__ __forceinline__ void gu_load(GuBuf<NCH, F> &b, const GuCursor &c, bool valid, int h) {
   const int lane = threadIdx.x & 63;
-  const uint32_t rowq = (uint32_t)h >> 1, rows = (uint32_t)(h >> 6) * 4;
+  const uint32_t rowq = F::row_bytes(h), nsc = F::row_scales(h), rows = nsc * 4;
   const size_t r = (size_t)c.r;
   const Rsrc qg = make_rsrc(c.qg + r * rowq, valid ? rowq : 0u);
   const Rsrc qu = make_rsrc(c.qu + r * rowq, valid ? rowq : 0u);
-  const Rsrc sg = make_rsrc(c.sg + r * (h >> 6), valid ? rows : 0u);
-  const Rsrc su = make_rsrc(c.su + r * (h >> 6), valid ? rows : 0u);
+  const Rsrc sg = make_rsrc(c.sg + r * nsc, valid ? rows : 0u);
+  const Rsrc su = make_rsrc(c.su + r * nsc, valid ? rows : 0u);
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     const uint32_t lc = (uint32_t)(lane + 64 * cc);
     b.g[cc] = bload16(qg, lc * 16, 0);
     b.u[cc] = bload16(qu, lc * 16, 0);
   }
+  if constexpr (F::kRowScale) {
+    b.gs[0] = bloadf(sg, 0, 0);
+    b.us[0] = bloadf(su, 0, 0);
+  } else {
 #pragma unroll
-  for (int cc = 0; cc < NCH; ++cc) {
-    const uint32_t lc = (uint32_t)(lane + 64 * cc);
-    b.gs[cc] = bloadf(sg, (lc >> 1) * 4, 0);
-    b.us[cc] = bloadf(su, (lc >> 1) * 4, 0);
+    for (int cc = 0; cc < NCH; ++cc) {
+      const uint32_t lc = (uint32_t)(lane + 64 * cc);
+      b.gs[cc] = bloadf(sg, (lc >> 1) * 4, 0);
+      b.us[cc] = bloadf(su, (lc >> 1) * 4, 0);
+    }
   }
 }
 
 // silu(g) * u of one row for every token of the slot, stored as float32.
 // XREG: the single token's planes are xr/xsr; otherwise they are read from
-// LDS (planes [T][6][nch] as uint4, then scales [T][nch]), one token at a
+// LDS (planes [T][XP][nch] as uint4, then scales [T][h/32]), one token at a
 // time.
-template <int NCH, bool XREG>
-__device__ __forceinline__ void gu_consume(const GuBuf<NCH> &b, const GuCursor &c, bool valid,
-                                           const uint4 (&xr)[XREG ? NCH : 1][kPlanes],
+template <int NCH, bool XREG, class F>
+__device__ __forceinline__ void gu_consume(const GuBuf<NCH, F> &b, const GuCursor &c, bool valid,
+                                           const uint4 (&xr)[XREG ? NCH : 1][F::kXPlanes],
                                            const float (&xsr)[XREG ? NCH : 1], const uint4 *xl, int nch,
                                            const SmallRouting &R, const DecodeProblem &P) {
+  constexpr int XP = F::kXPlanes, CPB = 32 / F::kChunkCols;  // chunks per activation block
   const int lane = threadIdx.x & 63;
-  const int cnt = XREG ? 1 : c.cnt, n_routed = P.T * P.k;
+  const int cnt = XREG ? 1 : c.cnt, n_routed = P.T * P.k, nblk = P.h >> 5;
   for (int t = 0; t < cnt; ++t) {
     float g = 0.0f, u = 0.0f;
     const int pos = c.p_begin + t;
     const int tok = XREG ? 0 : pos < n_routed ? uniform(R.sorted_ids[pos]) / P.k : pos - n_routed;
 #pragma unroll
     for (int cc = 0; cc < NCH; ++cc) {
-      uint4 xt[kPlanes];
+      uint4 xt[XP];
       float sx;
       if (XREG) {
 #pragma unroll
-        for (int j = 0; j < kPlanes; ++j) xt[j] = xr[XREG ? cc : 0][j];
+        for (int j = 0; j < XP; ++j) xt[j] = xr[XREG ? cc : 0][j];
         sx = xsr[XREG ? cc : 0];
       } else {
         const int lc = min(lane + 64 * cc, nch - 1);  // lanes past the row meet zero weights
 #pragma unroll
-        for (int j = 0; j < kPlanes; ++j) xt[j] = xl[(tok * kPlanes + j) * nch + lc];
-        sx = reinterpret_cast<const float *>(xl + P.T * kPlanes * nch)[tok * nch + lc];
+        for (int j = 0; j < XP; ++j) xt[j] = xl[(tok * XP + j) * nch + lc];
+        sx = reinterpret_cast<const float *>(xl + P.T * XP * nch)[tok * nblk + lc / CPB];
       }
-      g = __builtin_fmaf((float)dot_planes(b.g[cc], xt), b.gs[cc] * sx, g);
-      u = __builtin_fmaf((float)dot_planes(b.u[cc], xt), b.us[cc] * sx, u);
+      if constexpr (F::kRowScale) {
+        g = __builtin_fmaf(F::dot(b.g[cc], xt), sx, g);
+        u = __builtin_fmaf(F::dot(b.u[cc], xt), sx, u);
+      } else {
+        g = __builtin_fmaf(F::dot(b.g[cc], xt), b.gs[cc] * sx, g);
+        u = __builtin_fmaf(F::dot(b.u[cc], xt), b.us[cc] * sx, u);
+      }
     }
     if (valid) {
-      const float gg = wave_sum(g);
-      const float uu = wave_sum(u);
+      float gg = wave_sum(g);
+      float uu = wave_sum(u);
+      if constexpr (F::kRowScale) {
+        gg *= b.gs[0];
+        uu *= b.us[0];
+      }
       if (lane == 0) P.midf[(size_t)(c.p_begin + t) * P.I + c.r] = gg / (1.0f + expf(-gg)) * uu;
     }
   }
@@ -485,15 +502,16 @@ __device__ __forceinline__ void gu_consume(const GuBuf<NCH> &b, const GuCursor &
 // 0 alone merges the selection and hands the routing to the other waves
 // through an LDS flag, so that it never waits for waves stalled on issuing
 // row loads; with several tokens the merging waves meet at a block barrier.
-template <int NCH, bool XREG>
+template <int NCH, bool XREG, class F>
 __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodeProblem P) {
   extern __shared__ uint4 xl[];
   __shared__ SmallRouting R;
   __shared__ int routed;  // XREG: set by wave 0 once R holds the routing
   constexpr int kWaves = XREG ? 4 : 8;
+  constexpr int XP = F::kXPlanes, CPB = 32 / F::kChunkCols;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int h = P.h, I = P.I, T = P.T, nch = h >> 5;
-  uint4 xr[XREG ? NCH : 1][kPlanes];
+  const int h = P.h, I = P.I, T = P.T, nch = h / F::kChunkCols, nblk = h >> 5;
+  uint4 xr[XREG ? NCH : 1][XP];
   float xsr[XREG ? NCH : 1];
   // 1. the selection inputs
   SelectInput sel;
@@ -501,7 +519,7 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   // 2. the hidden rows' digit planes (written by the router launch), loaded
   // once per block (a share per thread, no branch) and kept in LDS; with
   // one token each wave then takes its lanes' chunks into registers
-  const int nx = T * kPlanes * nch, nxs = T * nch;  // uint4 plane chunks, scales
+  const int nx = T * XP * nch, nxs = T * nblk;  // uint4 plane chunks, scales
   const Rsrc rx = make_rsrc(P.xq, (uint32_t)nx * 16), rxs = make_rsrc(P.xs, (uint32_t)nxs * 4);
   constexpr int kXPer = 5, kXsPer = 2;
   uint4 xv[kXPer];
@@ -527,13 +545,13 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   int32_t *const qctr = P.queues + (int)(gw % kGuQueues) * kGuQueueStride;
   const int qoff = P0 + (int)(gw % kGuQueues);
   constexpr int D = NCH > 4 ? 1 : kSbDepth;  // wide rows: one in flight (register file)
-  GuBuf<NCH> bs;  // the wave's first shared row
-  GuBuf<NCH> buf[D];
+  GuBuf<NCH, F> bs;  // the wave's first shared row
+  GuBuf<NCH, F> buf[D];
   GuCursor cs{};
   const bool has0 = gw < P0;
   if (has0) {
     cs.slot = 0;
-    gu_set_slot(P, R, cs);  // the shared expert: no routing needed
+    gu_set_slot<F>(P, R, cs);  // the shared expert: no routing needed
     cs.r = (int)gw;
   }
   // one atomic increment of this wave's queue: lane 0 receives the index of
@@ -572,8 +590,8 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
       const int lc = lane + 64 * cc;
       const bool in = lc < nch;
 #pragma unroll
-      for (int j = 0; j < kPlanes; ++j) xr[cc][j] = in ? xl[j * nch + lc] : make_uint4(0, 0, 0, 0);
-      xsr[cc] = in ? xsl[lc] : 0.0f;
+      for (int j = 0; j < XP; ++j) xr[cc][j] = in ? xl[j * nch + lc] : make_uint4(0, 0, 0, 0);
+      xsr[cc] = in ? xsl[lc / CPB] : 0.0f;
     }
   }
   bool have_routing = true;
@@ -604,7 +622,7 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
     const int fr = f - hs * I;
     c.slot = fr < 0 ? 0 : hs + fr / I;
     c.r = fr < 0 ? f : fr % I;
-    gu_set_slot(P, R, c);
+    gu_set_slot<F>(P, R, c);
   };
   auto row_of = [&](int i) { return qoff + kGuQueues * i < N ? qoff + kGuQueues * i : -1; };
   // 5. the handed-out rows through a ring of D buffers.  The index of the
@@ -624,7 +642,7 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
     const RoutingOut o{P.idx, P.wsel, P.sorted_ids, P.inv, P.offsets, P.active, P.n_active};
     publish_routing(R, T, P.k, P.E, o);
   }
-  gu_consume<NCH, XREG>(bs, cs, has0, xr, xsr, xl, nch, R, P);
+  gu_consume<NCH, XREG, F>(bs, cs, has0, xr, xsr, xl, nch, R, P);
   // A queue hands out rows in increasing order, so once a ring entry is past
   // the end every later one is too.  The loop body is straight-line: absent
   // rows are summed from zeros and not stored, and every step issues its
@@ -636,7 +654,7 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   while (more) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      gu_consume<NCH, XREG>(buf[d], cur[d], fr[d] >= 0, xr, xsr, xl, nch, R, P);
+      gu_consume<NCH, XREG, F>(buf[d], cur[d], fr[d] >= 0, xr, xsr, xl, nch, R, P);
       const int f = row_of(uniform(pend));
       pend = grab();
       fr[d] = f;
@@ -649,23 +667,28 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
   }
 }
 
-template <int NCHD>
+template <int NCHD, class F>
 struct DnBuf {
+  static constexpr int NS = F::kRowScale ? 1 : NCHD;
   uint4 w[NCHD];
-  float s[NCHD];
+  float s[NS];
 };
 
-template <int NCHD>
-__device__ __forceinline__ void dn_load(DnBuf<NCHD> &b, const uint8_t *q, const float *sc, int row, bool valid,
+template <int NCHD, class F>
+__device__ __forceinline__ void dn_load(DnBuf<NCHD, F> &b, const uint8_t *q, const float *sc, int row, bool valid,
                                         int I) {
   const int lane = threadIdx.x & 63;
-  const uint32_t rowq = (uint32_t)I >> 1, rows = (uint32_t)(I >> 6) * 4;
+  const uint32_t rowq = F::row_bytes(I), nsc = F::row_scales(I), rows = nsc * 4;
   const Rsrc rq = make_rsrc(q + (size_t)row * rowq, valid ? rowq : 0u);
-  const Rsrc rs = make_rsrc(sc + (size_t)row * (I >> 6), valid ? rows : 0u);
+  const Rsrc rs = make_rsrc(sc + (size_t)row * nsc, valid ? rows : 0u);
 #pragma unroll
   for (int cc = 0; cc < NCHD; ++cc) b.w[cc] = bload16(rq, (uint32_t)(lane + 64 * cc) * 16, 0);
+  if constexpr (F::kRowScale) {
+    b.s[0] = bloadf(rs, 0, 0);
+  } else {
 #pragma unroll
-  for (int cc = 0; cc < NCHD; ++cc) b.s[cc] = bloadf(rs, (uint32_t)((lane + 64 * cc) >> 1) * 4, 0);
+    for (int cc = 0; cc < NCHD; ++cc) b.s[cc] = bloadf(rs, (uint32_t)((lane + 64 * cc) >> 1) * 4, 0);
+  }
 }
 
 // Slot q of the down sequence: tokens in order; for each token its
@@ -722,6 +745,7 @@ __device__ __forceinline__ DnSlot dn_shared_slot(const DecodeProblem &P, int t) 
   return DnSlot{P.sh_down.q, P.sh_down.s, t, 1.0f, true};
 }
 
+template <class F>
 __device__ __forceinline__ DnSlot dn_slot(const DecodeProblem &P, const DnTable &D, int qs) {
   DnSlot d;
   d.t = qs / (P.k + P.has_shared);
@@ -729,8 +753,8 @@ __device__ __forceinline__ DnSlot dn_slot(const DecodeProblem &P, const DnTable 
   d.live = e != kDnDropped;
   if (e >= 0) {
     const size_t x = table_index(P.slot_of, e);
-    d.q = P.down.q + x * ((size_t)P.h * (P.I >> 1));
-    d.s = P.down.s + x * ((size_t)P.h * (P.I >> 6));
+    d.q = P.down.q + x * ((size_t)P.h * F::row_bytes(P.I));
+    d.s = P.down.s + x * ((size_t)P.h * F::row_scales(P.I));
   } else if (e == -1) {
     d.q = P.sh_down.q;
     d.s = P.sh_down.s;
@@ -776,19 +800,22 @@ constexpr int dc_ring() {
 // group quantised when the ring reaches it.  No load is issued under a
 // branch that depends on the data, so the compiler's waits count exactly
 // the loads issued after the ones awaited.
-template <int NCHD, int RM, bool BYPOS>
+template <int NCHD, int RM, bool BYPOS, class F>
 __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(DecodeProblem P, float *__restrict__ out,
                                                                          int gs) {
   static_assert(kDcWaves * 64 >= kSmallAssign + kSmallT, "one thread per slot of the routing table");
   constexpr int NS = dc_ring<NCHD, RM>();
+  constexpr int XP = F::kXPlanes, CPB = 32 / F::kChunkCols;
   extern __shared__ uint4 ml[];
   __shared__ DnTable tab;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int h = P.h, I = P.I, nchd = I >> 5, words = I >> 3;
+  // nchd 16-byte chunks of a down row; activation blocks of 32 and words of
+  // 8 intermediate columns
+  const int h = P.h, I = P.I, nchd = I / F::kChunkCols, nblk = I >> 5, words = I >> 3;
   const int n_slots = P.T * (P.k + P.has_shared);
   const int64_t W = (int64_t)gridDim.x * kDcWaves, gw = (int64_t)blockIdx.x * kDcWaves + wave;
   const int r0 = (int)((int64_t)h * gw / W), nr = (int)((int64_t)h * (gw + 1) / W) - r0;
-  float *msc = reinterpret_cast<float *>(ml + (size_t)gs * kPlanes * nchd);
+  float *msc = reinterpret_cast<float *>(ml + (size_t)gs * XP * nchd);
   uint32_t *mw = reinterpret_cast<uint32_t *>(ml);
   const Rsrc rmid = make_rsrc(P.midf, (uint32_t)n_slots * I * 4);
   constexpr int kBatch = 5;  // 8-column words per thread and batch
@@ -796,7 +823,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(Decode
   float acc[RM];
 #pragma unroll
   for (int r = 0; r < RM; ++r) acc[r] = 0.0f;
-  DnBuf<NCHD> buf[NS][RM];
+  DnBuf<NCHD, F> buf[NS][RM];
   DnSlot ring[NS];
 
   // byte offsets of the batch's words in midf (past the group: an offset
@@ -831,8 +858,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(Decode
       const float v[8] = {__uint_as_float(va[j].x), __uint_as_float(va[j].y), __uint_as_float(va[j].z),
                           __uint_as_float(va[j].w), __uint_as_float(vc[j].x), __uint_as_float(vc[j].y),
                           __uint_as_float(vc[j].z), __uint_as_float(vc[j].w)};
-      quantize_word(v, (w & 3) == 0, valid, mw + (size_t)sl * kPlanes * words + w, (size_t)words,
-                    msc + sl * nchd + (w >> 2));
+      F::quantize(v, (w & 3) == 0, valid, mw + (size_t)sl * XP * nchd * 4, I, w, msc + sl * nblk + (w >> 2));
     }
   };
   // the rest of a group's words, one batch at a time (several batches only
@@ -849,7 +875,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(Decode
   // slot qs (past the last: no rows) into ring buffer u
   auto ring_load = [&](int u, int qs) {
     const bool v = qs < n_slots;
-    ring[u] = v ? dn_slot(P, tab, qs) : DnSlot{};
+    ring[u] = v ? dn_slot<F>(P, tab, qs) : DnSlot{};
 #pragma unroll
     for (int r = 0; r < RM; ++r) dn_load(buf[u][r], ring[u].q, ring[u].s, r0 + r, v && ring[u].live && r < nr, I);
   };
@@ -905,16 +931,27 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_rows_kernel(Decode
       }
       if (qc < n_slots) {
         const DnSlot &sc = ring[u];
+        float part[RM];  // int8: the slot's sums before its row scales
+#pragma unroll
+        for (int r = 0; r < RM; ++r) part[r] = 0.0f;
 #pragma unroll
         for (int cc = 0; cc < NCHD; ++cc) {
           const int lc = min(lane + 64 * cc, nchd - 1);  // lanes past the row meet zero weights
-          uint4 xp[kPlanes];
+          uint4 xp[XP];
 #pragma unroll
-          for (int j2 = 0; j2 < kPlanes; ++j2) xp[j2] = ml[(sl * kPlanes + j2) * nchd + lc];
-          const float sx = msc[sl * nchd + lc] * sc.w;
+          for (int j2 = 0; j2 < XP; ++j2) xp[j2] = ml[(sl * XP + j2) * nchd + lc];
+          const float sx = msc[sl * nblk + lc / CPB] * sc.w;
 #pragma unroll
-          for (int r = 0; r < RM; ++r)
-            acc[r] = __builtin_fmaf((float)dot_planes(buf[u][r].w[cc], xp), buf[u][r].s[cc] * sx, acc[r]);
+          for (int r = 0; r < RM; ++r) {
+            if constexpr (F::kRowScale)
+              part[r] = __builtin_fmaf(F::dot(buf[u][r].w[cc], xp), sx, part[r]);
+            else
+              acc[r] = __builtin_fmaf(F::dot(buf[u][r].w[cc], xp), buf[u][r].s[cc] * sx, acc[r]);
+          }
+        }
+        if constexpr (F::kRowScale) {
+#pragma unroll
+          for (int r = 0; r < RM; ++r) acc[r] = __builtin_fmaf(part[r], buf[u][r].s[0], acc[r]);
         }
         // the token's last slot: reduce and store
         if (qc + 1 == n_slots || dn_slot_token(P, qc + 1) != sc.t) {
@@ -1143,50 +1180,108 @@ hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s) {
   return launch(fill_i32_kernel, (n + 255) / 256, 256, 0, s, p, n, v);
 }
 
-bool small_batch(int T, int k, int h, int I) {
-  if (T > kSmallT || T * k > kSmallAssign || I > 64 * 32 * kDcMaxChunks) return false;
-  return T * (kPlanes * 4 * (h >> 3) + 4 * (h >> 5)) <= kSbMaxXLds;
+bool small_batch(int T, int k, int h, int I, bool int8) {
+  // down rows: at most kDcMaxChunks 16-byte chunks per lane
+  const int max_i = 64 * (int8 ? 16 : 32) * kDcMaxChunks;
+  if (T > kSmallT || T * k > kSmallAssign || I > max_i) return false;
+  return T * (3 * h + 4 * (h >> 5)) <= kSbMaxXLds;  // the hidden rows' planes and scales in LDS
 }
 
 namespace {
 
-template <int NCH, bool XREG>
+template <int NCH, bool XREG, class F>
 hipError_t launch_gu_rows_n(const DecodeProblem &P, hipStream_t s) {
-  const uint32_t lds = (uint32_t)(P.T * (kPlanes * 4 * (P.h >> 3) + 4 * (P.h >> 5)));
+  const uint32_t lds = (uint32_t)(P.T * (3 * P.h + 4 * (P.h >> 5)));
   {
     static bool attr_set = false;  // LDS above 64 KB must be allowed once per kernel
     if (!attr_set) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gate_up_rows_kernel<NCH, XREG>),
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gate_up_rows_kernel<NCH, XREG, F>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, kSbMaxXLds);
       if (e != hipSuccess) return e;
       attr_set = true;
     }
   }
-  return launch(gate_up_rows_kernel<NCH, XREG>, XREG ? kSbBlocks : kSbBlocksLds, XREG ? 256 : 512, lds, s, P);
+  return launch(gate_up_rows_kernel<NCH, XREG, F>, XREG ? kSbBlocks : kSbBlocksLds, XREG ? 256 : 512, lds, s, P);
 }
 
-template <int NCHD, int RM>
+// Chunks per lane of a row: int4 h <= 64 * 32 * 8, int8 h <= 64 * 16 * 8.
+// One token keeps its planes in registers up to 24 uint4 per lane.
+template <class F>
+hipError_t launch_gu_rows(const DecodeProblem &P, hipStream_t s) {
+  const int per = 64 * F::kChunkCols, nchl = (P.h + per - 1) / per;
+  const bool xreg = P.T == 1 && nchl * F::kXPlanes <= 24;
+  if constexpr (F::kRowScale) {
+    const int n = nchl <= 2 ? nchl : nchl <= 4 ? 4 : nchl <= 6 ? 6 : 8;
+    if (xreg) {
+      switch (n) {
+        case 1: return launch_gu_rows_n<1, true, F>(P, s);
+        case 2: return launch_gu_rows_n<2, true, F>(P, s);
+        case 4: return launch_gu_rows_n<4, true, F>(P, s);
+        case 6: return launch_gu_rows_n<6, true, F>(P, s);
+        default: return launch_gu_rows_n<8, true, F>(P, s);
+      }
+    }
+    switch (n) {
+      case 1: return launch_gu_rows_n<1, false, F>(P, s);
+      case 2: return launch_gu_rows_n<2, false, F>(P, s);
+      case 4: return launch_gu_rows_n<4, false, F>(P, s);
+      case 6: return launch_gu_rows_n<6, false, F>(P, s);
+      default: return launch_gu_rows_n<8, false, F>(P, s);
+    }
+  } else {
+    if (xreg) {
+      switch (nchl) {
+        case 1: return launch_gu_rows_n<1, true, F>(P, s);
+        case 2: return launch_gu_rows_n<2, true, F>(P, s);
+        case 3: return launch_gu_rows_n<3, true, F>(P, s);
+        default: return launch_gu_rows_n<4, true, F>(P, s);
+      }
+    }
+    switch (nchl) {
+      case 1: return launch_gu_rows_n<1, false, F>(P, s);
+      case 2: return launch_gu_rows_n<2, false, F>(P, s);
+      case 3: return launch_gu_rows_n<3, false, F>(P, s);
+      case 4: return launch_gu_rows_n<4, false, F>(P, s);
+      case 5:
+      case 6: return launch_gu_rows_n<6, false, F>(P, s);
+      default: return launch_gu_rows_n<8, false, F>(P, s);
+    }
+  }
+}
+
+template <int NCHD, int RM, class F>
 hipError_t launch_dc_rows_n(const DecodeProblem &P, float *out, int blocks, hipStream_t s) {
-  const int nchd = P.I >> 5, per_slot = nchd * (kPlanes * 16 + 4);
+  const int per_slot = 3 * P.I + 4 * (P.I >> 5);  // planes and scales of one intermediate row
   const int n_slots = P.T * (P.k + P.has_shared);
   const int gs = kDcLds / per_slot;  // >= 2: small batches have I <= 8192
   if (gs >= n_slots)
-    return launch(down_combine_rows_kernel<NCHD, RM, true>, blocks, kDcWaves * 64, (uint32_t)(n_slots * per_slot), s,
-                  P, out, n_slots);
-  return launch(down_combine_rows_kernel<NCHD, RM, false>, blocks, kDcWaves * 64, (uint32_t)(gs * per_slot), s, P,
+    return launch(down_combine_rows_kernel<NCHD, RM, true, F>, blocks, kDcWaves * 64, (uint32_t)(n_slots * per_slot),
+                  s, P, out, n_slots);
+  return launch(down_combine_rows_kernel<NCHD, RM, false, F>, blocks, kDcWaves * 64, (uint32_t)(gs * per_slot), s, P,
                 out, gs);
 }
 
-template <int NCHD>
+template <int NCHD, class F>
 hipError_t launch_dc_rows_r(const DecodeProblem &P, float *out, hipStream_t s) {
   const int blocks = min(kDcBlocks, (P.h + kDcWaves - 1) / kDcWaves);
   const int rm = (P.h + blocks * kDcWaves - 1) / (blocks * kDcWaves);  // rows per wave, at most
   switch (rm) {
-    case 1: return launch_dc_rows_n<NCHD, 1>(P, out, blocks, s);
-    case 2: return launch_dc_rows_n<NCHD, 2>(P, out, blocks, s);
-    case 3: return launch_dc_rows_n<NCHD, 3>(P, out, blocks, s);
-    case 4: return launch_dc_rows_n<NCHD, 4>(P, out, blocks, s);
-    default: return launch_dc_rows_n<NCHD, 8>(P, out, blocks, s);
+    case 1: return launch_dc_rows_n<NCHD, 1, F>(P, out, blocks, s);
+    case 2: return launch_dc_rows_n<NCHD, 2, F>(P, out, blocks, s);
+    case 3: return launch_dc_rows_n<NCHD, 3, F>(P, out, blocks, s);
+    case 4: return launch_dc_rows_n<NCHD, 4, F>(P, out, blocks, s);
+    default: return launch_dc_rows_n<NCHD, 8, F>(P, out, blocks, s);
+  }
+}
+
+template <class F>
+hipError_t launch_dc_rows(const DecodeProblem &P, float *out, hipStream_t s) {
+  const int per = 64 * F::kChunkCols;
+  switch ((P.I + per - 1) / per) {
+    case 1: return launch_dc_rows_r<1, F>(P, out, s);
+    case 2: return launch_dc_rows_r<2, F>(P, out, s);
+    case 3: return launch_dc_rows_r<3, F>(P, out, s);
+    default: return launch_dc_rows_r<4, F>(P, out, s);
   }
 }
 
@@ -1257,26 +1352,8 @@ hipError_t launch_read_probe(const DecodeProblem &P, const int32_t *experts, int
 
 hipError_t launch_gemv_gate_up(const DecodeProblem &P, hipStream_t s) {
   if (P.T == 0) return hipSuccess;
-  if (small_batch(P.T, P.k, P.h, P.I)) {
-    const int nchl = (P.h + 2047) / 2048;  // 32-column chunks per lane of a row
-    if (P.T == 1 && nchl <= kSbMaxXChunks) {
-      switch (nchl) {
-        case 1: return launch_gu_rows_n<1, true>(P, s);
-        case 2: return launch_gu_rows_n<2, true>(P, s);
-        case 3: return launch_gu_rows_n<3, true>(P, s);
-        default: return launch_gu_rows_n<4, true>(P, s);
-      }
-    }
-    switch (nchl) {
-      case 1: return launch_gu_rows_n<1, false>(P, s);
-      case 2: return launch_gu_rows_n<2, false>(P, s);
-      case 3: return launch_gu_rows_n<3, false>(P, s);
-      case 4: return launch_gu_rows_n<4, false>(P, s);
-      case 5:
-      case 6: return launch_gu_rows_n<6, false>(P, s);
-      default: return launch_gu_rows_n<8, false>(P, s);
-    }
-  }
+  if (small_batch(P.T, P.k, P.h, P.I, P.int8)) return P.int8 ? launch_gu_rows<FmtI8>(P, s) : launch_gu_rows<FmtI4>(P, s);
+  if (P.int8) return hipErrorInvalidValue;  // int8 tables take the small-batch launches only
   const int slots = P.n_routed_slots + (P.has_shared ? 1 : 0);
   if (slots == 0) return hipSuccess;
   // rows held in registers up to h = 6144 (wider rows do not fit the
@@ -1301,12 +1378,7 @@ hipError_t launch_gemv_gate_up(const DecodeProblem &P, hipStream_t s) {
 
 hipError_t launch_down_combine(const DecodeProblem &P, float *out, hipStream_t s) {
   if (P.T == 0) return hipSuccess;
-  switch ((P.I + 2047) / 2048) {
-    case 1: return launch_dc_rows_r<1>(P, out, s);
-    case 2: return launch_dc_rows_r<2>(P, out, s);
-    case 3: return launch_dc_rows_r<3>(P, out, s);
-    default: return launch_dc_rows_r<4>(P, out, s);
-  }
+  return P.int8 ? launch_dc_rows<FmtI8>(P, out, s) : launch_dc_rows<FmtI4>(P, out, s);
 }
 
 hipError_t launch_gemv_down(const DecodeProblem &P, hipStream_t s) {

@@ -75,10 +75,10 @@ hipError_t launch_router_permute(const float *wr, float *wrP, int h, int E, hipS
 // the wave owning (t, e) keeps p_l = fma(x[l+64m], w[l+64m], p_l) over
 // m = 0..h/64-1, then the 64 partials meet in an xor butterfly (32,16,..,1).
 // The same launch writes the digit-plane form of x (xq, xs) for the experts
-// (xq == NULL: no planes).  One token with h in {2048, 4096, 6144} takes a
+// (xq == NULL: no planes; byte_planes: the byte planes of int8 tables).  One token with h in {2048, 4096, 6144} takes a
 // launch that issues every load of a chain before its first fma.
 hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits,
-                                uint32_t *xq, float *xs, hipStream_t s);  // xq == NULL: no planes
+                                uint32_t *xq, float *xs, bool byte_planes, hipStream_t s);  // xq == NULL: no planes
 
 // One wave per token: sigmoid scores, biased key, top-k (key desc, index
 // asc), renormalised weights times rsf.
@@ -119,6 +119,7 @@ struct DecodeProblem {
   int h, I, T, k, E;
   int n_routed_slots;  // min(E, T*k): grid slots for routed experts
   int has_shared;
+  int int8;             // tables are int8 with a scale per row (else int4 gs64)
   float rsf;
   RouteLimits lim;      // run-time routing limits (small batches route in the gate/up launch)
   const float *logits;  // [T][E] router logits (small batches route from them)
@@ -141,8 +142,9 @@ struct DecodeProblem {
 constexpr int kRowQueueWords = 64 * 64;
 
 // True when the batch takes the small-batch launch structure (router and
-// routing in one launch, gate/up, then down fused with the combine).
-bool small_batch(int T, int k, int h, int I);
+// routing in one launch, gate/up, then down fused with the combine).  int8
+// tables run only there.
+bool small_batch(int T, int k, int h, int I, bool int8);
 // Fill n int32 values.
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t s);
 

@@ -44,7 +44,8 @@ template <int EPW, int TPW>
 __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restrict__ x,
                                                             const float *__restrict__ wrP, int T, int h, int E,
                                                             float *__restrict__ logits, int n_logit_blocks,
-                                                            uint32_t *__restrict__ xq, float *__restrict__ xs) {
+                                                            uint32_t *__restrict__ xq, float *__restrict__ xs,
+                                                            int byte_planes) {
   const int bid = blockIdx.x;
   if (bid < n_logit_blocks) {
     const int egroups = (E + 4 * EPW - 1) / (4 * EPW);
@@ -69,9 +70,14 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
     for (int i = 0; i < 8; ++i) v[i] = 0.0f;
   }
   // a 32-column block is 4 words and never straddles a row (words % 8 == 0),
-  // so the four lanes of a quad share the row and the block
-  quantize_word(v, (w & 3) == 0, valid, xq + t * kPlanes * words + w, (size_t)words,
-                xs + t * (words >> 2) + (w >> 2));
+  // so the four lanes of a quad share the row and the block; either plane
+  // form takes 3 h / 4 words per row
+  uint32_t *row = xq + t * (size_t)(3 * (h >> 2));
+  float *sb = xs + t * (words >> 2) + (w >> 2);
+  if (byte_planes)
+    FmtI8::quantize(v, (w & 3) == 0, valid, row, h, w, sb);
+  else
+    FmtI4::quantize(v, (w & 3) == 0, valid, row, h, w, sb);
 }
 
 __global__ __launch_bounds__(256) void router_select_kernel(const float *__restrict__ logits,
@@ -133,7 +139,8 @@ template <int MB>
 __global__ __launch_bounds__(256) void router_logits_t1_kernel(const float *__restrict__ x,
                                                                const float *__restrict__ wrP, int E,
                                                                float *__restrict__ logits, int n_logit_blocks,
-                                                               uint32_t *__restrict__ xq, float *__restrict__ xs) {
+                                                               uint32_t *__restrict__ xq, float *__restrict__ xs,
+                                                               int byte_planes) {
   constexpr int M = 4 * MB;  // chain length h / 64
   const int lane = threadIdx.x & 63;
   if ((int)blockIdx.x >= n_logit_blocks) {  // the token's digit planes, 256 words per block
@@ -149,7 +156,11 @@ __global__ __launch_bounds__(256) void router_logits_t1_kernel(const float *__re
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
-    quantize_word(v, (w & 3) == 0, valid, xq + (valid ? w : 0), (size_t)words, xs + (valid ? (w >> 2) : 0));
+    const int wq = valid ? w : 0;
+    if (byte_planes)
+      FmtI8::quantize(v, (w & 3) == 0, valid, xq, M * 64, wq, xs + (wq >> 2));
+    else
+      FmtI4::quantize(v, (w & 3) == 0, valid, xq, M * 64, wq, xs + (wq >> 2));
     return;
   }
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -174,36 +185,37 @@ size_t router_permuted_floats(int h, int E) { return (size_t)E * ((((h >> 6) + 3
 constexpr int kWideMinT = 256;
 
 hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits, uint32_t *xq,
-                                float *xs, hipStream_t s) {
+                                float *xs, bool byte_planes, hipStream_t s) {
+  const int bp = byte_planes ? 1 : 0;
   if (T <= 0) return hipSuccess;
   const int qblocks = xq ? (int)(((size_t)T * (h >> 3) + 255) / 256) : 0;
   if (T == 1 && (h == 2048 || h == 4096 || h == 6144)) {
     const int nlb = (E + 3) / 4;
-    if (h == 2048) return launch(router_logits_t1_kernel<8>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs);
-    if (h == 4096) return launch(router_logits_t1_kernel<16>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs);
-    return launch(router_logits_t1_kernel<24>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs);
+    if (h == 2048) return launch(router_logits_t1_kernel<8>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs, bp);
+    if (h == 4096) return launch(router_logits_t1_kernel<16>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs, bp);
+    return launch(router_logits_t1_kernel<24>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs, bp);
   }
   // tiles per wave (experts x tokens) by batch size, measured on the GLM-like
   // layer (h = 6144, E = 256): the smallest tiles while they give the chip
   // enough waves, larger ones as the batch grows
   if (T < 12) {
     const int nlb = T * ((E + 3) / 4);
-    return launch(router_logits_kernel<1, 1>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
+    return launch(router_logits_kernel<1, 1>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs, bp);
   } else if (T < 24) {
     const int nlb = ((T + 1) / 2) * ((E + 3) / 4);
-    return launch(router_logits_kernel<1, 2>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
+    return launch(router_logits_kernel<1, 2>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs, bp);
   } else if (T < 48) {
     const int nlb = ((T + 1) / 2) * ((E + 7) / 8);
-    return launch(router_logits_kernel<2, 2>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
+    return launch(router_logits_kernel<2, 2>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs, bp);
   } else if (T < kWideMinT) {
     const int nlb = ((T + 3) / 4) * ((E + 7) / 8);
-    return launch(router_logits_kernel<2, 4>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs);
+    return launch(router_logits_kernel<2, 4>, nlb + qblocks, 256, 0, s, x, wrP, T, h, E, logits, nlb, xq, xs, bp);
   }
   // large batches: the wide tiles, then (GEMV path only) the digit planes
   const unsigned nwb = (unsigned)(((T + kWideT - 1) / kWideT) * ((E + kWideE - 1) / kWideE));
   hipError_t err = launch(router_logits_wide_kernel, nwb, kWideWaves * 64, 0, s, x, wrP, T, h, E, logits);
   if (err != hipSuccess || qblocks == 0) return err;
-  return launch(router_logits_kernel<2, 4>, qblocks, 256, 0, s, x, wrP, T, h, E, logits, 0, xq, xs);
+  return launch(router_logits_kernel<2, 4>, qblocks, 256, 0, s, x, wrP, T, h, E, logits, 0, xq, xs, bp);
 }
 
 hipError_t launch_router_select(const float *logits, const float *bias, int T, int E, int k, float rsf,

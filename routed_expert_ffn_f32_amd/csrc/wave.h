@@ -206,4 +206,106 @@ __device__ __forceinline__ int dot_planes(const uint4 &w, const uint4 (&p)[kPlan
   return h;
 }
 
+// ---------------------------------------------------------------------------
+// Byte-plane activations (int8 weights).
+//
+// The same block floating point as above (N_c = rint(x_c / s_b), |N_c| <=
+// 2^22, one scale per 32 columns), written as three balanced base-256 digits
+// b_j in [-128, 127] (b_2 in [-64, 64]), N_c = b_0 + 256 b_1 + 65536 b_2.
+// Byte i of word w of plane j is digit j of column 4w + i: the byte order of
+// an int8 weight row, so v_dot4_i32_i8 on a weight word and a plane word
+// multiplies matching columns.
+// Layout: planes [row][kBytePlanes][cols/4] uint32, scales [row][cols/32].
+// ---------------------------------------------------------------------------
+constexpr int kBytePlanes = 3;
+
+// As quantize_word (same thread and quad layout, same scale), for byte
+// planes: the thread's 8 columns are words 0 and 1 of each plane at
+// planes_w[j * plane_stride + 0/1].  M = N + 0x808080 has the base-256
+// digits b_j + 128 (no carries, 0 <= M < 2^24); byte j of M with its top bit
+// flipped is b_j as a two's-complement byte.
+__device__ __forceinline__ void quantize_word8(const float v[8], bool first_of_block, bool store,
+                                               uint32_t *planes_w, size_t plane_stride, float *scale_b) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  m = quad_max(m);
+  int e = 0;
+  (void)__builtin_frexpf(m, &e);
+  e = m > 0.0f ? max(e, kMinExp) : kMinExp;
+  const float to_int = __int_as_float((127 + kMantBits - e) << 23);
+  const float to_real = __int_as_float((127 - kMantBits + e) << 23);
+  constexpr uint32_t kRound = 0x4B400000u;
+  uint32_t M[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    M[i] = __float_as_uint(__builtin_fmaf(v[i], to_int, __uint_as_float(kRound))) - (kRound - 0x808080u);
+#pragma unroll
+  for (int j = 0; j < kBytePlanes; ++j) {
+    // byte j of each value: pairs first, then the two pairs of a word
+    const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 8) | ((uint32_t)j << 16) | ((uint32_t)(4 + j) << 24);
+    const uint32_t a = __builtin_amdgcn_perm(M[1], M[0], sel), b = __builtin_amdgcn_perm(M[3], M[2], sel);
+    const uint32_t c = __builtin_amdgcn_perm(M[5], M[4], sel), d = __builtin_amdgcn_perm(M[7], M[6], sel);
+    const uint32_t w0 = __builtin_amdgcn_perm(b, a, 0x05040100u), w1 = __builtin_amdgcn_perm(d, c, 0x05040100u);
+    if (store) {
+      planes_w[j * plane_stride] = w0 ^ 0x80808080u;
+      planes_w[j * plane_stride + 1] = w1 ^ 0x80808080u;
+    }
+  }
+  if (store && first_of_block) *scale_b = to_real;
+}
+
+// sum over 16 columns of int8 weights (4 words) times the byte-plane
+// integers: d_j = sum_k dot4(w_k, p_j,k) is exact (|d_j| <= 16 * 128 * 128
+// = 2^18), d_0 + 256 d_1 too (< 2^27); the top plane joins in float32.
+__device__ __forceinline__ float dot_bytes(const uint4 &w, const uint4 (&p)[kBytePlanes]) {
+  int d[kBytePlanes];
+#pragma unroll
+  for (int j = 0; j < kBytePlanes; ++j) {
+    int a = __builtin_amdgcn_sdot4((int)w.x, (int)p[j].x, 0, false);
+    a = __builtin_amdgcn_sdot4((int)w.y, (int)p[j].y, a, false);
+    a = __builtin_amdgcn_sdot4((int)w.z, (int)p[j].z, a, false);
+    d[j] = __builtin_amdgcn_sdot4((int)w.w, (int)p[j].w, a, false);
+  }
+  return __builtin_fmaf((float)d[2], 65536.0f, (float)(d[0] + (d[1] << 8)));
+}
+
+// ---------------------------------------------------------------------------
+// Weight formats of the GEMV kernels.  A lane chunk is 16 bytes of a weight
+// row (a wave-load covers 1 KB of the row).
+//  - int4 gs64: 32 columns per chunk, a float32 scale per 64 columns;
+//    activations as six 4-bit digit planes (dot_planes).
+//  - int8 with one float32 scale per row: 16 columns per chunk; activations
+//    as three byte planes (dot_bytes); the row scale is applied once per row
+//    (and, in the down launch, per slot before the weighted sum).
+// Both keep 3 bytes of planes per activation column and one activation scale
+// per 32 columns, so plane buffers have the same size in either format.
+// ---------------------------------------------------------------------------
+struct FmtI4 {
+  static constexpr int kChunkCols = 32;
+  static constexpr int kXPlanes = kPlanes;
+  static constexpr bool kRowScale = false;
+  __device__ static uint32_t row_bytes(int cols) { return (uint32_t)cols >> 1; }
+  __device__ static uint32_t row_scales(int cols) { return (uint32_t)cols >> 6; }
+  __device__ static float dot(const uint4 &w, const uint4 (&p)[kXPlanes]) { return (float)dot_planes(w, p); }
+  // the thread's 8-column word w of a row: its plane words
+  __device__ static void quantize(const float v[8], bool first, bool store, uint32_t *row_planes, int cols, int w,
+                                  float *scale_b) {
+    quantize_word(v, first, store, row_planes + w, (size_t)(cols >> 3), scale_b);
+  }
+};
+
+struct FmtI8 {
+  static constexpr int kChunkCols = 16;
+  static constexpr int kXPlanes = kBytePlanes;
+  static constexpr bool kRowScale = true;
+  __device__ static uint32_t row_bytes(int cols) { return (uint32_t)cols; }
+  __device__ static uint32_t row_scales(int) { return 1u; }
+  __device__ static float dot(const uint4 &w, const uint4 (&p)[kXPlanes]) { return dot_bytes(w, p); }
+  __device__ static void quantize(const float v[8], bool first, bool store, uint32_t *row_planes, int cols, int w,
+                                  float *scale_b) {
+    quantize_word8(v, first, store, row_planes + 2 * w, (size_t)(cols >> 2), scale_b);
+  }
+};
+
 }  // namespace coli

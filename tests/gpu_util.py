@@ -53,7 +53,7 @@ class DeviceLayer:
         cfg = cm.make_config(hidden=shape.hidden, n_experts=shape.n_experts, top_k=shape.top_k,
                              inter=shape.inter, n_shared=shape.n_shared,
                              routed_scaling_factor=shape.rsf, max_tokens=max_tokens,
-                             prefill_threshold=prefill_threshold)
+                             prefill_threshold=prefill_threshold, weight_format=shape.weight_format)
         self.moe = cm.MoELayer(cfg, t)
         self.limits = {}  # run-time routing limits of the oracle calls (k_use, top_p)
 
