@@ -130,22 +130,24 @@ __global__ __launch_bounds__(kWideWaves * 64) void router_logits_wide_kernel(con
   logits_wide_tile(x, wrP, T, h, E, (blockIdx.x / egroups) * kWideT, (blockIdx.x % egroups) * kWideE, logits, xs, ws);
 }
 
-// One token: grid = ceil(E / 4) blocks of 4 waves, wave w of block b owns
-// expert 4b + w.  Every load of its chain (MB float4 blocks of the permuted
-// router, the token's h/64 values for this lane) is issued before the first
-// fma, so the launch costs one memory round trip; the arithmetic is
-// logits_tile's, element for element.
+// One token: grid = E blocks of one wave, block e owning expert e (one wave
+// per block spreads the table's read over every CU: 4-wave blocks on a
+// quarter of the CUs took 8% longer), then the digit-plane blocks.  Every
+// load of its chain (MB float4 blocks of the permuted router, the token's
+// h/64 values for this lane) is issued before the first fma, so the launch
+// costs one memory round trip; the arithmetic is logits_tile's, element for
+// element.
 template <int MB>
-__global__ __launch_bounds__(256) void router_logits_t1_kernel(const float *__restrict__ x,
+__global__ __launch_bounds__(64) void router_logits_t1_kernel(const float *__restrict__ x,
                                                                const float *__restrict__ wrP, int E,
                                                                float *__restrict__ logits, int n_logit_blocks,
                                                                uint32_t *__restrict__ xq, float *__restrict__ xs,
                                                                int byte_planes) {
   constexpr int M = 4 * MB;  // chain length h / 64
   const int lane = threadIdx.x & 63;
-  if ((int)blockIdx.x >= n_logit_blocks) {  // the token's digit planes, 256 words per block
+  if ((int)blockIdx.x >= n_logit_blocks) {  // the token's digit planes, 64 words per block
     const int words = M * 8;  // h / 8
-    const int w = (blockIdx.x - n_logit_blocks) * 256 + threadIdx.x;
+    const int w = (blockIdx.x - n_logit_blocks) * 64 + threadIdx.x;
     const bool valid = w < words;
     float v[8];
     if (valid) {
@@ -163,8 +165,7 @@ __global__ __launch_bounds__(256) void router_logits_t1_kernel(const float *__re
       FmtI4::quantize(v, (w & 3) == 0, valid, xq, M * 64, wq, xs + (wq >> 2));
     return;
   }
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;  // uniform over the wave
+  const int e = blockIdx.x;
   const float acc = logit_t1<MB>(x, wrP, e);
   if (lane == 0) logits[e] = acc;
 }
@@ -190,10 +191,10 @@ hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, 
   if (T <= 0) return hipSuccess;
   const int qblocks = xq ? (int)(((size_t)T * (h >> 3) + 255) / 256) : 0;
   if (T == 1 && (h == 2048 || h == 4096 || h == 6144)) {
-    const int nlb = (E + 3) / 4;
-    if (h == 2048) return launch(router_logits_t1_kernel<8>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs, bp);
-    if (h == 4096) return launch(router_logits_t1_kernel<16>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs, bp);
-    return launch(router_logits_t1_kernel<24>, nlb + qblocks, 256, 0, s, x, wrP, E, logits, nlb, xq, xs, bp);
+    const int qb = xq ? (h / 8 + 63) / 64 : 0;  // 64 plane words per block
+    if (h == 2048) return launch(router_logits_t1_kernel<8>, E + qb, 64, 0, s, x, wrP, E, logits, E, xq, xs, bp);
+    if (h == 4096) return launch(router_logits_t1_kernel<16>, E + qb, 64, 0, s, x, wrP, E, logits, E, xq, xs, bp);
+    return launch(router_logits_t1_kernel<24>, E + qb, 64, 0, s, x, wrP, E, logits, E, xq, xs, bp);
   }
   // tiles per wave (experts x tokens) by batch size, measured on the GLM-like
   // layer (h = 6144, E = 256): the smallest tiles while they give the chip
