@@ -236,8 +236,11 @@ int coli_moe_last_routing(const coli_moe_t *m, int32_t *idx, float *w, int32_t *
  * sorted_ids [T*k], inv [T*k], active [E], n_active [1] (same meaning as
  * above; dropped assignments follow every group).  1 <= E <= 512,
  * 1 <= k <= 32, 0 <= T*k <= 2^20.  (cf-1.com Colibri article, section 3.3,
- * step 3.)  Errors: -4.  Values >= E give unspecified (but in-bounds)
- * results.
+ * step 3.)  Runs the same launches as coli_moe_forward for this T*k: one
+ * workgroup up to 1024 assignments, else a count launch and a scatter launch
+ * over ceil(T*k / 1024) workgroups, whose count array (that many times E+1
+ * ints) this call allocates and frees in stream order.  Errors: -4.  Values
+ * >= E give unspecified (but in-bounds) results.
  */
 int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *offsets,
                            int32_t *sorted_ids, int32_t *inv, int32_t *active, int32_t *n_active,

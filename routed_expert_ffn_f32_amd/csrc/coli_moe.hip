@@ -112,6 +112,7 @@ Layout layout_of(const coli_moe_config_t &c) {
   L.inv = o;        o = align_up(o + T * k * 4);
   L.active = o;     o = align_up(o + E * 4);
   L.n_active = o;   o = align_up(o + 4);
+  L.dcnt = o;       o = align_up(o + coli::dispatch_count_ints((int)(T * k), (int)E) * 4);
   L.mq = o;         o = align_up(o + P * planes * (I / 8) * 4);
   L.ms = o;         o = align_up(o + P * (I / 32) * 4);
   L.midf = o;       o = align_up(o + P * I * 4);
@@ -314,7 +315,7 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
                            [&] { return launch_router_select(logits, bias, T, E, k, rsf, lim, idx, wsel, s); });
     if (err != hipSuccess) return err;
     return timed(m, K_DISPATCH, s, [&] {
-      return launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, s);
+      return launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, at<int32_t>(m, L.dcnt), s);
     });
   };
   // Routing alone (phase kPhaseRoute without kPhaseExperts): selection and
@@ -545,10 +546,15 @@ int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, 
       (int64_t)T * k > (1 << 20))
     return COLI_MOE_EARG;
   if (!offsets || !active || !n_active || (T > 0 && (!idx || !sorted_ids || !inv))) return COLI_MOE_EARG;
-  if (coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active,
-                            static_cast<hipStream_t>(stream)) != hipSuccess)
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the many-workgroup sort's count array, stream-ordered
+  const size_t cnt_bytes = coli::dispatch_count_ints(T * k, E) * 4;
+  int32_t *cnt = nullptr;
+  if (cnt_bytes && hipMallocAsync(reinterpret_cast<void **>(&cnt), cnt_bytes, s) != hipSuccess)
     return COLI_MOE_EDEVICE;
-  return COLI_MOE_OK;
+  const hipError_t e = coli::launch_dispatch(idx, T * k, E, offsets, sorted_ids, inv, active, n_active, cnt, s);
+  if (cnt && hipFreeAsync(cnt, s) != hipSuccess) return COLI_MOE_EDEVICE;
+  return e == hipSuccess ? COLI_MOE_OK : COLI_MOE_EDEVICE;
 }
 
 int coli_moe_probe_read(const coli_moe_t *mc, const int32_t *experts, int32_t n, void *stream) {

@@ -13,6 +13,7 @@
 // Byte offsets of the workspace regions.
 struct Layout {
   size_t wrP, logits, xq, xs, idx, w, offsets, sorted_ids, inv, active, n_active, mq, ms, midf, y;
+  size_t dcnt;                      // per-workgroup key counts of the many-workgroup dispatch
   size_t xb, xexp, xn2, midb, pstats, tiles, n_tiles;  // prefill path
   size_t queues;                    // row queues of the small-batch gate/up launch
   size_t total;

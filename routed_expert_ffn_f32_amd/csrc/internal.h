@@ -13,7 +13,9 @@ namespace coli {
 
 // Kernel launch.  When the library's profiling wrapper has set an event pair,
 // the launch records it at the kernel's own start and end (AMD's extended
-// launch), so that the measured time is the kernel's duration alone.
+// launch), so that the measured time is the kernel's duration alone.  A step
+// of two launches splits the pair (split_launch_events): the start event on
+// the first, the stop event on the second.
 struct LaunchEvents {
   hipEvent_t start, stop;
 };
@@ -22,7 +24,7 @@ extern thread_local LaunchEvents launch_events;
 template <typename... KArgs, typename... Args>
 hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args &&...args) {
   static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
-  if (launch_events.start) {
+  if (launch_events.start || launch_events.stop) {
     const LaunchEvents ev = launch_events;
     launch_events = LaunchEvents{nullptr, nullptr};
     hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, ev.start, ev.stop, 0u, static_cast<KArgs>(args)...);
@@ -30,6 +32,14 @@ hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shme
     kernel<<<grid, block, shmem, s>>>(static_cast<KArgs>(args)...);
   }
   return hipGetLastError();
+}
+
+// The pending event pair, taken for a step of two launches: the caller sets
+// launch_events to {first.start, nullptr} and then {nullptr, first.stop}.
+inline LaunchEvents split_launch_events() {
+  const LaunchEvents ev = launch_events;
+  launch_events = LaunchEvents{nullptr, nullptr};
+  return ev;
 }
 
 constexpr int kWave = 64;              // CDNA wavefront width
@@ -93,10 +103,13 @@ hipError_t launch_select_dispatch(const float *logits, const float *bias, int T,
 
 // ---------------------------------------------------------------------------
 // Dispatch (dispatch.hip): stable counting sort of assignments by expert;
-// negative ids (dropped slots) follow every expert's group.
+// negative ids (dropped slots) follow every expert's group.  Batches of more
+// than one workgroup's assignments are sorted over many workgroups when a
+// count array of dispatch_count_ints(n, E) ints is given (else by one).
 // ---------------------------------------------------------------------------
+size_t dispatch_count_ints(int n, int E);
 hipError_t launch_dispatch(const int32_t *idx, int n, int E, int32_t *offsets, int32_t *sorted_ids,
-                           int32_t *inv, int32_t *active, int32_t *n_active, hipStream_t s);
+                           int32_t *inv, int32_t *active, int32_t *n_active, int32_t *cnt, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Expert GEMV path (expert_gemv.hip), decode-sized batches.

@@ -86,7 +86,8 @@ def test_dispatch_worked_examples_from_pages(dev):
 
 @pytest.mark.parametrize("T,k,E,skew", [(1, 8, 256, 0), (4, 2, 8, 0), (64, 8, 256, 0), (16, 8, 64, 0),
                                         (4096, 8, 256, 1), (333, 3, 17, 0), (1000, 1, 1, 0),
-                                        (8192, 16, 512, 1), (0, 4, 8, 0), (1, 32, 32, 0)])
+                                        (8192, 16, 512, 1), (0, 4, 8, 0), (1, 32, 32, 0),
+                                        (1025, 1, 5, 0), (1024, 1, 7, 0), (2049, 2, 300, 1), (4000, 8, 512, 0)])
 def test_dispatch_kernel_matches_oracle(dev, T, k, E, skew):
     import oracle
     log(f"dispatch T={T} k={k} E={E} skew={skew}")
