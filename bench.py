@@ -49,10 +49,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 F16_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_gemv_gate_up.txt")
+TRAFFIC_FILE_DOWN = os.path.join(ROOT, "profiles", "traffic_expert_gemv_down.txt")
 # sources of the dominant kernel: a counter summary taken on other sources
 # describes other code
 TRAFFIC_SOURCES = ["routed_expert_ffn_f32_amd/csrc/expert_gemv.hip", "routed_expert_ffn_f32_amd/csrc/wave.h",
-                   "routed_expert_ffn_f32_amd/csrc/select.h", "routed_expert_ffn_f32_amd/csrc/internal.h"]
+                   "routed_expert_ffn_f32_amd/csrc/select.h", "routed_expert_ffn_f32_amd/csrc/small_route.h",
+                   "routed_expert_ffn_f32_amd/csrc/internal.h"]
 
 
 def parse():
@@ -90,12 +92,13 @@ def sources_digest() -> str:
     return h.hexdigest()
 
 
-def read_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None when it is absent or was taken on other sources."""
+def read_traffic(path=None):
+    """HBM bytes per launch of a decode kernel (default: the dominant one) from
+    its committed counter summary, or None when it is absent or was taken on
+    other sources."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path or TRAFFIC_FILE) as f:
             for line in f:
                 line = line.strip()
                 if line and not line.startswith("#") and "=" in line:
@@ -336,6 +339,12 @@ def main():
         if n:
             us = 1e3 * ms / n
             kernel_rates[name] = {"bytes": int(nbytes), "us": round(us, 3), "GBps": round(nbytes / us / 1e3, 1)}
+    # HBM traffic per launch from the committed counter summaries (null when
+    # the kernel's sources changed since the counters were taken)
+    for name, path in ((dom_name, TRAFFIC_FILE), ("expert_gemv_down", TRAFFIC_FILE_DOWN)):
+        if name in kernel_rates:
+            tr = read_traffic(path)
+            kernel_rates[name]["traffic"] = None if tr is None else round(tr)
 
     result = {
         "metric": "MoE-layer tokens/s + expert-weight HBM GB/s (int4 gs64, decode T=1)",
