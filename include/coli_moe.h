@@ -217,6 +217,27 @@ int coli_moe_set_routing(coli_moe_t *m, int32_t k_use, float top_p);
 void coli_moe_free(coli_moe_t *m);
 
 /*
+ * Error word of the handle's launches.  The one-token gate/up launch hands
+ * the routing from one wave of each workgroup to the others through a flag
+ * in LDS; the others wait a bounded time (COLI_MOE_DEFAULT_SPIN_LIMIT polls
+ * of about 64 cycles, about 0.1 s).  A wave that gives up computes none of
+ * its routed rows and stores 1 in a device word of the workspace, so that
+ * call's output is wrong.  This call waits for `stream`, reads the word and
+ * clears it: COLI_MOE_OK when no launch since the last call (or since init)
+ * gave up, COLI_MOE_EDEVICE when one did or the read failed, -4 for NULL.
+ * Synchronous.  coli_moe_forward_noalloc has no handle and no such report.
+ */
+int coli_moe_status(coli_moe_t *m, void *stream);
+
+/*
+ * For tests of the error path: the bound of that wait, in polls (>= 0; 0:
+ * every waiting wave gives up at once, so every one-token call fails and is
+ * reported).  Takes effect from the next forward.  -4 for NULL or polls < 0.
+ */
+#define COLI_MOE_DEFAULT_SPIN_LIMIT (1 << 22)
+int coli_moe_test_spin_limit(coli_moe_t *m, int32_t polls);
+
+/*
  * Copy the routing and dispatch of the handle's last forward (T tokens) into
  * caller DEVICE buffers, enqueued on `stream` (for parity checks).  Any
  * pointer may be NULL to skip it.  Sizes: idx and w [T*k] (assignment

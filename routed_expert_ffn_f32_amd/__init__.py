@@ -29,6 +29,7 @@ COLI_MOE_EDEVICE = -3
 COLI_MOE_EARG = -4
 COLI_MOE_N_KERNELS = 10
 COLI_MOE_STATIC_SCRATCH_BYTES = 64 << 20
+COLI_MOE_DEFAULT_SPIN_LIMIT = 1 << 22
 
 
 class ColiMoeError(RuntimeError):
@@ -95,6 +96,10 @@ def load_library():
         L.coli_moe_set_routing.restype = ctypes.c_int
         L.coli_moe_last_routing.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.coli_moe_last_routing.restype = ctypes.c_int
+        L.coli_moe_status.argtypes = [vp, vp]
+        L.coli_moe_status.restype = ctypes.c_int
+        L.coli_moe_test_spin_limit.argtypes = [vp, i32]
+        L.coli_moe_test_spin_limit.restype = ctypes.c_int
         L.coli_moe_test_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.coli_moe_test_dispatch.restype = ctypes.c_int
         L.coli_moe_probe_read.argtypes = [vp, vp, i32, vp]
@@ -412,6 +417,12 @@ class MoELayer:
         k_use = self.cfg.top_k if k_use is None else int(k_use)
         coli_moe_set_routing(self.handle, k_use, top_p)
         _warn_lossy(k_use, self.cfg.top_k, top_p)
+
+    def status(self) -> int:
+        """Waits for the layer's stream; COLI_MOE_OK unless a launch since the
+        last check gave up its bounded wait (COLI_MOE_EDEVICE).  Clears the
+        error word."""
+        return int(load_library().coli_moe_status(self.handle, ctypes.c_void_p(self.stream)))
 
     def last_routing(self):
         """Device tensors of the last forward's routing and dispatch."""

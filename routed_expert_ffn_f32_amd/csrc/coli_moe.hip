@@ -127,6 +127,7 @@ Layout layout_of(const coli_moe_config_t &c) {
   L.tiles = o;      o = align_up(o + tiles * 8);
   L.n_tiles = o;    o = align_up(o + 4);
   L.queues = o;     o = align_up(o + coli::kRowQueueWords * 4);
+  L.status = o;     o = align_up(o + 4);
   L.total = o;
   return L;
 }
@@ -220,6 +221,7 @@ void set_up(coli_moe_t *m, const coli_moe_config_t &cfg, const coli_moe_weights_
   m->slot_of = nullptr;
   m->k_use = cfg.top_k;
   m->top_p = 1.0f;
+  m->spin_limit = coli::kSpinLimit;
 }
 
 // The workspace state every forward starts from: the lane-permuted router,
@@ -228,6 +230,7 @@ hipError_t stage(coli_moe_t *m, hipStream_t s) {
   hipError_t e = coli::launch_router_permute(m->w.router_w, at<float>(m, m->L.wrP), m->cfg.hidden,
                                              m->cfg.n_experts, s);
   if (e == hipSuccess) e = coli::launch_fill_i32(at<int32_t>(m, m->L.queues), coli::kRowQueueWords, 0, s);
+  if (e == hipSuccess) e = coli::launch_fill_i32(at<int32_t>(m, m->L.status), 1, 0, s);
   if (e == hipSuccess && prefill_enabled(m->cfg)) e = coli::launch_prefill_stats(prefill_problem(m, 0), s);
   return e;
 }
@@ -383,6 +386,8 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
   P.n_active = n_active;
   P.queues = at<int32_t>(m, L.queues);
   P.slot_of = m->slot_of;
+  P.status = at<int32_t>(m, L.status);
+  P.spin_limit = m->spin_limit;
 
   if (small) {
     // 2. gate/up (each block routes the batch itself), 3. down + combine
@@ -537,6 +542,26 @@ int coli_moe_last_routing(const coli_moe_t *mc, int32_t *idx, float *w, int32_t 
       return COLI_MOE_EDEVICE;
   }
   return m->last_T;
+}
+
+static_assert(coli::kSpinLimit == COLI_MOE_DEFAULT_SPIN_LIMIT, "one default bound");
+
+int coli_moe_status(coli_moe_t *m, void *stream) {
+  if (!m) return COLI_MOE_EARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t word = 0;
+  if (hipMemcpyAsync(&word, m->ws + m->L.status, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return COLI_MOE_EDEVICE;
+  if (word == 0) return COLI_MOE_OK;
+  if (coli::launch_fill_i32(at<int32_t>(m, m->L.status), 1, 0, s) != hipSuccess) return COLI_MOE_EDEVICE;
+  return COLI_MOE_EDEVICE;
+}
+
+int coli_moe_test_spin_limit(coli_moe_t *m, int32_t polls) {
+  if (!m || polls < 0) return COLI_MOE_EARG;
+  m->spin_limit = polls;
+  return COLI_MOE_OK;
 }
 
 int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *offsets,

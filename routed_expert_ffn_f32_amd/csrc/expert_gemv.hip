@@ -604,13 +604,18 @@ __global__ __launch_bounds__(XREG ? 256 : 512) void gate_up_rows_kernel(DecodePr
     gu_load(bs, cs, has0, h);
     if (wave != 0) {
       // wave 0 sets the flag without waiting for any other wave; the bound
-      // only guards against a hang (a wave that gives up streams no routed
-      // row)
+      // only guards against a hang: a wave that gives up streams no routed
+      // row (the rows it took from its queue stay uncomputed) and stores 1
+      // in the error word, so the call is reported as failed
       int spins = 0;
-      while (__hip_atomic_load(&routed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0 && ++spins < (1 << 22))
+      while (__hip_atomic_load(&routed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0 &&
+             ++spins < P.spin_limit)
         __builtin_amdgcn_s_sleep(1);
       asm volatile("" ::: "memory");  // R is read after the flag
-      have_routing = spins < (1 << 22);
+      have_routing = __builtin_amdgcn_readfirstlane(spins < P.spin_limit ? 1 : 0) != 0;
+      // every lane stores the same word: a store under a lane condition
+      // here made the compiler keep the wave's uniform values in VGPRs
+      if (!have_routing) __hip_atomic_store(P.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
     route_small_b(T, P.E, P.k, P.rsf, P.lim, R);

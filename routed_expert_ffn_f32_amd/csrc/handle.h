@@ -16,6 +16,7 @@ struct Layout {
   size_t dcnt;                      // per-workgroup key counts of the many-workgroup dispatch
   size_t xb, xexp, xn2, midb, pstats, tiles, n_tiles;  // prefill path
   size_t queues;                    // row queues of the small-batch gate/up launch
+  size_t status;                    // device error word (coli_moe_status)
   size_t total;
 };
 
@@ -41,6 +42,7 @@ struct coli_moe {
   // run-time routing limits (k_use = top_k, top_p = 1: none)
   int32_t k_use;
   float top_p;
+  int32_t spin_limit;  // bound of the one-token gate/up launch's LDS-flag wait, in polls
 };
 
 namespace coli {

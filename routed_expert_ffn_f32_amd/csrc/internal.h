@@ -151,7 +151,12 @@ struct DecodeProblem {
   // zero when it starts; the down launch clears them again)
   int32_t *queues;
   const int32_t *slot_of;  // expert -> table index (NULL: identity)
+  // error word: a launch that gave up a bounded wait stores 1 (read and
+  // cleared by coli_moe_status); the bound of that wait in polls
+  int32_t *status;
+  int32_t spin_limit;
 };
+constexpr int32_t kSpinLimit = 1 << 22;  // polls of about 64 cycles: about 0.1 s
 constexpr int kRowQueueWords = 64 * 64;
 
 // True when the batch takes the small-batch launch structure (router and
