@@ -372,7 +372,7 @@ def check_mfma(shape, seed, T, dev, threshold, max_tokens=None, wr=None, bias=No
 
 def test_mfma_path_several_tiles_ragged(dev):
     """T = 300 tokens, 16 experts, k = 4: about 75 tokens per expert, the
-    shared expert in 3 tiles (128 + 128 + 44 rows), every N tile count > 1."""
+    shared expert in 2 tiles (256 + 44 rows), every N tile count > 1."""
     log("MFMA path T=300 h=256 I=512 E=16 k=4")
     check_mfma(MID, 21, 300, dev, threshold=64)
 
