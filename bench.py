@@ -323,6 +323,18 @@ def main():
     probe_us = 1e3 * probe_ms / (K * L)
     probe_bytes = mean_experts * gate_up_w
 
+    # the same for the down + combine launch: its experts' down rows, its
+    # grid and row split, loads only
+    def run_probe_down(s0, steps):
+        for st in range(s0, s0 + steps):
+            for l in range(L):
+                e = exs[l][(st * L + l) % args.pool]
+                cm.coli_moe_probe_read_down(layers[l].handle, e.data_ptr(), e.numel(), stream)
+
+    run_probe_down(0, W)
+    probe_down_ms = time_calls(torch, lambda st: run_probe_down(W + st, 1), K)
+    probe_down_us = 1e3 * probe_down_ms / (K * L)
+
     # every decode kernel's algorithmic bytes and rate: the router (f32 table
     # and the token row, the digit planes written), gate/up (above), down with
     # the combine (the experts' down codes and scales, the intermediate rows,
@@ -374,6 +386,13 @@ def main():
         "read_ceiling": {"kernel": "read probe: the same calls' gate and up rows, loads only, same grid",
                          "us_per_launch": round(probe_us, 3), "GBps": round(probe_bytes / probe_us / 1e3, 1),
                          "dominant_kernel_time_over_probe": round(1e6 * dom_avg_s / probe_us, 4)},
+        "read_ceiling_down": {"kernel": "read probe: the same calls' down rows, loads only, the down + combine "
+                                        "launch's grid and row split",
+                              "us_per_launch": round(probe_down_us, 3),
+                              "GBps": round(mean_experts * down_w / probe_down_us / 1e3, 1),
+                              "down_kernel_time_over_probe": (round(kernel_rates["expert_gemv_down"]["us"] /
+                                                                    probe_down_us, 4)
+                                                              if "expert_gemv_down" in kernel_rates else None)},
     }
     # per-step times of the same stack (a separate loop, one event per step)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]

@@ -281,6 +281,16 @@ int coli_moe_test_dispatch(const int32_t *idx, int32_t T, int32_t k, int32_t E, 
 int coli_moe_probe_read(const coli_moe_t *m, const int32_t *experts, int32_t n, void *stream);
 
 /*
+ * Measurement only: the same for the one-token down + combine kernel.  One
+ * launch with that kernel's grid and row split (each wave owns a contiguous
+ * range of output rows) that loads, and otherwise discards, the down codes
+ * and scales of those rows of the n experts listed in DEVICE experts [n]
+ * (as above), two experts in flight per wave.  Overwrites the handle's
+ * logits buffer.  1 <= n <= 64, inter <= 8192.  Errors: -4, -3.
+ */
+int coli_moe_probe_read_down(const coli_moe_t *m, const int32_t *experts, int32_t n, void *stream);
+
+/*
  * Measurement only: the rates this GPU reaches, for setting the layer's
  * figures against them (no handle needed).
  *

@@ -104,6 +104,8 @@ def load_library():
         L.coli_moe_test_dispatch.restype = ctypes.c_int
         L.coli_moe_probe_read.argtypes = [vp, vp, i32, vp]
         L.coli_moe_probe_read.restype = ctypes.c_int
+        L.coli_moe_probe_read_down.argtypes = [vp, vp, i32, vp]
+        L.coli_moe_probe_read_down.restype = ctypes.c_int
         L.coli_moe_probe_stream.argtypes = [vp, ctypes.c_size_t, vp, vp]
         L.coli_moe_probe_stream.restype = ctypes.c_int
         L.coli_moe_probe_mfma.argtypes = [i32, i32, vp, vp]
@@ -223,6 +225,13 @@ def coli_moe_probe_read(handle, experts: int, n: int, stream: int = 0) -> int:
     """Pure-load probe of the gate/up rows of n experts (device int32 ids, -1
     = shared): the read ceiling of the gate/up access pattern."""
     return _check(load_library().coli_moe_probe_read(handle, experts, int(n), stream), "coli_moe_probe_read")
+
+
+def coli_moe_probe_read_down(handle, experts: int, n: int, stream: int = 0) -> int:
+    """Pure-load probe of the down rows of n experts with the one-token down +
+    combine launch's grid: the read ceiling of that access pattern."""
+    return _check(load_library().coli_moe_probe_read_down(handle, experts, int(n), stream),
+                  "coli_moe_probe_read_down")
 
 
 def coli_moe_probe_stream(buf: int, nbytes: int, sink: int, stream: int = 0) -> int:

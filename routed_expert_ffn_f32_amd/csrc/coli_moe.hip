@@ -602,6 +602,24 @@ int coli_moe_probe_read(const coli_moe_t *mc, const int32_t *experts, int32_t n,
   return COLI_MOE_OK;
 }
 
+int coli_moe_probe_read_down(const coli_moe_t *mc, const int32_t *experts, int32_t n, void *stream) {
+  if (!mc || !experts || n < 1 || n > 64 || mc->cfg.inter > 8192 ||
+      mc->cfg.weight_format != COLI_MOE_WEIGHTS_INT4_GS64)
+    return COLI_MOE_EARG;
+  coli_moe_t *m = const_cast<coli_moe_t *>(mc);
+  coli::DecodeProblem P{};
+  P.down = {m->w.down_q, m->w.down_s};
+  P.sh_down = {m->w.sh_down_q, m->w.sh_down_s};
+  P.h = m->cfg.hidden;
+  P.I = m->cfg.inter;
+  P.E = m->cfg.n_experts;
+  P.has_shared = m->cfg.n_shared;
+  if (coli::launch_read_probe_down(P, experts, n, at<uint32_t>(m, m->L.logits), static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return COLI_MOE_EDEVICE;
+  return COLI_MOE_OK;
+}
+
 int coli_moe_probe_stream(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
   if (!buf || !sink || bytes == 0 || bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4)) return COLI_MOE_EARG;
   return coli::launch_stream_probe(buf, bytes, sink, static_cast<hipStream_t>(stream)) == hipSuccess

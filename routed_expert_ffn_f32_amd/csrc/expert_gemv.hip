@@ -1343,7 +1343,68 @@ __global__ __launch_bounds__(256) void read_probe_kernel(DecodeProblem P, const 
   if (acc == 0x9e3779b9u) sink[0] = acc;  // (almost) never taken; the loads must stay
 }
 
+// Read probe of the one-token down + combine launch: the down codes and
+// scales of the n experts' rows, loaded with that launch's grid and row split
+// (wave w of W owns rows [w h / W, (w + 1) h / W), at most RM), two experts
+// in flight per wave, as its two-slot ring, and nothing computed but an XOR.
+template <int NCHD, int RM>
+__global__ __launch_bounds__(kDcWaves * 64) void read_probe_down_kernel(DecodeProblem P,
+                                                                       const int32_t *__restrict__ experts, int n,
+                                                                       uint32_t *__restrict__ sink) {
+  const int wave = uniform(threadIdx.x >> 6);
+  const int h = P.h, I = P.I;
+  const int64_t W = (int64_t)gridDim.x * kDcWaves, gw = (int64_t)blockIdx.x * kDcWaves + wave;
+  const int r0 = (int)((int64_t)h * gw / W), nr = (int)((int64_t)h * (gw + 1) / W) - r0;
+  const size_t qstride = (size_t)h * (I >> 1), sstride = (size_t)h * (I >> 6);
+  uint32_t acc = 0;
+  for (int s0 = 0; s0 < n; s0 += 2) {
+    DnBuf<NCHD, FmtI4> b[2][RM];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const int e = uniform(experts[min(s0 + d, n - 1)]);
+      const bool shared = e == -1 && P.has_shared;
+      const bool valid = shared || (e >= 0 && e < P.E);
+      const uint8_t *q = shared ? P.sh_down.q : P.down.q + (valid ? (size_t)e * qstride : 0);
+      const float *sc = shared ? P.sh_down.s : P.down.s + (valid ? (size_t)e * sstride : 0);
+#pragma unroll
+      for (int r = 0; r < RM; ++r) dn_load(b[d][r], q, sc, r0 + r, valid && r < nr, I);
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int r = 0; r < RM; ++r)
+#pragma unroll
+        for (int cc = 0; cc < NCHD; ++cc)
+          acc ^= b[d][r].w[cc].x ^ b[d][r].w[cc].y ^ b[d][r].w[cc].z ^ b[d][r].w[cc].w ^ __float_as_uint(b[d][r].s[cc]);
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;  // (almost) never taken; the loads must stay
+}
+
+template <int NCHD>
+hipError_t launch_read_probe_down_r(const DecodeProblem &P, const int32_t *experts, int n, uint32_t *sink,
+                                    hipStream_t s) {
+  const int blocks = min(kDcBlocks, (P.h + kDcWaves - 1) / kDcWaves);
+  const int rm = (P.h + blocks * kDcWaves - 1) / (blocks * kDcWaves);
+  switch (rm) {
+    case 1: return launch(read_probe_down_kernel<NCHD, 1>, blocks, kDcWaves * 64, 0, s, P, experts, n, sink);
+    case 2: return launch(read_probe_down_kernel<NCHD, 2>, blocks, kDcWaves * 64, 0, s, P, experts, n, sink);
+    case 3: return launch(read_probe_down_kernel<NCHD, 3>, blocks, kDcWaves * 64, 0, s, P, experts, n, sink);
+    case 4: return launch(read_probe_down_kernel<NCHD, 4>, blocks, kDcWaves * 64, 0, s, P, experts, n, sink);
+    default: return launch(read_probe_down_kernel<NCHD, 8>, blocks, kDcWaves * 64, 0, s, P, experts, n, sink);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_read_probe_down(const DecodeProblem &P, const int32_t *experts, int n, uint32_t *sink,
+                                  hipStream_t s) {
+  switch ((P.I + 2047) / 2048) {
+    case 1: return launch_read_probe_down_r<1>(P, experts, n, sink, s);
+    case 2: return launch_read_probe_down_r<2>(P, experts, n, sink, s);
+    case 3: return launch_read_probe_down_r<3>(P, experts, n, sink, s);
+    default: return launch_read_probe_down_r<4>(P, experts, n, sink, s);
+  }
+}
 
 hipError_t launch_read_probe(const DecodeProblem &P, const int32_t *experts, int n, uint32_t *sink,
                              hipStream_t s) {

@@ -182,6 +182,8 @@ hipError_t launch_mfma_probe(int iters, int blocks, uint32_t *sink, hipStream_t 
 hipError_t launch_mfma_probe_f16(int iters, int blocks, uint32_t seed, uint32_t *sink, hipStream_t s);
 hipError_t launch_read_probe(const DecodeProblem &P, const int32_t *experts, int n, uint32_t *sink,
                              hipStream_t s);
+hipError_t launch_read_probe_down(const DecodeProblem &P, const int32_t *experts, int n, uint32_t *sink,
+                                  hipStream_t s);
 // Small batches: out[t] = sum_j w[t,j] Wd_e mid[inv(t,j)] + Wd_sh mid[T*k + t].
 hipError_t launch_down_combine(const DecodeProblem &P, float *out, hipStream_t s);
 // Larger batches: y[p] = Wd mid[p] ...

@@ -125,6 +125,7 @@ def test_int8_config_checks(dev):
     try:
         e = torch.tensor([0, 1], dtype=torch.int32, device=dev)
         assert lib.coli_moe_probe_read(L.moe.handle, ctypes.c_void_p(e.data_ptr()), 2, None) == -4
+        assert lib.coli_moe_probe_read_down(L.moe.handle, ctypes.c_void_p(e.data_ptr()), 2, None) == -4
     finally:
         L.close()
 

@@ -207,6 +207,17 @@ def test_measurement_probes(dev):
     cm.coli_moe_probe_mfma(1000, 96, sink.data_ptr(), stream)
     torch.cuda.synchronize()
     assert int(sink.item()) == 96 * 4
+    # the read probes of the two decode launches run on a layer's tables,
+    # out-of-range ids reading nothing
+    shape = synth.LayerShape(hidden=6144, n_experts=16, top_k=4, inter=2048, n_shared=1, rsf=2.5, bias_sigma=0.05)
+    L = DeviceLayer(shape, 9, 0, dev, max_tokens=1)
+    try:
+        e = torch.tensor([0, 15, -1, 16, -2], dtype=torch.int32, device=dev)
+        cm.coli_moe_probe_read(L.moe.handle, e.data_ptr(), e.numel(), stream)
+        cm.coli_moe_probe_read_down(L.moe.handle, e.data_ptr(), e.numel(), stream)
+        torch.cuda.synchronize()
+    finally:
+        L.close()
 
 
 def test_all_codes_including_minus_eight(dev):
