@@ -363,7 +363,7 @@ def test_small_batch_calls_in_a_row(dev, name, T):
 
 
 # ---------------------------------------------------------------------------
-# The bf16 MFMA (prefill) path on small layers: full outputs.
+# The fp16 MFMA (prefill) path on small layers: full outputs.
 # ---------------------------------------------------------------------------
 
 MID = synth.LayerShape(hidden=256, n_experts=16, top_k=4, inter=512, n_shared=1, rsf=2.5, bias_sigma=0.05)
