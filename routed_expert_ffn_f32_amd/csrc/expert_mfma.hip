@@ -39,17 +39,21 @@
 //
 // Tiles: 256 rows of A (tokens of one expert) x 256 weight rows (gate/up:
 // 128 intermediate rows of gate and the same 128 of up; down: 256 output
-// rows); 8 waves, two per SIMD.  Wave w owns one 32-row MFMA block of B
-// (gate/up: pair w / 2, gate for even w, up for odd w) and all 256 tokens
-// (8 blocks of 32 tokens, those wholly past the expert's last token
-// skipped), so each converted weight feeds up to 8 MFMAs.  K runs in steps
-// of 64 columns (one scale group); each lane owns 32 of the 64 columns, so
-// the 4 MFMAs of a step cover columns {8j..8j+7} and {32+8j..32+8j+7}.  A
-// rows and weights are copied into LDS rings ahead of use, the copies spread
-// between MFMA groups.  For SwiGLU the up waves hand their accumulators to
-// the gate waves through LDS.  Tiles are long in M and short in N because a
-// token row per step is one whole cache line while a weight row per step is
-// a 32-byte piece of one: the copies cost least per MFMA that way.
+// rows) in 8 groups of 32 rows; 8 waves, two per SIMD, wave w copying group
+// w.  K runs in steps of 64 columns (one scale group); each lane owns 32 of
+// the 64 columns, so the 4 MFMAs of a step cover columns {8j..8j+7} and
+// {32+8j..32+8j+7}.  A rows and weights are copied into LDS rings ahead of
+// use, the copies spread between MFMA groups.
+//  - down: wave w computes group w for all 256 tokens (8 blocks of 32
+//    tokens, those wholly past the expert's last token skipped), so each
+//    converted weight feeds up to 8 MFMAs;
+//  - gate/up: wave w computes the gate group and the up group of pair w % 4
+//    for the 128 tokens of half w / 4, so each A fragment read from LDS
+//    feeds two MFMAs (half the LDS reads per MFMA, twice the conversions:
+//    4% faster than one group per wave) and SwiGLU needs no exchange.
+// Tiles are long in M and short in N because a token row per step is one
+// whole cache line while a weight row per step is a 32-byte piece of one: the
+// copies cost least per MFMA that way.
 //
 // The tile list (expert slot, first token) is built on the device from the
 // dispatch offsets, largest tiles first.  The grid is launched for the
@@ -205,7 +209,7 @@ struct Sources {
   const uint8_t *q_base; // codes of this wave's 32 rows
   uint32_t q_off;        // row lane / 2 of the 32, this lane's 16 bytes
   const float *s_row;    // scales of row 32 w + lane (lanes 0..31)
-  float wm;              // 2^ew of this wave's weight table
+  float wm[2];           // 2^ew of the weight groups this wave computes
 };
 
 template <int NMB>
@@ -273,57 +277,84 @@ struct QCopies {
   }
 };
 
-// One wave's share of a tile: acc = A x B^T for its 32 weight rows over the
-// K columns of the tile (G steps of 64), for the first NMB token blocks of
-// the tile (NMB is uniform over the block, so the MFMA sequence is
-// straight-line code).
-template <int NMB>
+// One wave's share of a tile: acc = A x B^T for its weight rows over the K
+// columns of the tile (G steps of 64).  Wave w copies weight group w (rows
+// 32 w .. 32 w + 31 of the tile's 256) and
+//  - PAIRS = false: computes group w for the first NMB token blocks;
+//  - PAIRS = true: computes groups 2 (w % 4) and 2 (w % 4) + 1 (a gate/up
+//    pair) for NMW token blocks of its token half (blocks 4 (w / 4) ..), so
+//    that every A fragment read from LDS feeds two MFMAs; each weight is
+//    converted by the two waves that read it.  Waves read groups that other
+//    waves copy, so every step, not only every pair of steps, starts at a
+//    block barrier.
+// NMB / NMW are uniform over the wave, so the MFMA sequence is straight-line
+// code.
+template <int NMB, int NMW, bool PAIRS>
 struct WaveGemm {
-  f32x16 acc[NMB];
+  static constexpr int NBW = PAIRS ? 2 : 1;         // weight groups computed
+  static constexpr int NA = NMW > 0 ? NMW : 1;
+  f32x16 acc[NBW][NA];
 
-  // One 64-column step.  Software-pipelined by MFMA group: while the NMB
-  // MFMAs of group j run, the A fragments of group j + 1 are read from LDS
-  // and its weights converted (the compiler interleaves them; a fixed
-  // one MFMA : one LDS read : three VALU pattern measured 3% slower).
-  // Step g from A slot g & 3, Q slot sq.
+  // One 64-column step.  Software-pipelined by MFMA group: while the MFMAs
+  // of group j run, the A fragments of group j + 1 are read from LDS and its
+  // weights converted (the compiler interleaves them; a fixed one MFMA : one
+  // LDS read : three VALU pattern measured 3% slower).  Step g from A slot
+  // g & 3, Q slot sq.
   template <class C>
-  __device__ __forceinline__ void compute(const char *lds, int g, int sq, float wm, const C &copies) {
+  __device__ __forceinline__ void compute(const char *lds, int g, int sq, const float (&wm)[2], const C &copies) {
     const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
-    const char *A = lds + (g & 3) * kASlotBytes;
-    const char *Q = lds + kQRingOff + sq * kQSlotBytes;
-    const uint4 q = *reinterpret_cast<const uint4 *>(Q + 32 * wave * 32 + 16 * (2 * nl + (half ^ ((nl >> 3) & 1))));
-    const float c = *reinterpret_cast<const float *>(lds + kSRingOff + ((g >> 2) & 1) * kSSlotBytes +
-                                                     (32 * wave + nl) * 16 + (g & 3) * 4);
-    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-    const float sc = c * wm;
-    const _Float16 h1 = (_Float16)sc, h16 = (_Float16)(sc * 0.0625f);
-    const f16x2 s1 = {h1, h1}, s16 = {h16, h16};
-    // row r = 32 mb + nl of group j: chunk slot (4 half + j) ^ ((r >> 1) & 7), (r >> 1) & 7 = (nl >> 1) & 7
+    if constexpr (NMW == 0) {  // a token half past the tile: copies only
+#pragma unroll
+      for (int j = 0; j < 4; ++j) copies.after(j);
+      return;
+    }
+    const int grp = PAIRS ? 2 * (wave & 3) : wave, row0 = PAIRS ? 128 * (wave >> 2) : 0;
+    const char *A = lds + (g & 3) * kASlotBytes + row0 * 128;
+    const char *Q = lds + kQRingOff + sq * kQSlotBytes + grp * (32 * 32);
+    const char *Sc = lds + kSRingOff + ((g >> 2) & 1) * kSSlotBytes + grp * (32 * 16);
+    uint32_t qw[NBW][4];
+    f16x2 s1[NBW], s16[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const uint4 q = *reinterpret_cast<const uint4 *>(Q + nb * (32 * 32) + 16 * (2 * nl + (half ^ ((nl >> 3) & 1))));
+      qw[nb][0] = q.x, qw[nb][1] = q.y, qw[nb][2] = q.z, qw[nb][3] = q.w;
+      const float sc = *reinterpret_cast<const float *>(Sc + (32 * nb + nl) * 16 + (g & 3) * 4) * wm[nb];
+      const _Float16 h1 = (_Float16)sc, h16 = (_Float16)(sc * 0.0625f);
+      s1[nb] = f16x2{h1, h1};
+      s16[nb] = f16x2{h16, h16};
+    }
+    // row r = row0 + 32 mb + nl of group j: chunk slot (4 half + j) ^ ((r >> 1) & 7),
+    // (r >> 1) & 7 = (nl >> 1) & 7
     const char *arow = A + nl * 128;
     const int sw_ = (nl >> 1) & 7;
-    f16x8 af[2][NMB], bf[2];
+    f16x8 af[2][NA], bf[2][NBW];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int mb = 0; mb < NMW; ++mb)
       af[0][mb] = *reinterpret_cast<const f16x8 *>(arow + mb * 4096 + (((4 * half) ^ sw_) * 16));
-    bf[0] = convert8(qw[0], s1, s16);
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) bf[0][nb] = convert8(qw[nb][0], s1[nb], s16[nb]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int cur = j & 1, nxt = cur ^ 1;
       if (j < 3) {
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
+        for (int mb = 0; mb < NMW; ++mb)
           af[nxt][mb] = *reinterpret_cast<const f16x8 *>(arow + mb * 4096 + (((4 * half + j + 1) ^ sw_) * 16));
-        bf[nxt] = convert8(qw[j + 1], s1, s16);
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) bf[nxt][nb] = convert8(qw[nb][j + 1], s1[nb], s16[nb]);
       }
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][mb], bf[cur], acc[mb], 0, 0, 0);
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < NMW; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][mb], bf[cur][nb], acc[nb][mb], 0, 0, 0);
       copies.after(j);
     }
   }
 
   // Issue order (pair of steps g, g + 1, g even):
   //   [barrier] A(g+2) A(g+3) Q(g+2) (S(g/4 + 1) when g % 4 == 0) | step g |
-  //   Q(g+3) | step g + 1
+  //   ([barrier] when PAIRS) Q(g+3) | step g + 1
   // (indices past the end re-fetch the last one).  Before step g: A(g),
   // A(g+1), Q(g) and S(g/4) are done once at most Q(g+1) and, when g % 4 ==
   // 2, S(g/4) are pending; before step g + 1, Q(g+1) is done once at most the
@@ -332,7 +363,9 @@ struct WaveGemm {
 
   __device__ __forceinline__ void run(const Sources &S, int G, char *lds) {  // G >= 4, G % 4 == 0
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < NA; ++mb) acc[nb][mb] = f32x16{};
     const int last_chunk = G / kSChunk - 1;
 #pragma unroll
     for (int i = 0; i < kA; ++i) copy_a<NMB>(S, 0, lds, 0, i);
@@ -357,6 +390,7 @@ struct WaveGemm {
         dma_wait<2 * kA + 2>();
       else
         dma_wait<2 * kA + 1>();
+      if constexpr (PAIRS) block_barrier();  // Q(g+1) of every wave visible; every wave done with step g's slot
       compute(lds, g + 1, sq1, S.wm, QCopies{S, lds, min(g + 3, G - 1), sq});  // Q(g+3) into step g's slot
       sq = sq2;
     }
@@ -416,13 +450,44 @@ __device__ __forceinline__ RowExp row_exp(const PrefillProblem &P, const Tile &t
 
 // ---------------------------------------------------------------------------
 // gate/up: mid'[p][c] = half(silu(g) * u * 2^(14 - eb)), g = x . Wg[c],
-// u = x . Wu[c].  Column blocks of 128 intermediate rows.
+// u = x . Wu[c].  Column blocks of 128 intermediate rows: weight group 2 q
+// holds the gate rows c0 .. c0 + 31, group 2 q + 1 the up rows of the same c
+// (c0 = 128 n + 32 q); wave w computes the pair q = w % 4 for the tokens of
+// its half w / 4 (WaveGemm with PAIRS), so SwiGLU needs nothing from another
+// wave.
 // ---------------------------------------------------------------------------
+template <int NMB, int NMW>
+__device__ __forceinline__ void gate_up_finish(const PrefillProblem &P, const Tile &t, int n_blk, char *lds,
+                                               const Sources &S, const PrefillStats &st, const RowExp &rx) {
+  const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
+  WaveGemm<NMB, NMW, true> W;
+  W.run(S, P.h / BK, lds);
+  int2 *rowx = reinterpret_cast<int2 *>(lds + kRowExpOff);
+  if (threadIdx.x < BM) rowx[threadIdx.x] = make_int2(rx.ex, rx.eb);
+  block_barrier();
+  const int cs = perm8(n_blk * 128 + (wave & 3) * 32 + nl);
+#pragma unroll
+  for (int mb = 0; mb < NMW; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int m = 128 * (wave >> 2) + acc_row(mb, half, i);
+      if (m < t.rows) {
+        const int2 e = rowx[m];
+        const float g = __builtin_amdgcn_ldexpf(W.acc[0][mb][i], e.x - st.ew[0]);
+        const float u = __builtin_amdgcn_ldexpf(W.acc[1][mb][i], e.x - st.ew[1]);
+        // silu in float32 with the hardware exp and reciprocal
+        const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+        const float mid = __builtin_amdgcn_ldexpf(sg * u, 14 - e.y);
+        P.mid[(size_t)(t.p_begin + m) * P.I + cs] = (_Float16)mid;
+      }
+    }
+}
+
 template <int NMB>
 __device__ __forceinline__ void gate_up_tile(const PrefillProblem &P, const Tile &t, int n_blk, char *lds) {
   const int h = P.h, I = P.I;
-  const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31, half = lane >> 5;
-  const int pair = wave >> 1, up = wave & 1;
+  const int lane = threadIdx.x & 63, wave = wave_id(), nl = lane & 31;
+  const int pair = wave >> 1, up = wave & 1;  // the group this wave copies
   const PrefillStats st = P.stats[t.stat];
   Sources S;
   S.a_base = reinterpret_cast<const char *>(P.xb);
@@ -430,52 +495,26 @@ __device__ __forceinline__ void gate_up_tile(const PrefillProblem &P, const Tile
   const size_t qstride = (size_t)I * (h >> 1), sstride = (size_t)I * (h >> 6);
   const ExpertTables &M = t.e < 0 ? (up ? P.sh_up : P.sh_gate) : (up ? P.up : P.gate);
   const size_t eq = t.e < 0 ? 0 : (size_t)t.e * qstride, es = t.e < 0 ? 0 : (size_t)t.e * sstride;
-  const int row0 = n_blk * 128 + pair * 32;  // this wave's gate or up rows row0 .. row0 + 31
+  const int row0 = n_blk * 128 + pair * 32;  // gate or up rows row0 .. row0 + 31
   S.q_base = M.q + eq + (size_t)row0 * (h >> 1);
   S.q_off = (uint32_t)((lane >> 1) * (h >> 1) + ((lane & 1) ^ ((lane >> 4) & 1)) * 16);
   S.s_row = M.s + es + (size_t)(row0 + nl) * (h >> 6);
-  S.wm = pow2f(st.ew[up]);
+  S.wm[0] = pow2f(st.ew[0]);
+  S.wm[1] = pow2f(st.ew[1]);
   // this thread's tile row: its token's exponent and the intermediate's
   // (loads issued now, used after the K loop)
   const RowExp rx = row_exp(P, t, st, threadIdx.x);
-
-  WaveGemm<NMB> W;
-  W.run(S, h / BK, lds);
-  int2 *rowx = reinterpret_cast<int2 *>(lds + kRowExpOff);
-  if (threadIdx.x < BM) rowx[threadIdx.x] = make_int2(rx.ex, rx.eb);
-
-  // up waves hand their accumulators to the gate wave of their pair, lane by
-  // lane (the same lane holds the same (token, row) in both waves)
-  float *xchg = reinterpret_cast<float *>(lds) + (size_t)pair * (NMB * 16 * 64);
-  if (up) {
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xchg[(mb * 16 + i) * 64 + lane] = W.acc[mb][i];
-  }
-  block_barrier();
-  if (!up) {
-    const int cs = perm8(row0 + nl);
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = acc_row(mb, half, i);
-        if (m < t.rows) {
-          const int2 e = rowx[m];
-          const float g = __builtin_amdgcn_ldexpf(W.acc[mb][i], e.x - st.ew[0]);
-          const float u = __builtin_amdgcn_ldexpf(xchg[(mb * 16 + i) * 64 + lane], e.x - st.ew[1]);
-          // silu in float32 with the hardware exp and reciprocal
-          const float sg = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-          const float mid = __builtin_amdgcn_ldexpf(sg * u, 14 - e.y);
-          P.mid[(size_t)(t.p_begin + m) * I + cs] = (_Float16)mid;
-        }
-      }
-  }
+  constexpr int N0 = NMB < 4 ? NMB : 4, N1 = NMB > 4 ? NMB - 4 : 0;  // token blocks of the two halves
+  if (wave < 4)
+    gate_up_finish<NMB, N0>(P, t, n_blk, lds, S, st, rx);
+  else
+    gate_up_finish<NMB, N1>(P, t, n_blk, lds, S, st, rx);
 }
 
 // ---------------------------------------------------------------------------
-// down: y[p][r] = mid[p] . Wd[r], float32.  Column blocks of 256 output rows.
+// down: y[p][r] = mid[p] . Wd[r], float32.  Column blocks of 256 output rows;
+// wave w computes its own group, rows 32 w .. 32 w + 31, for every token
+// block (with pairs, the grid of the gate/up tiles, down measured 7% slower).
 // ---------------------------------------------------------------------------
 template <int NMB>
 __device__ __forceinline__ void down_tile(const PrefillProblem &P, const Tile &t, int n_blk, char *lds) {
@@ -491,10 +530,10 @@ __device__ __forceinline__ void down_tile(const PrefillProblem &P, const Tile &t
   S.q_base = D.q + (t.e < 0 ? 0 : (size_t)t.e * qstride) + (size_t)row0 * (I >> 1);
   S.q_off = (uint32_t)((lane >> 1) * (I >> 1) + ((lane & 1) ^ ((lane >> 4) & 1)) * 16);
   S.s_row = D.s + (t.e < 0 ? 0 : (size_t)t.e * sstride) + (size_t)(row0 + nl) * (I >> 6);
-  S.wm = pow2f(st.ew[2]);
+  S.wm[0] = S.wm[1] = pow2f(st.ew[2]);
   const RowExp rx = row_exp(P, t, st, threadIdx.x);
 
-  WaveGemm<NMB> W;
+  WaveGemm<NMB, NMB, false> W;
   W.run(S, I / BK, lds);
   int *rowe = reinterpret_cast<int *>(lds + kRowExpOff);
   if (threadIdx.x < BM) rowe[threadIdx.x] = rx.eb - st.ew[2] - 14;
@@ -506,7 +545,7 @@ __device__ __forceinline__ void down_tile(const PrefillProblem &P, const Tile &t
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int m = acc_row(mb, half, i);
-      if (m < t.rows) P.y[(size_t)(t.p_begin + m) * h + r] = __builtin_amdgcn_ldexpf(W.acc[mb][i], rowe[m]);
+      if (m < t.rows) P.y[(size_t)(t.p_begin + m) * h + r] = __builtin_amdgcn_ldexpf(W.acc[0][mb][i], rowe[m]);
     }
 }
 
