@@ -309,31 +309,24 @@ def main():
 
     # read ceiling of the same access pattern: a pure-load launch of the
     # same calls' gate and up rows (same grid, nothing computed)
-    exs = make_pool.experts
     stream = torch.cuda.current_stream().cuda_stream
 
-    def run_probe(s0, steps):
-        for st in range(s0, s0 + steps):
-            for l in range(L):
-                e = exs[l][(st * L + l) % args.pool]
-                cm.coli_moe_probe_read(layers[l].handle, e.data_ptr(), e.numel(), stream)
+    def probe_us_per_call(probe, exs, pool, s0, n):
+        """Mean time of one probe launch per layer call over the calls
+        s0 .. s0+n-1 of the stack (the experts those calls read)."""
+        def run(a, steps):
+            for st in range(a, a + steps):
+                for l in range(L):
+                    e = exs[l][(st * L + l) % pool]
+                    probe(layers[l].handle, e.data_ptr(), e.numel(), stream)
+        run(0, s0)
+        return 1e3 * time_calls(torch, lambda st: run(s0 + st, 1), n) / (n * L)
 
-    run_probe(0, W)
-    probe_ms = time_calls(torch, lambda st: run_probe(W + st, 1), K)
-    probe_us = 1e3 * probe_ms / (K * L)
+    probe_us = probe_us_per_call(cm.coli_moe_probe_read, make_pool.experts, args.pool, W, K)
     probe_bytes = mean_experts * gate_up_w
-
     # the same for the down + combine launch: its experts' down rows, its
     # grid and row split, loads only
-    def run_probe_down(s0, steps):
-        for st in range(s0, s0 + steps):
-            for l in range(L):
-                e = exs[l][(st * L + l) % args.pool]
-                cm.coli_moe_probe_read_down(layers[l].handle, e.data_ptr(), e.numel(), stream)
-
-    run_probe_down(0, W)
-    probe_down_ms = time_calls(torch, lambda st: run_probe_down(W + st, 1), K)
-    probe_down_us = 1e3 * probe_down_ms / (K * L)
+    probe_down_us = probe_us_per_call(cm.coli_moe_probe_read_down, make_pool.experts, args.pool, W, K)
 
     # every decode kernel's algorithmic bytes and rate: the router (f32 table
     # and the token row, the digit planes written), gate/up (above), down with
@@ -426,6 +419,14 @@ def main():
                             "us_per_layer_call": round(1e3 * ms / n_calls, 2),
                             "expert_weight_GBps": round(reads * eb / (ms / 1e3) / 1e9, 1),
                             "mean_distinct_experts": round(float(na.mean()), 1)}
+            if Tb <= 4:
+                # the small-batch launches stream the batch's distinct experts
+                # over the grids of the two read probes: their sum is the
+                # floor of the call's expert reads
+                fl = sum(probe_us_per_call(pr, make_pool.experts, pool, 3, steps)
+                         for pr in (cm.coli_moe_probe_read, cm.coli_moe_probe_read_down))
+                res[str(Tb)]["read_probe_floor_us"] = round(fl, 2)
+                res[str(Tb)]["call_over_read_floor"] = round(1e3 * ms / n_calls / fl, 3)
             del xb, ob
             log(f"decode T={Tb}: {res[str(Tb)]}")
         result["decode_batches"] = res

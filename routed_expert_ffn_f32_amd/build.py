@@ -20,8 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libcoli_moe.so")
-SOURCES = ["coli_moe.hip", "expert_cache.hip", "router.hip", "dispatch.hip", "expert_gemv.hip", "expert_mfma.hip",
-           "probes.hip"]
+SOURCES = ["coli_moe.hip", "expert_cache.hip", "router.hip", "dispatch.hip", "expert_gemv.hip", "expert_batch.hip",
+           "expert_mfma.hip", "probes.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

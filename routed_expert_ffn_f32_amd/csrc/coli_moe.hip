@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "coli_moe.h"
+#include "expert_batch.h"
 #include "handle.h"
 #include "internal.h"
 
@@ -292,12 +293,15 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
   const bool int8 = int8_tables(c);
   const bool prefill = !int8 && T >= c.prefill_threshold && prefill_shape(c);
   const bool small = !prefill && coli::small_batch(T, k, h, I, int8);
+  // larger batches of int4 experts: int8 matrix cores on byte planes
+  const bool batch = !prefill && !small && !int8 && coli::batch_mfma_fits(T, k, c.n_shared, h, I);
   hipError_t e;
   // 1. router logits (and, for the GEMV path, the hidden rows in digit-plane
   // form)
   if (phase & kPhaseRoute) {
     e = timed(m, K_ROUTER_LOGITS, s, [&] {
-      return launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill ? nullptr : xq, xs, int8, s);
+      return launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill || batch ? nullptr : xq, xs,
+                                  int8, s);
     });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
   }
@@ -418,9 +422,22 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
     // 2. selection and dispatch
     if (!routed && select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
     // 3. gate/up, down, weighted combine
-    e = timed(m, K_GATE_UP, s, [&] { return launch_gemv_gate_up(P, s); });
-    if (e != hipSuccess) return COLI_MOE_EDEVICE;
-    e = timed(m, K_DOWN, s, [&] { return launch_gemv_down(P, s); });
+    if (batch) {
+      // the hidden rows and then the intermediates as byte planes (in the
+      // digit-plane buffers, which this path does not otherwise use)
+      const int n_mid = T * (k + c.n_shared);
+      e = coli::launch_batch_quantize(hidden, T, h, reinterpret_cast<uint8_t *>(xq), xs, s);
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+      e = timed(m, K_GATE_UP, s, [&] { return coli::launch_batch_gate_up(P, s); });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+      e = coli::launch_batch_quantize(P.midf, n_mid, I, reinterpret_cast<uint8_t *>(P.mq), P.ms, s);
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+      e = timed(m, K_DOWN, s, [&] { return coli::launch_batch_down(P, s); });
+    } else {
+      e = timed(m, K_GATE_UP, s, [&] { return launch_gemv_gate_up(P, s); });
+      if (e != hipSuccess) return COLI_MOE_EDEVICE;
+      e = timed(m, K_DOWN, s, [&] { return launch_gemv_down(P, s); });
+    }
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
     e = timed(m, K_COMBINE, s,
               [&] { return launch_combine(y, wsel, idx, inv, T, k, h, c.n_shared, out, s); });
