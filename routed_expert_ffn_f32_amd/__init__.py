@@ -100,6 +100,8 @@ def load_library():
         L.coli_moe_status.restype = ctypes.c_int
         L.coli_moe_test_spin_limit.argtypes = [vp, i32]
         L.coli_moe_test_spin_limit.restype = ctypes.c_int
+        L.coli_moe_test_batch_kernels.argtypes = [vp, i32]
+        L.coli_moe_test_batch_kernels.restype = ctypes.c_int
         L.coli_moe_test_dispatch.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp]
         L.coli_moe_test_dispatch.restype = ctypes.c_int
         L.coli_moe_probe_read.argtypes = [vp, vp, i32, vp]

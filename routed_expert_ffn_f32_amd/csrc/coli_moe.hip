@@ -223,6 +223,7 @@ void set_up(coli_moe_t *m, const coli_moe_config_t &cfg, const coli_moe_weights_
   m->k_use = cfg.top_k;
   m->top_p = 1.0f;
   m->spin_limit = coli::kSpinLimit;
+  m->batch_mfma = 1;
 }
 
 // The workspace state every forward starts from: the lane-permuted router,
@@ -294,7 +295,7 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
   const bool prefill = !int8 && T >= c.prefill_threshold && prefill_shape(c);
   const bool small = !prefill && coli::small_batch(T, k, h, I, int8);
   // larger batches of int4 experts: int8 matrix cores on byte planes
-  const bool batch = !prefill && !small && !int8 && coli::batch_mfma_fits(T, k, c.n_shared, h, I);
+  const bool batch = !prefill && !small && !int8 && m->batch_mfma && coli::batch_mfma_fits(T, k, c.n_shared, h, I);
   hipError_t e;
   // 1. router logits (and, for the GEMV path, the hidden rows in digit-plane
   // form)
@@ -578,6 +579,12 @@ int coli_moe_status(coli_moe_t *m, void *stream) {
 int coli_moe_test_spin_limit(coli_moe_t *m, int32_t polls) {
   if (!m || polls < 0) return COLI_MOE_EARG;
   m->spin_limit = polls;
+  return COLI_MOE_OK;
+}
+
+int coli_moe_test_batch_kernels(coli_moe_t *m, int32_t mfma) {
+  if (!m || (mfma != 0 && mfma != 1)) return COLI_MOE_EARG;
+  m->batch_mfma = mfma;
   return COLI_MOE_OK;
 }
 

@@ -114,6 +114,7 @@ def test_forward_and_dispatch_argument_errors():
     assert lib.coli_moe_status(None, None) == -4
     assert lib.coli_moe_probe_read_down(None, 0x1000, 2, None) == -4
     assert lib.coli_moe_test_spin_limit(None, 5) == -4
+    assert lib.coli_moe_test_batch_kernels(None, 1) == -4
     assert lib.coli_moe_test_dispatch(0x1000, -1, 2, 8, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
     assert lib.coli_moe_test_dispatch(None, 4, 2, 8, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, None) == -4
     lib.coli_moe_free(None)  # no-op
