@@ -239,10 +239,11 @@ int coli_moe_test_spin_limit(coli_moe_t *m, int32_t polls);
 
 /*
  * For tests of both kernel families of the larger int4 batches (above the
- * small-batch limits, below the prefill threshold): mfma = 1 (the default)
- * runs them on the int8 matrix cores, mfma = 0 on the v_dot8 GEMV kernels
- * (which also serve batches too large for the former's 31-bit offsets).
- * Takes effect from the next forward.  -4 for NULL or mfma not 0 or 1.
+ * small-batch limits, below the prefill threshold): mfma = 1 runs them on
+ * the int8 matrix cores, mfma = 0 on the v_dot8 GEMV kernels (which also
+ * serve batches too large for the former's 31-bit offsets), mfma = 2 (the
+ * default) picks by size: the matrix cores from 16 tokens.  Takes effect
+ * from the next forward.  -4 for NULL or mfma outside 0..2.
  */
 int coli_moe_test_batch_kernels(coli_moe_t *m, int32_t mfma);
 

@@ -52,7 +52,7 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kBtTokens = 4;               // tokens per pass over the rows
+constexpr int kBtMinPass = 4;              // fewest tokens per pass over the rows (the grid's bound)
 constexpr int kBtMant = 22;
 constexpr int kBtMinExp = -100;            // groups with max |x| < 2^-101 quantise to zero
 constexpr uint32_t kBtOut = 0x80000000u;   // a buffer offset past every table: the load returns zeros
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) void quantize_bytes_kernel(const float *__rest
 // in-order completion of a wave's loads never holds an operand behind a
 // later code load.
 // ---------------------------------------------------------------------------
-template <int R, int CG>
+template <int R, int CG, int NTT>
 struct BatchShape {
   static constexpr int kTiles = R / 16;
   static constexpr int kRowBytes = 32 * CG;       // codes per row and chunk
@@ -147,8 +147,9 @@ struct BatchShape {
   static constexpr int kSWrap = 64 / CG;          // scale rows per turn of the 64 banks
   static constexpr int kStageCodes = R * kRowBytes;
   static constexpr int kStage = kStageCodes + R * kSStride;
-  static constexpr int kRed = 4 * kTiles * 64 * 4;  // partial sums of the 4 waves
-  static constexpr int kOut = 4 * R * 4 * 4;         // results of up to 4 row blocks x 4 tokens
+  static constexpr int kTokens = 4 * NTT;           // tokens per pass
+  static constexpr int kRed = 4 * NTT * kTiles * 64 * 4;  // partial sums of the 4 waves
+  static constexpr int kOut = 4 * R * kTokens * 4;        // results of up to 4 row blocks
   static constexpr int kLds = 2 * kStage + kRed + kOut;
   static constexpr int kSActive = R / 4 * kSLanes;   // lanes of the scale load
   static_assert(kRpi * kLpr == 64 && kLoads >= 1 && kSActive <= 64, "shape");
@@ -167,30 +168,32 @@ struct BatchWaveSrc {
   int xstep;         // rows of those tables from one row block to the next
   int rowq, G;       // code bytes per row, groups per row
   Rsrc a, as;        // activation byte planes and group scales
-  uint32_t a_off;    // A lane: its token's digit at chunk lane / 16 of group 0; kBtOut: zeros
-  uint32_t as_off;   // C lane: its token's scale row
+  uint32_t a_off[2];   // token tile t, A lane: its token's digit at chunk lane / 16 of group 0; kBtOut: zeros
+  uint32_t as_off[2];  // token tile t, C lane: its token's scale row
 };
 
-// The partial sums of the 4 waves, added in wave order: returns, for wave
-// `w_out` and each tile r it reduces (r % 4 == its tile set), the total.
-template <int R, int CG>
-__device__ __forceinline__ void batch_share(const float (&acc)[R / 16], char *lds) {
-  using B = BatchShape<R, CG>;
+// The partial sums of the 4 waves to LDS (then a barrier); batch_total adds
+// them in wave order.
+template <int R, int CG, int NTT>
+__device__ __forceinline__ void batch_share(const float (&acc)[NTT][R / 16], char *lds) {
+  using B = BatchShape<R, CG, NTT>;
   float *red = reinterpret_cast<float *>(lds + 2 * B::kStage);
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int r = 0; r < R / 16; ++r) red[(wave * (R / 16) + r) * 64 + lane] = acc[r];
+  for (int t = 0; t < NTT; ++t)
+#pragma unroll
+    for (int r = 0; r < R / 16; ++r) red[((wave * NTT + t) * (R / 16) + r) * 64 + lane] = acc[t][r];
   block_barrier();
 }
-template <int R, int CG>
-__device__ __forceinline__ float batch_total(const char *lds, int r) {
-  using B = BatchShape<R, CG>;
+template <int R, int CG, int NTT>
+__device__ __forceinline__ float batch_total(const char *lds, int t, int r) {
+  using B = BatchShape<R, CG, NTT>;
   const float *red = reinterpret_cast<const float *>(lds + 2 * B::kStage);
   const int lane = threadIdx.x & 63;
-  float t = red[r * 64 + lane];
+  float v = red[(t * (R / 16) + r) * 64 + lane];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) t += red[(w * (R / 16) + r) * 64 + lane];
-  return t;
+  for (int w = 1; w < 4; ++w) v += red[((w * NTT + t) * (R / 16) + r) * 64 + lane];
+  return v;
 }
 
 // The block's stream of nx row blocks x (each R rows of the slot) times
@@ -199,16 +202,16 @@ __device__ __forceinline__ float batch_total(const char *lds, int r) {
 // current row block and the pass's 4 tokens (lane: token lane / 16, row
 // lane % 16 of the tile); after a row block's last chunk the waves' parts
 // meet in LDS and epi(x) takes the totals.
-template <int R, int CG, class Epi>
-__device__ __forceinline__ void batch_stream(const BatchWaveSrc &Q, int nx, char *lds, const Epi &epi) {
-  using B = BatchShape<R, CG>;
+template <int R, int CG, int NTT, class Epi>
+__device__ __forceinline__ void batch_stream(const BatchWaveSrc &Q, int ntt, int nx, char *lds, const Epi &epi) {
+  using B = BatchShape<R, CG, NTT>;
   const int lane = threadIdx.x & 63, j = lane & 15, kg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: buffer offsets come from it
   const int G = Q.G, C = (G + CG - 1) / CG, K = nx * C;
   uint4 wr[2][B::kLoads];
   float4 sr[2];
-  v4i ar[2][B::kGw];
-  float xr[2][B::kGw];
+  v4i ar[2][B::kGw][NTT];
+  float xr[2][B::kGw][NTT];
   const uint32_t w_voff = (uint32_t)((lane / B::kLpr) * Q.rowq + 16 * (lane % B::kLpr));
   const bool s_lane = lane < B::kSActive;
   const uint32_t s_voff = s_lane ? (uint32_t)((lane / B::kSLanes) * Q.G * 4 + 16 * (lane % B::kSLanes)) : kBtOut;
@@ -220,15 +223,18 @@ __device__ __forceinline__ void batch_stream(const BatchWaveSrc &Q, int nx, char
       w[i] = bload16(Q.wq, w_voff, (uint32_t)((row + i * B::kRpi) * Q.rowq + B::kRowBytes * c));
     sc = bload16f(Q.ws, s_voff, (uint32_t)(row * Q.G * 4 + 4 * CG * c));
   };
-  auto load_a = [&](int k, v4i (&a)[B::kGw], float (&x)[B::kGw]) {
+  auto load_a = [&](int k, v4i (&a)[B::kGw][NTT], float (&x)[B::kGw][NTT]) {
     k = min(k, K - 1);
     const int c = k % C;
 #pragma unroll
     for (int i = 0; i < B::kGw; ++i) {
       const int g = min(CG * c + B::kGw * wave + i, G - 1);
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(Q.a, (int)Q.a_off, 192 * g, 0);
-      a[i] = v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
-      x[i] = bloadf(Q.as, Q.as_off, (uint32_t)(4 * g));
+#pragma unroll
+      for (int t = 0; t < NTT; ++t) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(Q.a, (int)Q.a_off[t], 192 * g, 0);
+        a[i][t] = v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+        x[i][t] = bloadf(Q.as, Q.as_off[t], (uint32_t)(4 * g));
+      }
     }
   };
   // stage addresses (relative to a buffer): this lane's code pieces and
@@ -263,9 +269,11 @@ __device__ __forceinline__ void batch_stream(const BatchWaveSrc &Q, int nx, char
   load_w(1, wr[1], sr[1]);
   __builtin_amdgcn_sched_barrier(0);
   const v4i zero = {0, 0, 0, 0};
-  float acc[R / 16];
+  float acc[NTT][R / 16];
 #pragma unroll
-  for (int r = 0; r < R / 16; ++r) acc[r] = 0.0f;
+  for (int t = 0; t < NTT; ++t)
+#pragma unroll
+    for (int r = 0; r < R / 16; ++r) acc[t][r] = 0.0f;
   // jobs in pairs (ring slots 0, 1); an odd count ends with a job that only
   // loads and stages (no branch around loads, so every wait counts the same
   // loads in flight)
@@ -299,24 +307,32 @@ __device__ __forceinline__ void batch_stream(const BatchWaveSrc &Q, int nx, char
                         (int)(w.y & 0xF0F0F0F0u)};
             sw[r] = *reinterpret_cast<const float *>(st + 16 * r * B::kSStride + rd_s[i]);
           }
-          v4i cc[R / 16];
 #pragma unroll
-          for (int r = 0; r < R / 16; ++r) cc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ar[u][i], bq[r], zero, 0, 0, 0);
+          for (int t = 0; t < NTT; ++t) {
+            if (t < ntt) {
+              v4i cc[R / 16];
 #pragma unroll
-          for (int r = 0; r < R / 16; ++r) {
-            const int lo = (int)((uint32_t)cc[r][1] << 8) + cc[r][0];  // |.| < 2^29
-            const float y = __builtin_fmaf((float)cc[r][2], 65536.0f, (float)lo);
-            acc[r] = __builtin_fmaf(sw[r] * xr[u][i], y, acc[r]);
+              for (int r = 0; r < R / 16; ++r)
+                cc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ar[u][i][t], bq[r], zero, 0, 0, 0);
+#pragma unroll
+              for (int r = 0; r < R / 16; ++r) {
+                const int lo = (int)((uint32_t)cc[r][1] << 8) + cc[r][0];  // |.| < 2^29
+                const float y = __builtin_fmaf((float)cc[r][2], 65536.0f, (float)lo);
+                acc[t][r] = __builtin_fmaf(sw[r] * xr[u][i][t], y, acc[t][r]);
+              }
+            }
           }
         }
       }
       if (real && c == C - 1) {
         // the row block's totals (the next job's barrier comes after every
         // wave has read them, before the sums are written again)
-        batch_share<R, CG>(acc, lds);
+        batch_share<R, CG, NTT>(acc, lds);
         epi(x);
 #pragma unroll
-        for (int r = 0; r < R / 16; ++r) acc[r] = 0.0f;
+        for (int t = 0; t < NTT; ++t)
+#pragma unroll
+          for (int r = 0; r < R / 16; ++r) acc[t][r] = 0.0f;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -333,7 +349,8 @@ struct BatchSlot {
 
 // Block y of the grid: y < n_sh is chunk y of the shared expert's tokens;
 // then routed slot y - n_sh.  False when the block has no work.
-__device__ __forceinline__ bool batch_slot(const DecodeProblem &P, int n_sh, bool down, BatchSlot &S, int &t_first,
+__device__ __forceinline__ bool batch_slot(const DecodeProblem &P, int n_sh, bool down, int pass, BatchSlot &S,
+                                           int &t_first,
                                            int &t_end) {
   const int y = (int)blockIdx.y;
   if (y < n_sh) {
@@ -344,8 +361,8 @@ __device__ __forceinline__ bool batch_slot(const DecodeProblem &P, int n_sh, boo
     S.p_begin = P.T * P.k;
     S.cnt = P.T;
     S.base = -1;
-    t_first = y * kBtTokens;
-    t_end = min(P.T, t_first + kBtTokens);
+    t_first = y * pass;
+    t_end = min(P.T, t_first + pass);
     return t_first < t_end;
   }
   const int slot = y - n_sh;
@@ -370,18 +387,23 @@ __device__ __forceinline__ bool batch_slot(const DecodeProblem &P, int n_sh, boo
   return S.cnt > 0;
 }
 
-constexpr int kGuR = 32, kGuCG = 16;  // gate/up: 16 gate + 16 up rows, 512 bytes of codes per row and chunk
-constexpr int kDnR = 64, kDnCG = 16;  // down: 64 rows, 512 bytes of codes per row and chunk
+// gate/up: 16 gate + 16 up rows, 512 bytes of codes per row and chunk;
+// down: 64 rows, 512 bytes per row and chunk; 4 tokens a pass (a second
+// token tile in gate/up, 8 tokens a pass, took GLM-like T = 64 from 515 to
+// 487 us but T = 16 from 222 to 262 us: the registers of the second tile
+// cost a workgroup per CU)
+constexpr int kGuR = 32, kGuCG = 16, kGuTT = 1;
+constexpr int kDnR = 64, kDnCG = 16, kDnTT = 1;
 
 // gate/up: block x owns intermediate rows [16 nx x, 16 nx (x + 1)), row
 // block i of them rows 16 (nx x + i) + (0..15) (tile 0: gate rows, tile 1:
 // up rows); waves 0, 1 load gate rows, waves 2, 3 up rows.
 __global__ __launch_bounds__(256) void gate_up_batch_kernel(DecodeProblem P, int n_sh, int nx) {
-  using B = BatchShape<kGuR, kGuCG>;
+  using B = BatchShape<kGuR, kGuCG, kGuTT>;
   __shared__ __attribute__((aligned(16))) char lds[B::kLds];
   BatchSlot S;
   int t_first, t_end;
-  if (!batch_slot(P, n_sh, false, S, t_first, t_end)) return;
+  if (!batch_slot(P, n_sh, false, B::kTokens, S, t_first, t_end)) return;
   const int lane = threadIdx.x & 63, j = lane & 15, kg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: buffer offsets come from it
   const int h = P.h, I = P.I, G = h >> 6, rowq = h >> 1;
@@ -398,23 +420,30 @@ __global__ __launch_bounds__(256) void gate_up_batch_kernel(DecodeProblem P, int
   Q.as = make_rsrc(P.xs, (uint32_t)((size_t)P.T * G * 4));
   const int ti = (lane & 15) >> 2, d = lane & 3;
   auto token_of = [&](int i) { return S.base < 0 ? i : P.sorted_ids[S.base + i] / P.k; };
-  for (int t0 = t_first; t0 < t_end; t0 += kBtTokens) {
-    const int ia = t0 + ti;
-    Q.a_off = d < 3 && ia < t_end ? (uint32_t)(token_of(ia) * 3 * h + 48 * kg + 16 * d) : kBtOut;
-    Q.as_off = (uint32_t)(token_of(min(t0 + kg, t_end - 1)) * G * 4);
-    // wave 0 (token kg, intermediate row 16 x + j of the block's) leaves the
-    // results in LDS: global stores inside the stream would make its waits
-    // count them
+  for (int t0 = t_first; t0 < t_end; t0 += B::kTokens) {
+#pragma unroll
+    for (int t = 0; t < kGuTT; ++t) {
+      const int ia = t0 + 4 * t + ti;
+      Q.a_off[t] = d < 3 && ia < t_end ? (uint32_t)(token_of(ia) * 3 * h + 48 * kg + 16 * d) : kBtOut;
+      Q.as_off[t] = (uint32_t)(token_of(min(t0 + 4 * t + kg, t_end - 1)) * G * 4);
+    }
+    const int ntt = (min(B::kTokens, t_end - t0) + 3) >> 2;
+    // wave 0 (token 4 t + kg, intermediate row 16 x + j of the block's)
+    // leaves the results in LDS: global stores inside the stream would make
+    // its waits count them
     float *outb = reinterpret_cast<float *>(lds + 2 * B::kStage + B::kRed);  // [x][token][16 rows]
-    batch_stream<kGuR, kGuCG>(Q, nx, lds, [&](int x) {
+    batch_stream<kGuR, kGuCG, kGuTT>(Q, ntt, nx, lds, [&](int x) {
       if (wave == 0) {
-        const float g = batch_total<kGuR, kGuCG>(lds, 0), u = batch_total<kGuR, kGuCG>(lds, 1);
-        outb[(x * 4 + kg) * 16 + j] = g / (1.0f + expf(-g)) * u;
+#pragma unroll
+        for (int t = 0; t < kGuTT; ++t) {
+          const float g = batch_total<kGuR, kGuCG, kGuTT>(lds, t, 0), u = batch_total<kGuR, kGuCG, kGuTT>(lds, t, 1);
+          outb[(x * B::kTokens + 4 * t + kg) * 16 + j] = g / (1.0f + expf(-g)) * u;
+        }
       }
     });
     block_barrier();
-    for (int i = threadIdx.x; i < nx * 64; i += 256) {
-      const int x = i >> 6, t = (i >> 4) & 3, row = i & 15;
+    for (int i = threadIdx.x; i < nx * B::kTokens * 16; i += 256) {
+      const int x = i / (B::kTokens * 16), t = (i >> 4) % B::kTokens, row = i & 15;
       if (t0 + t < t_end) P.midf[(size_t)(S.p_begin + t0 + t) * I + r0 + 16 * x + row] = outb[i];
     }
     block_barrier();  // the stage, the sums and the results are rewritten by the next pass
@@ -425,11 +454,11 @@ __global__ __launch_bounds__(256) void gate_up_batch_kernel(DecodeProblem P, int
 // kDnR rows, tiles of 16), wave w loads rows kDnR / 4 * w .. of each; y per
 // assignment position; wave r stores tile r.
 __global__ __launch_bounds__(256) void down_batch_kernel(DecodeProblem P, int n_sh, int nx) {
-  using B = BatchShape<kDnR, kDnCG>;
+  using B = BatchShape<kDnR, kDnCG, kDnTT>;
   __shared__ __attribute__((aligned(16))) char lds[B::kLds];
   BatchSlot S;
   int t_first, t_end;
-  if (!batch_slot(P, n_sh, true, S, t_first, t_end)) return;
+  if (!batch_slot(P, n_sh, true, B::kTokens, S, t_first, t_end)) return;
   const int lane = threadIdx.x & 63, j = lane & 15, kg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // scalar: buffer offsets come from it
   const int h = P.h, I = P.I, G = I >> 6, rowq = I >> 1;
@@ -445,15 +474,15 @@ __global__ __launch_bounds__(256) void down_batch_kernel(DecodeProblem P, int n_
   Q.a = make_rsrc(P.mq, (uint32_t)(n_rows * 3 * I));
   Q.as = make_rsrc(P.ms, (uint32_t)(n_rows * G * 4));
   const int ti = (lane & 15) >> 2, d = lane & 3;
-  for (int t0 = t_first; t0 < t_end; t0 += kBtTokens) {
+  for (int t0 = t_first; t0 < t_end; t0 += B::kTokens) {
     const int ia = t0 + ti;
-    Q.a_off = d < 3 && ia < t_end ? (uint32_t)((S.p_begin + ia) * 3 * I + 48 * kg + 16 * d) : kBtOut;
-    Q.as_off = (uint32_t)((S.p_begin + min(t0 + kg, t_end - 1)) * G * 4);
+    Q.a_off[0] = d < 3 && ia < t_end ? (uint32_t)((S.p_begin + ia) * 3 * I + 48 * kg + 16 * d) : kBtOut;
+    Q.as_off[0] = (uint32_t)((S.p_begin + min(t0 + kg, t_end - 1)) * G * 4);
     // wave r (token kg, row kDnR x + 16 r + j of the block's) leaves the
     // results in LDS
     float *outb = reinterpret_cast<float *>(lds + 2 * B::kStage + B::kRed);  // [x][token][kDnR rows]
-    batch_stream<kDnR, kDnCG>(Q, nx, lds, [&](int x) {
-      if (wave < kDnR / 16) outb[(x * 4 + kg) * kDnR + 16 * wave + j] = batch_total<kDnR, kDnCG>(lds, wave);
+    batch_stream<kDnR, kDnCG, kDnTT>(Q, 1, nx, lds, [&](int x) {
+      if (wave < kDnR / 16) outb[(x * 4 + kg) * kDnR + 16 * wave + j] = batch_total<kDnR, kDnCG, kDnTT>(lds, 0, wave);
     });
     block_barrier();
     for (int i = threadIdx.x; i < nx * 4 * kDnR; i += 256) {
@@ -467,7 +496,7 @@ __global__ __launch_bounds__(256) void down_batch_kernel(DecodeProblem P, int n_
 // Row blocks per workgroup: the most of 4, 2, 1 that divides the count.
 int row_blocks_per_group(int n) { return n % 4 == 0 ? 4 : n % 2 == 0 ? 2 : 1; }
 
-int shared_chunks(const DecodeProblem &P) { return P.has_shared ? (P.T + kBtTokens - 1) / kBtTokens : 0; }
+int shared_chunks(const DecodeProblem &P, int pass) { return P.has_shared ? (P.T + pass - 1) / pass : 0; }
 
 }  // namespace
 
@@ -476,7 +505,7 @@ bool batch_mfma_fits(int T, int k, int has_shared, int h, int I) {
   // the out-of-range offset kBtOut)
   const uint64_t rows = (uint64_t)T * (k + has_shared);
   return (uint64_t)T * 3 * h < kBtOut && rows * 3 * I < kBtOut && (uint64_t)I * (h >> 1) < kBtOut &&
-         (uint64_t)T / kBtTokens + 1 + kMaxExperts <= 65535;
+         (uint64_t)T / kBtMinPass + 1 + kMaxExperts <= 65535;
 }
 
 hipError_t launch_batch_quantize(const float *src, int n, int cols, uint8_t *planes, float *scales,
@@ -488,14 +517,14 @@ hipError_t launch_batch_quantize(const float *src, int n, int cols, uint8_t *pla
 }
 
 hipError_t launch_batch_gate_up(const DecodeProblem &P, hipStream_t s) {
-  const int n_sh = shared_chunks(P);
+  const int n_sh = shared_chunks(P, 4 * kGuTT);
   if (P.T == 0 || n_sh + P.n_routed_slots == 0) return hipSuccess;
   const int nx = row_blocks_per_group(P.I / 16);
   return launch(gate_up_batch_kernel, dim3(P.I / 16 / nx, n_sh + P.n_routed_slots), 256, 0, s, P, n_sh, nx);
 }
 
 hipError_t launch_batch_down(const DecodeProblem &P, hipStream_t s) {
-  const int n_sh = shared_chunks(P);
+  const int n_sh = shared_chunks(P, 4 * kDnTT);
   if (P.T == 0 || n_sh + P.n_routed_slots == 0) return hipSuccess;
   const int nx = row_blocks_per_group(P.h / kDnR);
   return launch(down_batch_kernel, dim3(P.h / kDnR / nx, n_sh + P.n_routed_slots), 256, 0, s, P, n_sh, nx);

@@ -43,7 +43,7 @@ struct coli_moe {
   int32_t k_use;
   float top_p;
   int32_t spin_limit;  // bound of the one-token gate/up launch's LDS-flag wait, in polls
-  int32_t batch_mfma;  // larger int4 batches: 1 = int8 MFMA kernels, 0 = the v_dot8 GEMV kernels
+  int32_t batch_mfma;  // larger int4 batches: 2 = by size (default), 1 = int8 MFMA kernels, 0 = v_dot8 GEMV kernels
 };
 
 namespace coli {

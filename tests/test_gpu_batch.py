@@ -2,7 +2,8 @@
 the small-batch limits and below the prefill threshold) against the CPU
 oracle, for both kernel families: the int8 matrix-core kernels (the
 default: byte-plane activations, exact int32 products per 64-column group)
-and the v_dot8 GEMV kernels (coli_moe_test_batch_kernels(handle, 0)).
+and the v_dot8 GEMV kernels, each forced with coli_moe_test_batch_kernels
+(by default the library picks the GEMV kernels below 16 tokens).
 
 Bar: routing and dispatch bit-exact, outputs within 2e-3 element-wise
 (floored at the row RMS), as for every GEMV-class path.  Covered: token
@@ -117,6 +118,7 @@ def test_batch_kernel_families_agree_and_repeat(dev):
         diff = rel_err(outs[("mfma", 0)], outs[("gemv", 0)])
         log(f"  families: rel diff {diff:.3e}")
         assert diff <= 2 * TOL
-        assert lib.coli_moe_test_batch_kernels(L.moe.handle, 2) == -4
+        assert lib.coli_moe_test_batch_kernels(L.moe.handle, 3) == -4
+        assert lib.coli_moe_test_batch_kernels(L.moe.handle, 2) == 0
     finally:
         L.close()
