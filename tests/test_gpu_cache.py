@@ -61,15 +61,20 @@ def check_cache_routing(C, L: DeviceLayer, x: np.ndarray):
 
 
 SMALL = synth.LayerShape(hidden=256, n_experts=32, top_k=2, inter=128, n_shared=1, rsf=2.5, bias_sigma=0.05)
+# calls of 16 tokens and more take the matrix-core batch kernels, here on
+# cache slots
+BATCH = synth.LayerShape(hidden=512, n_experts=48, top_k=2, inter=256, n_shared=1, rsf=2.5, bias_sigma=0.05)
 
 
 @pytest.mark.parametrize("name,shape,max_t,n_slots,Ts", [
     ("olmoe", synth.OLMOE, 2, 20, (1, 2, 1, 1, 2, 1, 2, 2, 1, 1, 2, 1)),
-    ("small_shared", SMALL, 6, 14, (3, 6, 1, 4, 5, 6, 2, 1, 3, 6))])
+    ("small_shared", SMALL, 6, 14, (3, 6, 1, 4, 5, 6, 2, 1, 3, 6)),
+    ("batch_mfma", BATCH, 20, 44, (16, 20, 17, 5, 18, 16))])
 def test_cache_matches_resident_layer(dev, name, shape, max_t, n_slots, Ts):
     """Every call bit-identical to the resident layer (small-batch and
-    larger-batch launch structures both run), routing bit-exact, outputs
-    against the oracle, counters consistent."""
+    larger-batch launch structures both run, the latter on the GEMV and on
+    the matrix-core kernels), routing bit-exact, outputs against the oracle,
+    counters consistent."""
     log(f"expert cache {name}: {shape.n_experts} experts in host memory, {n_slots} HBM slots")
     L = DeviceLayer(shape, 17, 0, dev, max_tokens=max_t, keep_host=True)
     C = make_cache(L, n_slots)
