@@ -62,14 +62,16 @@ def check_cache_routing(C, L: DeviceLayer, x: np.ndarray):
 
 SMALL = synth.LayerShape(hidden=256, n_experts=32, top_k=2, inter=128, n_shared=1, rsf=2.5, bias_sigma=0.05)
 # calls of 16 tokens and more take the matrix-core batch kernels, here on
-# cache slots
-BATCH = synth.LayerShape(hidden=512, n_experts=48, top_k=2, inter=256, n_shared=1, rsf=2.5, bias_sigma=0.05)
+# cache slots.  A cache holds at least max_tokens * top_k slots (40 here);
+# these six calls route to 8 to 25 distinct experts each and 48 in all, so
+# the 40 slots fill and then evict
+BATCH = synth.LayerShape(hidden=512, n_experts=64, top_k=2, inter=256, n_shared=1, rsf=2.5, bias_sigma=0.05)
 
 
 @pytest.mark.parametrize("name,shape,max_t,n_slots,Ts", [
     ("olmoe", synth.OLMOE, 2, 20, (1, 2, 1, 1, 2, 1, 2, 2, 1, 1, 2, 1)),
     ("small_shared", SMALL, 6, 14, (3, 6, 1, 4, 5, 6, 2, 1, 3, 6)),
-    ("batch_mfma", BATCH, 20, 44, (16, 20, 17, 5, 18, 16))])
+    ("batch_mfma", BATCH, 20, 40, (16, 20, 17, 5, 18, 16))])
 def test_cache_matches_resident_layer(dev, name, shape, max_t, n_slots, Ts):
     """Every call bit-identical to the resident layer (small-batch and
     larger-batch launch structures both run, the latter on the GEMV and on
