@@ -11,6 +11,8 @@
 // elements come as one float4.
 #pragma once
 
+#include <type_traits>
+
 #include "internal.h"
 #include "wave.h"
 
@@ -230,8 +232,12 @@ __device__ __forceinline__ void logits_wide_tile(const float *__restrict__ x, co
   // two register sets: block b + 2's loads are issued while block b is
   // computed (one block of fmas is shorter than a load's latency here);
   // past the last block they re-read it (unused)
+  // The set index is a compile-time constant at every use (passed as an
+  // integral_constant): indexed at run time, the compiler moves the sets to
+  // LDS, with an LDS round trip per step and a wait for every load.
   float4 xv[2][XK], wv[2][WK];
-  auto load = [&](int b, int set) {
+  auto load = [&](int b, auto setc) {
+    constexpr int set = decltype(setc)::value;
     b = min(b, MB - 1);
 #pragma unroll
     for (int k = 0; k < XK; ++k) {
@@ -241,18 +247,25 @@ __device__ __forceinline__ void logits_wide_tile(const float *__restrict__ x, co
       xv[set][k] = make_float4(f[0], f[1], f[2], f[3]);
     }
 #pragma unroll
-    for (int k = 0; k < WK; ++k) wv[set][k] = wr[k][(size_t)b * 64];
+    for (int k = 0; k < WK; ++k) {
+      const float4 v = wr[k][(size_t)b * 64];
+      wv[set][k] = make_float4(v.x, v.y, v.z, v.w);
+    }
   };
   float acc[64];
 #pragma unroll
   for (int j = 0; j < 64; ++j) acc[j] = 0.0f;
-  auto step = [&](int b, int set) {
+  auto step = [&](int b, auto setc) {
+    constexpr int set = decltype(setc)::value;
 #pragma unroll
     for (int k = 0; k < XK; ++k) xs[set][wave + NW * k][lane] = xv[set][k];
 #pragma unroll
     for (int k = 0; k < WK; ++k) ws[set][wave + NW * k][lane] = wv[set][k];
-    __syncthreads();  // block b staged; every wave past block b - 1's reads of the other buffer
-    load(b + 2, set);
+    // block b staged; every wave past block b - 1's reads of the other
+    // buffer.  An LDS-only barrier: the next block's global loads stay in
+    // flight across it (__syncthreads would wait for them too).
+    block_barrier();
+    load(b + 2, setc);
     float4 a[8], c[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) a[t] = xs[set][8 * tw + t][lane];
@@ -278,12 +291,19 @@ __device__ __forceinline__ void logits_wide_tile(const float *__restrict__ x, co
         if (4 * b + i < M) fmas(i);
     }
   };
-  load(0, 0);
-  load(1, 1);
-  for (int b = 0; b < MB; b += 2) {
-    step(b, 0);
-    if (b + 1 < MB) step(b + 1, 1);
+  const std::integral_constant<int, 0> set0;
+  const std::integral_constant<int, 1> set1;
+  load(0, set0);
+  load(1, set1);
+  // straight-line pairs (a skippable second step would leave the compiler's
+  // count of loads in flight unknown at the loop head, and it would wait
+  // for all of them there), then an odd last block
+  int b = 0;
+  for (; b + 1 < MB; b += 2) {
+    step(b, set0);
+    step(b + 1, set1);
   }
+  if (b < MB) step(b, set0);
   const float sum = butterfly64_transposed(acc);
   const int t = t0 + 8 * tw + (lane >> 3), e = e0 + 8 * ew + (lane & 7);
   if (t < T && e < E) logits[(size_t)t * E + e] = sum;
