@@ -387,19 +387,28 @@ __device__ __forceinline__ bool batch_slot(const DecodeProblem &P, int n_sh, boo
   return S.cnt > 0;
 }
 
-// gate/up: 16 gate + 16 up rows, 512 bytes of codes per row and chunk;
-// down: 64 rows, 512 bytes per row and chunk; 4 tokens a pass (a second
-// token tile in gate/up, 8 tokens a pass, took GLM-like T = 64 from 515 to
-// 487 us but T = 16 from 222 to 262 us: the registers of the second tile
-// cost a workgroup per CU)
-constexpr int kGuR = 32, kGuCG = 16, kGuTT = 1;
+// gate/up: 16 gate + 16 up rows, 512 bytes of codes per row and chunk,
+// one token tile (4 tokens a pass) or two (8 tokens a pass);
+// down: 64 rows, 512 bytes per row and chunk, 4 tokens a pass.
+constexpr int kGuR = 32, kGuCG = 16;
 constexpr int kDnR = 64, kDnCG = 16, kDnTT = 1;
+
+// Two gate/up token tiles halve the passes over the rows of an expert with
+// more than 4 tokens and the chunks of the shared expert, which every pass
+// reads again; their registers cost a workgroup per CU.  Outputs are the
+// same bits either way.  Measured (gate/up kernel, microseconds, one tile
+// against two): GLM-like layer (E = 256, k = 8) T = 32: 328 / 353, T = 40:
+// 372 / 382, T = 48: 417 / 410, T = 64: 509 / 485; OLMoE-like layer
+// (E = 64, k = 8) two tiles faster from T = 16 (38 / 37) to T = 64
+// (73 / 65).  Both switch where a call holds 1.5 assignments per expert.
+bool gate_up_two_tiles(int T, int k, int E) { return 2 * (int64_t)T * k >= 3 * (int64_t)E; }
 
 // gate/up: block x owns intermediate rows [16 nx x, 16 nx (x + 1)), row
 // block i of them rows 16 (nx x + i) + (0..15) (tile 0: gate rows, tile 1:
 // up rows); waves 0, 1 load gate rows, waves 2, 3 up rows.
+template <int TT>
 __global__ __launch_bounds__(256) void gate_up_batch_kernel(DecodeProblem P, int n_sh, int nx) {
-  using B = BatchShape<kGuR, kGuCG, kGuTT>;
+  using B = BatchShape<kGuR, kGuCG, TT>;
   __shared__ __attribute__((aligned(16))) char lds[B::kLds];
   BatchSlot S;
   int t_first, t_end;
@@ -422,7 +431,7 @@ __global__ __launch_bounds__(256) void gate_up_batch_kernel(DecodeProblem P, int
   auto token_of = [&](int i) { return S.base < 0 ? i : P.sorted_ids[S.base + i] / P.k; };
   for (int t0 = t_first; t0 < t_end; t0 += B::kTokens) {
 #pragma unroll
-    for (int t = 0; t < kGuTT; ++t) {
+    for (int t = 0; t < TT; ++t) {
       const int ia = t0 + 4 * t + ti;
       Q.a_off[t] = d < 3 && ia < t_end ? (uint32_t)(token_of(ia) * 3 * h + 48 * kg + 16 * d) : kBtOut;
       Q.as_off[t] = (uint32_t)(token_of(min(t0 + 4 * t + kg, t_end - 1)) * G * 4);
@@ -432,11 +441,11 @@ __global__ __launch_bounds__(256) void gate_up_batch_kernel(DecodeProblem P, int
     // leaves the results in LDS: global stores inside the stream would make
     // its waits count them
     float *outb = reinterpret_cast<float *>(lds + 2 * B::kStage + B::kRed);  // [x][token][16 rows]
-    batch_stream<kGuR, kGuCG, kGuTT>(Q, ntt, nx, lds, [&](int x) {
+    batch_stream<kGuR, kGuCG, TT>(Q, ntt, nx, lds, [&](int x) {
       if (wave == 0) {
 #pragma unroll
-        for (int t = 0; t < kGuTT; ++t) {
-          const float g = batch_total<kGuR, kGuCG, kGuTT>(lds, t, 0), u = batch_total<kGuR, kGuCG, kGuTT>(lds, t, 1);
+        for (int t = 0; t < TT; ++t) {
+          const float g = batch_total<kGuR, kGuCG, TT>(lds, t, 0), u = batch_total<kGuR, kGuCG, TT>(lds, t, 1);
           outb[(x * B::kTokens + 4 * t + kg) * 16 + j] = g / (1.0f + expf(-g)) * u;
         }
       }
@@ -517,10 +526,13 @@ hipError_t launch_batch_quantize(const float *src, int n, int cols, uint8_t *pla
 }
 
 hipError_t launch_batch_gate_up(const DecodeProblem &P, hipStream_t s) {
-  const int n_sh = shared_chunks(P, 4 * kGuTT);
+  const bool two = gate_up_two_tiles(P.T, P.k, P.E);
+  const int n_sh = shared_chunks(P, two ? 8 : 4);
   if (P.T == 0 || n_sh + P.n_routed_slots == 0) return hipSuccess;
   const int nx = row_blocks_per_group(P.I / 16);
-  return launch(gate_up_batch_kernel, dim3(P.I / 16 / nx, n_sh + P.n_routed_slots), 256, 0, s, P, n_sh, nx);
+  const dim3 grid(P.I / 16 / nx, n_sh + P.n_routed_slots);
+  if (two) return launch(gate_up_batch_kernel<2>, grid, 256, 0, s, P, n_sh, nx);
+  return launch(gate_up_batch_kernel<1>, grid, 256, 0, s, P, n_sh, nx);
 }
 
 hipError_t launch_batch_down(const DecodeProblem &P, hipStream_t s) {
