@@ -140,6 +140,12 @@ __device__ __forceinline__ float logit_t1(const float *__restrict__ x, const flo
   for (int b = 0; b < MB; ++b) wv[b] = wp[(size_t)b * 64];
 #pragma unroll
   for (int m = 0; m < M; ++m) xv[m] = x[lane + 64 * m];
+  // left to itself the scheduler keeps about a quarter of these loads in
+  // flight (for occupancy the launch does not need: one wave per block, a
+  // block per expert) and issues the rest between the fmas.  Measured: the
+  // same 4.1 us either way at h = 6144, E = 256 (the launch is bound by its
+  // dispatch and one round trip, not by the loads' issue).
+  __builtin_amdgcn_sched_barrier(0);
   float acc = 0.0f;
 #pragma unroll
   for (int b = 0; b < MB; ++b) {
