@@ -395,13 +395,21 @@ constexpr int kDnR = 64, kDnCG = 16, kDnTT = 1;
 
 // Two gate/up token tiles halve the passes over the rows of an expert with
 // more than 4 tokens and the chunks of the shared expert, which every pass
-// reads again; their registers cost a workgroup per CU.  Outputs are the
-// same bits either way.  Measured (gate/up kernel, microseconds, one tile
-// against two): GLM-like layer (E = 256, k = 8) T = 32: 328 / 353, T = 40:
-// 372 / 382, T = 48: 417 / 410, T = 64: 509 / 485; OLMoE-like layer
-// (E = 64, k = 8) two tiles faster from T = 16 (38 / 37) to T = 64
-// (73 / 65).  Both switch where a call holds 1.5 assignments per expert.
-bool gate_up_two_tiles(int T, int k, int E) { return 2 * (int64_t)T * k >= 3 * (int64_t)E; }
+// reads again; in return each pass carries the second tile's registers and
+// work.  Outputs are the same bits either way.  Measured (microseconds, one
+// tile against two):
+//  - GLM-like layer (E = 256, k = 8, a shared expert), gate/up kernel:
+//    T = 16: 220 / 258, T = 32: 330 / 353, T = 40: 372 / 382,
+//    T = 48: 413 / 410, T = 64: 510 / 480;
+//  - OLMoE-like layer (E = 64, k = 8, no shared expert), whole calls with
+//    the weights from HBM (8 copies in turn): T = 16: 82 / 85,
+//    T = 24: 95 / 93, T = 32: 105 / 101, T = 64: 153 / 143.
+// Two tiles therefore from 2.5 assignments per expert, or from 48 tokens
+// with a shared expert (its passes are then the larger saving).  A variant
+// held to 168 registers (three workgroups per CU) spilled and was slower.
+bool gate_up_two_tiles(int T, int k, int E, bool shared) {
+  return 2 * (int64_t)T * k >= 5 * (int64_t)E || (shared && T >= 48);
+}
 
 // gate/up: block x owns intermediate rows [16 nx x, 16 nx (x + 1)), row
 // block i of them rows 16 (nx x + i) + (0..15) (tile 0: gate rows, tile 1:
@@ -526,7 +534,7 @@ hipError_t launch_batch_quantize(const float *src, int n, int cols, uint8_t *pla
 }
 
 hipError_t launch_batch_gate_up(const DecodeProblem &P, hipStream_t s) {
-  const bool two = gate_up_two_tiles(P.T, P.k, P.E);
+  const bool two = gate_up_two_tiles(P.T, P.k, P.E, P.has_shared != 0);
   const int n_sh = shared_chunks(P, two ? 8 : 4);
   if (P.T == 0 || n_sh + P.n_routed_slots == 0) return hipSuccess;
   const int nx = row_blocks_per_group(P.I / 16);

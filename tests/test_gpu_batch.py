@@ -12,9 +12,10 @@ the routed experts, one expert holding every token (passes of 4 in a row),
 rows narrower than a column chunk (one weight group), widths whose row
 blocks per workgroup are 4, 2 and 1, no shared expert, calls of decreasing
 size in a row on one handle, and wide hidden rows.  The gate/up kernel runs
-one token tile (4 tokens a pass) below 1.5 assignments per expert and two
-(8 a pass) from there: h1024_I512_shared T = 5 and the cache test take one,
-the other cases two, with ragged last passes both ways.
+one token tile (4 tokens a pass) or two (8 a pass, from 2.5 assignments per
+expert, or from 48 tokens with a shared expert): T = 5 and 7 of
+h1024_I512_shared, T = 9 of the one-group rows, OLMoE-like T = 16 and the
+wide rows take one, the other cases two, with ragged last passes both ways.
 """
 import dataclasses
 
