@@ -122,8 +122,15 @@ struct ExpertTables {
 // Index of routed expert e's tables in the stacked arrays: e itself, or its
 // cache slot when the tables are the slots of an expert cache (slot_of[e],
 // valid for every expert a call routes to).
+// The map is read through the constant address space: with a wave-uniform
+// e that is a scalar load, whose wait counts scalar and LDS operations only
+// (a vector load here made the kernels wait for every row load in flight at
+// each routed row or slot).  The map is written before the launch and never
+// during it.
+typedef const __attribute__((address_space(4))) int32_t *SlotMapPtr;
 __device__ __forceinline__ size_t table_index(const int32_t *slot_of, int e) {
-  return (size_t)(slot_of ? slot_of[e] : e);
+  if (!slot_of) return (size_t)e;
+  return (size_t)((SlotMapPtr)slot_of)[e];
 }
 
 struct DecodeProblem {
