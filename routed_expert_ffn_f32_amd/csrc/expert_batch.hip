@@ -118,7 +118,8 @@ __global__ __launch_bounds__(256) void quantize_bytes_kernel(const float *__rest
 // The block's product loop (gate/up and down).
 //
 // A block of 4 waves owns R weight rows (R / 16 MFMA tiles) of one slot and
-// a pass of 4 tokens, and runs the columns in chunks of CG groups.  Each
+// a pass of 4 NTT tokens (NTT token tiles of 4), and runs the columns in
+// chunks of CG groups.  Each
 // wave loads R / 4 of the rows, whole row pieces of 32 CG contiguous bytes
 // (the access pattern of the GEMV: 512 or 1024 bytes per row and load), and
 // their scales, into registers, then writes them to the block's LDS stage
@@ -199,8 +200,9 @@ __device__ __forceinline__ float batch_total(const char *lds, int t, int r) {
 // The block's stream of nx row blocks x (each R rows of the slot) times
 // the C chunks of the columns, one ring across all of them: acc[r] sums
 // this wave's part (its groups) of the products of tile r's rows of the
-// current row block and the pass's 4 tokens (lane: token lane / 16, row
-// lane % 16 of the tile); after a row block's last chunk the waves' parts
+// current row block and token tile t of the pass (lane: token 4 t + lane / 16,
+// row lane % 16 of the tile; ntt of the NTT tiles hold tokens of this pass);
+// after a row block's last chunk the waves' parts
 // meet in LDS and epi(x) takes the totals.
 template <int R, int CG, int NTT, class Epi>
 __device__ __forceinline__ void batch_stream(const BatchWaveSrc &Q, int ntt, int nx, char *lds, const Epi &epi) {
