@@ -175,15 +175,20 @@ def test_larger_batch_row_widths(dev, h, I):
     check_full(shape, 11, 12, dev)
 
 
-def test_router_wide_tiles_ragged(dev):
+@pytest.mark.parametrize("h,E", [(320, 20), (192, 20), (768, 36)])
+def test_router_wide_tiles_ragged(dev, h, E):
     """T = 300 takes the router's wide tiles (32 tokens x 16 experts per
-    block) with every edge ragged: T not a multiple of 32, E = 20 not a
-    multiple of 16, h = 320 (5 chain steps per lane, a partial 4-step
-    block).  Routing weights must match the oracle bit for bit, which needs
-    each logit's fma chain and butterfly unchanged; h = 320 keeps the call
-    on the GEMV path, so the digit-plane launch that follows runs too."""
-    log("router wide tiles T=300 E=20 h=320")
-    shape = synth.LayerShape(hidden=320, n_experts=20, top_k=3, inter=128, n_shared=1, rsf=2.5, bias_sigma=0.05)
+    block) with every edge ragged: T not a multiple of 32, E not a multiple
+    of 16, and the chain blocks of 4 steps per lane (h / 256 of them, the
+    last partial when h / 64 is not a multiple of 4) in every arrangement
+    the loop has: h = 320, two blocks (one pair, the second partial);
+    h = 192, one partial block (no pair, the odd tail alone); h = 768,
+    three full blocks (a pair and the odd tail).  Routing weights must match
+    the oracle bit for bit, which needs each logit's fma chain and butterfly
+    unchanged; h = 320 keeps the call on the GEMV path, so the digit-plane
+    launch that follows runs too."""
+    log(f"router wide tiles T=300 E={E} h={h}")
+    shape = synth.LayerShape(hidden=h, n_experts=E, top_k=3, inter=128, n_shared=1, rsf=2.5, bias_sigma=0.05)
     check_full(shape, 31, 300, dev)
 
 
