@@ -368,6 +368,11 @@ constexpr int kSbBlocksLds = kSbBlocks / 2; // gate/up grid, T = 2..4 (8 waves p
 constexpr int kDcWaves = 8;     // down: waves per block
 constexpr int kDcBlocks = 256;   // down: blocks (at most; fewer when h is small)
 constexpr int kDcLds = 64 * 1024;           // down: LDS for the digit planes of a slot group
+// down: LDS up to which every slot's planes are kept at once (one block per
+// CU either way).  GLM-like T = 2 (18 slots, 115 KB): 27.5-28.1 us against
+// 28.9-30.3 us in groups of 10; T = 3 and 4 do not fit, and larger groups
+// measured slower for them than groups of 10.
+constexpr int kDcLdsAll = 144 * 1024;
 constexpr int kSbMaxXLds = 96 * 1024;       // bytes of hidden-row planes staged in LDS
 constexpr int kDcMaxChunks = 4;             // down: I <= 64*32*4
 constexpr int kDcMaxRing = 2;    // down: slots in flight per wave, at most
@@ -1259,7 +1264,7 @@ hipError_t launch_dc_rows_n(const DecodeProblem &P, float *out, int blocks, hipS
   const int per_slot = 3 * P.I + 4 * (P.I >> 5);  // planes and scales of one intermediate row
   const int n_slots = P.T * (P.k + P.has_shared);
   const int gs = kDcLds / per_slot;  // >= 2: small batches have I <= 8192
-  if (gs >= n_slots)
+  if (gs >= n_slots || n_slots * per_slot <= kDcLdsAll)
     return launch(down_combine_rows_kernel<NCHD, RM, true, F>, blocks, kDcWaves * 64, (uint32_t)(n_slots * per_slot),
                   s, P, out, n_slots);
   return launch(down_combine_rows_kernel<NCHD, RM, false, F>, blocks, kDcWaves * 64, (uint32_t)(gs * per_slot), s, P,
