@@ -302,12 +302,14 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
   const bool batch = !prefill && !small && !int8 && coli::batch_mfma_fits(T, k, c.n_shared, h, I) &&
                      (m->batch_mfma == 1 || (m->batch_mfma == 2 && T >= kBatchMfmaMinTokens));
   hipError_t e;
-  // 1. router logits (and, for the GEMV path, the hidden rows in digit-plane
-  // form)
+  // 1. router logits and, for every path but prefill, the hidden rows in
+  // the plane form of the expert kernels (the batch path's byte planes go in
+  // the digit-plane buffers, which it does not otherwise use)
   if (phase & kPhaseRoute) {
+    const int planes = batch ? kPlanesMatrixCore : int8 ? kPlanesInt8 : kPlanesInt4;
     e = timed(m, K_ROUTER_LOGITS, s, [&] {
-      return launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill || batch ? nullptr : xq, xs,
-                                  int8, s);
+      return launch_router_logits(hidden, at<float>(m, L.wrP), T, h, E, logits, prefill ? nullptr : xq, xs, planes,
+                                  s);
     });
     if (e != hipSuccess) return COLI_MOE_EDEVICE;
   }
@@ -429,11 +431,9 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
     if (!routed && select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
     // 3. gate/up, down, weighted combine
     if (batch) {
-      // the hidden rows and then the intermediates as byte planes (in the
-      // digit-plane buffers, which this path does not otherwise use)
+      // the hidden rows' byte planes come from the router launch; the
+      // intermediates' are written between the two products
       const int n_mid = T * (k + c.n_shared);
-      e = coli::launch_batch_quantize(hidden, T, h, reinterpret_cast<uint8_t *>(xq), xs, s);
-      if (e != hipSuccess) return COLI_MOE_EDEVICE;
       e = timed(m, K_GATE_UP, s, [&] { return coli::launch_batch_gate_up(P, s); });
       if (e != hipSuccess) return COLI_MOE_EDEVICE;
       e = coli::launch_batch_quantize(P.midf, n_mid, I, reinterpret_cast<uint8_t *>(P.mq), P.ms, s);

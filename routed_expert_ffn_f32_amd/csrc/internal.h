@@ -85,10 +85,14 @@ hipError_t launch_router_permute(const float *wr, float *wrP, int h, int E, hipS
 // the wave owning (t, e) keeps p_l = fma(x[l+64m], w[l+64m], p_l) over
 // m = 0..h/64-1, then the 64 partials meet in an xor butterfly (32,16,..,1).
 // The same launch writes the digit-plane form of x (xq, xs) for the experts
-// (xq == NULL: no planes; byte_planes: the byte planes of int8 tables).  One token with h in {2048, 4096, 6144} takes a
-// launch that issues every load of a chain before its first fma.
+// (xq == NULL: no planes), in the form plane_mode names: the int4 digit
+// planes of the GEMV kernels, the byte planes of int8 tables, or the byte
+// planes of the matrix-core batch kernels (byte_planes.h).  One token with h
+// in {2048, 4096, 6144} takes a launch that issues every load of a chain
+// before its first fma.
+constexpr int kPlanesInt4 = 0, kPlanesInt8 = 1, kPlanesMatrixCore = 2;
 hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits,
-                                uint32_t *xq, float *xs, bool byte_planes, hipStream_t s);  // xq == NULL: no planes
+                                uint32_t *xq, float *xs, int plane_mode, hipStream_t s);  // xq == NULL: no planes
 
 // One wave per token: sigmoid scores, biased key, top-k (key desc, index
 // asc), renormalised weights times rsf.

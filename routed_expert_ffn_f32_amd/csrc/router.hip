@@ -12,6 +12,7 @@
 //
 // Compiled with -ffp-contract=off and correctly rounded float32 division, so
 // the only fused multiply-adds are the explicit __builtin_fmaf calls.
+#include "byte_planes.h"
 #include "dispatch_block.h"
 #include "internal.h"
 #include "router_tile.h"
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
                                                             const float *__restrict__ wrP, int T, int h, int E,
                                                             float *__restrict__ logits, int n_logit_blocks,
                                                             uint32_t *__restrict__ xq, float *__restrict__ xs,
-                                                            int byte_planes) {
+                                                            int plane_mode) {
   const int bid = blockIdx.x;
   if (bid < n_logit_blocks) {
     const int egroups = (E + 4 * EPW - 1) / (4 * EPW);
@@ -74,7 +75,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
   // form takes 3 h / 4 words per row
   uint32_t *row = xq + t * (size_t)(3 * (h >> 2));
   float *sb = xs + t * (words >> 2) + (w >> 2);
-  if (byte_planes)
+  if (plane_mode == kPlanesMatrixCore)
+    byte_planes_word(v, valid, t, w, h, reinterpret_cast<uint8_t *>(xq), xs);
+  else if (plane_mode == kPlanesInt8)
     FmtI8::quantize(v, (w & 3) == 0, valid, row, h, w, sb);
   else
     FmtI4::quantize(v, (w & 3) == 0, valid, row, h, w, sb);
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(64) void router_logits_t1_kernel(const float *__res
                                                                const float *__restrict__ wrP, int E,
                                                                float *__restrict__ logits, int n_logit_blocks,
                                                                uint32_t *__restrict__ xq, float *__restrict__ xs,
-                                                               int byte_planes) {
+                                                               int plane_mode) {
   constexpr int M = 4 * MB;  // chain length h / 64
   const int lane = threadIdx.x & 63;
   if ((int)blockIdx.x >= n_logit_blocks) {  // the token's digit planes, 64 words per block
@@ -159,7 +162,9 @@ __global__ __launch_bounds__(64) void router_logits_t1_kernel(const float *__res
       for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
     const int wq = valid ? w : 0;
-    if (byte_planes)
+    if (plane_mode == kPlanesMatrixCore)
+      byte_planes_word(v, valid, 0, wq, M * 64, reinterpret_cast<uint8_t *>(xq), xs);
+    else if (plane_mode == kPlanesInt8)
       FmtI8::quantize(v, (w & 3) == 0, valid, xq, M * 64, wq, xs + (wq >> 2));
     else
       FmtI4::quantize(v, (w & 3) == 0, valid, xq, M * 64, wq, xs + (wq >> 2));
@@ -186,8 +191,8 @@ size_t router_permuted_floats(int h, int E) { return (size_t)E * ((((h >> 6) + 3
 constexpr int kWideMinT = 256;
 
 hipError_t launch_router_logits(const float *x, const float *wrP, int T, int h, int E, float *logits, uint32_t *xq,
-                                float *xs, bool byte_planes, hipStream_t s) {
-  const int bp = byte_planes ? 1 : 0;
+                                float *xs, int plane_mode, hipStream_t s) {
+  const int bp = plane_mode;
   if (T <= 0) return hipSuccess;
   const int qblocks = xq ? (int)(((size_t)T * (h >> 3) + 255) / 256) : 0;
   if (T == 1 && (h == 2048 || h == 4096 || h == 6144)) {
