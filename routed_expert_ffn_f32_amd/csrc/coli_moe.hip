@@ -431,12 +431,9 @@ int forward_phases(coli_moe_t *m, const float *hidden, float *out, int32_t T, hi
     if (!routed && select_and_dispatch() != hipSuccess) return COLI_MOE_EDEVICE;
     // 3. gate/up, down, weighted combine
     if (batch) {
-      // the hidden rows' byte planes come from the router launch; the
-      // intermediates' are written between the two products
-      const int n_mid = T * (k + c.n_shared);
+      // the hidden rows' byte planes come from the router launch, the
+      // intermediates' from the gate/up launch's epilogue
       e = timed(m, K_GATE_UP, s, [&] { return coli::launch_batch_gate_up(P, s); });
-      if (e != hipSuccess) return COLI_MOE_EDEVICE;
-      e = coli::launch_batch_quantize(P.midf, n_mid, I, reinterpret_cast<uint8_t *>(P.mq), P.ms, s);
       if (e != hipSuccess) return COLI_MOE_EDEVICE;
       e = timed(m, K_DOWN, s, [&] { return coli::launch_batch_down(P, s); });
     } else {

@@ -10,20 +10,15 @@ namespace coli {
 // offset within 31 bits, the grid within its limits).
 bool batch_mfma_fits(int T, int k, int has_shared, int h, int I);
 
-// Rows of `cols` float32 activations (cols a multiple of 64) as byte planes:
-// per group of 64 columns a power-of-two scale and three balanced base-256
-// digits of each column's 23-bit integer (expert_batch.hip describes the
-// format).  planes [n][3][cols] bytes, scales [n][cols/64] float32.
-hipError_t launch_batch_quantize(const float *src, int n, int cols, uint8_t *planes, float *scales,
-                                 hipStream_t s);
-
 // gate/up of every active slot on the byte planes of the hidden rows (P.xq
-// and P.xs in the format above): midf [P][I] float32 for every assignment
-// position (routed: p = sorted position; shared: p = T*k + t).
+// and P.xs, written by the router launch; format in byte_planes.h and
+// expert_batch.hip): the byte planes of mid (P.mq [P][3I] bytes, P.ms
+// [P][I/64]) for every assignment position (routed: p = sorted position;
+// shared: p = T*k + t).  I a multiple of 64.
 hipError_t launch_batch_gate_up(const DecodeProblem &P, hipStream_t s);
 
-// down of every active slot on the byte planes of midf (P.mq and P.ms in the
-// format above): y [P][h] float32 per assignment position.
+// down of every active slot on the byte planes of mid (P.mq and P.ms): y
+// [P][h] float32 per assignment position.
 hipError_t launch_batch_down(const DecodeProblem &P, hipStream_t s);
 
 }  // namespace coli

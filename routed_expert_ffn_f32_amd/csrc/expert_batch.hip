@@ -57,31 +57,6 @@ constexpr int kBtMinPass = 4;              // fewest tokens per pass over the ro
 constexpr uint32_t kBtOut = 0x80000000u;   // a buffer offset past every table: the load returns zeros
 
 // ---------------------------------------------------------------------------
-// Quantiser: one thread per 8 columns (word w of row p); the 8 words of a
-// 64-column group are an aligned octet of lanes (cols and the block size are
-// multiples of 64 and 8).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quantize_bytes_kernel(const float *__restrict__ src, int n, int cols,
-                                                            uint8_t *__restrict__ planes,
-                                                            float *__restrict__ scales) {
-  const int words = cols >> 3;
-  const size_t wg = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = wg < (size_t)n * words;
-  const size_t p = valid ? wg / words : 0;
-  const int w = valid ? (int)(wg % words) : 0;
-  float v[8];
-  if (valid) {
-    const float4 a = *reinterpret_cast<const float4 *>(src + p * cols + 8 * w);
-    const float4 b = *reinterpret_cast<const float4 *>(src + p * cols + 8 * w + 4);
-    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-  }
-  byte_planes_word(v, valid, p, w, cols, planes, scales);
-}
-
-// ---------------------------------------------------------------------------
 // The block's product loop (gate/up and down).
 //
 // A block of 4 waves owns R weight rows (R / 16 MFMA tiles) of one slot and
@@ -380,9 +355,10 @@ bool gate_up_two_tiles(int T, int k, int E, bool shared) {
   return 2 * (int64_t)T * k >= 5 * (int64_t)E || (shared && T >= 48);
 }
 
-// gate/up: block x owns intermediate rows [16 nx x, 16 nx (x + 1)), row
-// block i of them rows 16 (nx x + i) + (0..15) (tile 0: gate rows, tile 1:
-// up rows); waves 0, 1 load gate rows, waves 2, 3 up rows.
+// gate/up: block x owns intermediate rows [16 nx x, 16 nx (x + 1)) (nx = 4:
+// one 64-column group of mid, whose byte planes it writes), row block i of
+// them rows 16 (nx x + i) + (0..15) (tile 0: gate rows, tile 1: up rows);
+// waves 0, 1 load gate rows, waves 2, 3 up rows.
 template <int TT>
 __global__ __launch_bounds__(256) void gate_up_batch_kernel(DecodeProblem P, int n_sh, int nx) {
   using B = BatchShape<kGuR, kGuCG, TT>;
@@ -428,9 +404,17 @@ __global__ __launch_bounds__(256) void gate_up_batch_kernel(DecodeProblem P, int
       }
     });
     block_barrier();
-    for (int i = threadIdx.x; i < nx * B::kTokens * 16; i += 256) {
-      const int x = i / (B::kTokens * 16), t = (i >> 4) % B::kTokens, row = i & 15;
-      if (t0 + t < t_end) P.midf[(size_t)(S.p_begin + t0 + t) * I + r0 + 16 * x + row] = outb[i];
+    // the block holds one whole 64-column group of mid (4 row blocks of 16):
+    // its byte planes for the down kernel straight from LDS, thread 8 t + i
+    // taking word i of token t (an aligned octet per token)
+    const int tt = threadIdx.x >> 3, wi = threadIdx.x & 7;
+    if (tt < B::kTokens) {
+      const bool valid = t0 + tt < t_end;
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = valid ? outb[((wi >> 1) * B::kTokens + tt) * 16 + 8 * (wi & 1) + i] : 0.0f;
+      byte_planes_word(v, valid, valid ? (size_t)(S.p_begin + t0 + tt) : 0, (r0 >> 3) + wi, I,
+                       reinterpret_cast<uint8_t *>(P.mq), P.ms);
     }
     block_barrier();  // the stage, the sums and the results are rewritten by the next pass
   }
@@ -482,6 +466,7 @@ __global__ __launch_bounds__(256) void down_batch_kernel(DecodeProblem P, int n_
 // Row blocks per workgroup: the most of 4, 2, 1 that divides the count.
 int row_blocks_per_group(int n) { return n % 4 == 0 ? 4 : n % 2 == 0 ? 2 : 1; }
 
+
 int shared_chunks(const DecodeProblem &P, int pass) { return P.has_shared ? (P.T + pass - 1) / pass : 0; }
 
 }  // namespace
@@ -494,19 +479,12 @@ bool batch_mfma_fits(int T, int k, int has_shared, int h, int I) {
          (uint64_t)T / kBtMinPass + 1 + kMaxExperts <= 65535;
 }
 
-hipError_t launch_batch_quantize(const float *src, int n, int cols, uint8_t *planes, float *scales,
-                                 hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const size_t threads = (size_t)n * (cols >> 3);
-  return launch(quantize_bytes_kernel, dim3((unsigned)((threads + 255) / 256)), 256, 0, s, src, n, cols, planes,
-                scales);
-}
-
 hipError_t launch_batch_gate_up(const DecodeProblem &P, hipStream_t s) {
   const bool two = gate_up_two_tiles(P.T, P.k, P.E, P.has_shared != 0);
   const int n_sh = shared_chunks(P, two ? 8 : 4);
+  if (P.I % 64) return hipErrorInvalidValue;  // a workgroup writes whole 64-column groups of mid
   if (P.T == 0 || n_sh + P.n_routed_slots == 0) return hipSuccess;
-  const int nx = row_blocks_per_group(P.I / 16);
+  const int nx = 4;
   const dim3 grid(P.I / 16 / nx, n_sh + P.n_routed_slots);
   if (two) return launch(gate_up_batch_kernel<2>, grid, 256, 0, s, P, n_sh, nx);
   return launch(gate_up_batch_kernel<1>, grid, 256, 0, s, P, n_sh, nx);
